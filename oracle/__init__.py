@@ -1,0 +1,137 @@
+"""CPU fp64 oracle for length-aware decode attention (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding)
+never imports, links or calls it, and it imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 masked softmax attention
+over the visible cells only; see that file's header for the definition and
+the passages each step follows).  This module only builds it with gcc and
+marshals arguments through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags: tuple = ()) -> str:
+    """Compile ``oracle.c`` into a shared library with gcc and return its path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", *extra_flags, src,
+           "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it first if it is missing)."""
+    global _lib
+    if path is None:
+        if _lib is not None:
+            return _lib
+        path = _LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
+    lib.ck_oracle_attn.restype = ctypes.c_int
+    lib.ck_oracle_attn.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.ck_oracle_nthreads_default.restype = ctypes.c_int
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _bits(a) -> np.ndarray:
+    """bf16 data as a contiguous uint16 numpy array of its bit patterns."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            if a.dtype != torch.bfloat16:
+                raise TypeError("oracle inputs must be bfloat16 tensors or uint16 bit arrays")
+            return np.ascontiguousarray(a.detach().cpu().contiguous().view(torch.int16).numpy()
+                                        .view(np.uint16))
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle inputs must be bfloat16 tensors or uint16 bit arrays")
+    return np.ascontiguousarray(a)
+
+
+def _np(a, dtype) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def attn(q, k_cache, v_cache, kv_lens, scale: float, causal: bool = False, keep_mask=None,
+         idx=None, idx_head_stride: int | None = None, num_splits: int = 0,
+         nthreads: int = 0, lib=None):
+    """Masked softmax attention in fp64 over the visible cells.
+
+    q [B, n_q, Hq, D], k_cache / v_cache [B, cap, Hkv, D] (bf16 tensors or
+    uint16 bit arrays), kv_lens [B] int32, keep_mask [B, n_q, Hkv, cap] uint8
+    or None, idx [B, n_q, Hkv, W] or [B, n_q, W] int32 or None.
+    Returns (out [B, n_q, Hq, D] float64, lse [B, n_q, Hq] float64).
+    """
+    lib = lib or load()
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    B, n_q, Hq, D = qb.shape
+    Bk, cap, Hkv, Dk = kb.shape
+    if vb.shape != kb.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k_cache and v_cache")
+    lens = _np(kv_lens, np.int32).reshape(-1)
+    if lens.shape[0] != B:
+        raise ValueError("kv_lens must have B entries")
+    mask_arr = None
+    if keep_mask is not None:
+        mask_arr = _np(keep_mask, np.uint8)
+        if mask_arr.shape != (B, n_q, Hkv, cap):
+            raise ValueError("keep_mask must be [B, n_q, Hkv, cap]")
+    idx_arr, W, hs = None, 0, 0
+    if idx is not None:
+        idx_arr = _np(idx, np.int32)
+        if idx_arr.ndim == 3:
+            if idx_arr.shape[:2] != (B, n_q):
+                raise ValueError("shared idx must be [B, n_q, W]")
+            W, hs = idx_arr.shape[2], 0
+        elif idx_arr.ndim == 4:
+            if idx_arr.shape[:3] != (B, n_q, Hkv):
+                raise ValueError("idx must be [B, n_q, Hkv, W]")
+            W = idx_arr.shape[3]
+            hs = W
+        else:
+            raise ValueError("idx must be 3-D or 4-D")
+        if idx_head_stride is not None and idx_head_stride != hs:
+            raise ValueError("idx_head_stride does not match idx's layout")
+    out = np.empty((B, n_q, Hq, D), dtype=np.float64)
+    lse = np.empty((B, n_q, Hq), dtype=np.float64)
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.ck_oracle_attn(B, n_q, Hq, Hkv, D, cap, ptr(qb), ptr(kb), ptr(vb), ptr(lens),
+                            ctypes.c_float(scale), 1 if causal else 0, ptr(mask_arr),
+                            ptr(idx_arr), W, hs, num_splits, ptr(out), ptr(lse), nthreads)
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return out, lse
+
+
+def default_threads() -> int:
+    return load().ck_oracle_nthreads_default()

@@ -1,0 +1,276 @@
+/*
+ * CPU fp64 oracle for length-aware decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header, table or helper with the HIP
+ * library: it is the plain definition of masked softmax attention, written
+ * out, with no blocking, fusion or reordering.
+ *
+ * What it computes (one result per batch entry b, query i, query head h):
+ *
+ *   g    = h / G, G = Hq / Hkv            consecutive query heads share a KV
+ *                                         head (the packed GQA group of
+ *                                         ComfyUI issue "Qwen3.5 text
+ *                                         generation attends over the full KV
+ *                                         capacity every step…", Feature Idea)
+ *   L    = clamp(kv_lens[b], 0, cap)      only the filled prefix is attended
+ *                                         (same page, Feature Idea: the
+ *                                         device-side seqlen bounds the read)
+ *   lim  = causal ? clamp(L - n_q + i + 1, 0, L) : L
+ *                                         bottom-right aligned causal window:
+ *                                         each verification query sees the
+ *                                         cache plus the drafts before it
+ *                                         (same page, Feature Idea and
+ *                                         Existing Solutions)
+ *   visible set V:
+ *     dense : { j in [0, lim) : keep_mask == NULL || keep_mask[b,i,g,j] != 0 }
+ *             in increasing j
+ *     gather: [ idx[b,i,g,t] for t in 0..W-1 if 0 <= idx < lim ] in list
+ *             order (llama.cpp PR "qwen4exp: attend the selected cells
+ *             instead of masking the window", PR body: the selected cells
+ *             are gathered into a window of their own and the mask is taken
+ *             at those cells; llama.cpp PR "qwen4exp : gather-based sparse
+ *             attention for QSA decode", Overview)
+ *   V empty -> o = 0, lse = -inf
+ *   else      s_j = scale * sum_d q[b,i,h,d] * K[b,j,g,d]
+ *             m   = max_j s_j,  e_j = exp(s_j - m),  l = sum_j e_j
+ *             o_d = sum_j e_j * V[b,j,g,d] / l,  lse = m + ln(l)
+ *
+ * Split mode (num_splits > 0) cuts V into num_splits contiguous pieces,
+ * takes (m_c, l_c, acc_c) per piece in fp64 and merges them with
+ *   M = max_c m_c,  w_c = exp(m_c - M),  o = sum_c w_c acc_c / sum_c w_c l_c,
+ * the merge that split-KV decoding relies on (comfy-kitchen PR "Performance
+ * improvements for qwen 3.x LLM (Part 1)", section GQA decode: the KV prefix
+ * is split and the splits' results are combined).  It exists to pin that
+ * algebra; it must agree with the unsplit result to rounding.
+ *
+ * Inputs are bf16 bit patterns (uint16); each is widened to fp64 exactly.
+ * scale arrives as the fp32 value the GPU receives and is widened.  Cells
+ * outside V are never read, so garbage (NaN/Inf bit patterns) there cannot
+ * reach the result.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_NOMEM (-2)
+
+static double bf16_to_f64(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    int B, n_q, Hq, Hkv, D, cap;
+    const uint16_t *q, *k, *v;
+    const int32_t *kv_lens;
+    double scale;
+    int causal;
+    const uint8_t *keep_mask;
+    const int32_t *idx;
+    int W;
+    long long idx_head_stride;
+    int num_splits;
+    double *out, *lse;
+} job_t;
+
+typedef struct {
+    const job_t *job;
+    long long unit_begin, unit_end;
+    int status;
+} worker_t;
+
+/* Visible cell list for (b, i, g), written to vis[]; returns its length. */
+static int visible_cells(const job_t *J, int b, int i, int g, int32_t *vis) {
+    long long L = J->kv_lens[b];
+    if (L < 0) L = 0;
+    if (L > J->cap) L = J->cap;
+    long long lim = L;
+    if (J->causal) {
+        lim = L - J->n_q + i + 1;
+        if (lim < 0) lim = 0;
+        if (lim > L) lim = L;
+    }
+    int n = 0;
+    if (J->idx == NULL) {
+        for (long long j = 0; j < lim; ++j) {
+            if (J->keep_mask != NULL) {
+                size_t mo = (((size_t)b * J->n_q + i) * J->Hkv + g) * (size_t)J->cap + (size_t)j;
+                if (J->keep_mask[mo] == 0) continue;
+            }
+            vis[n++] = (int32_t)j;
+        }
+    } else {
+        const int32_t *list;
+        if (J->idx_head_stride == 0)
+            list = J->idx + ((size_t)b * J->n_q + i) * (size_t)J->W;
+        else
+            list = J->idx + ((size_t)b * J->n_q + i) * (size_t)J->Hkv * (size_t)J->idx_head_stride
+                   + (size_t)g * (size_t)J->idx_head_stride;
+        for (int t = 0; t < J->W; ++t) {
+            long long j = list[t];
+            if (j >= 0 && j < lim) vis[n++] = (int32_t)j;
+        }
+    }
+    return n;
+}
+
+static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, double *acc,
+                     double *qrow) {
+    const int D = J->D;
+    const int G = J->Hq / J->Hkv;
+    int h = (int)(unit % J->Hq);
+    int i = (int)((unit / J->Hq) % J->n_q);
+    int b = (int)(unit / ((long long)J->Hq * J->n_q));
+    int g = h / G;
+
+    size_t qo = (((size_t)b * J->n_q + i) * J->Hq + h) * (size_t)D;
+    double *o = J->out + qo;
+    double *lse = J->lse ? J->lse + ((size_t)b * J->n_q + i) * J->Hq + h : NULL;
+
+    int n = visible_cells(J, b, i, g, vis);
+    if (n == 0) {
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (lse) *lse = -INFINITY;
+        return;
+    }
+    for (int d = 0; d < D; ++d) qrow[d] = bf16_to_f64(J->q[qo + d]);
+
+    /* scores over the visible list */
+    for (int t = 0; t < n; ++t) {
+        size_t ko = (((size_t)b * J->cap + (size_t)vis[t]) * J->Hkv + g) * (size_t)D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qrow[d] * bf16_to_f64(J->k[ko + d]);
+        s[t] = J->scale * dot;
+    }
+
+    int S = J->num_splits > 0 ? J->num_splits : 1;
+    double M = -INFINITY, den = 0.0;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    /* First pass: the overall max of the per-piece maxima. */
+    double *m_c = (double *)malloc(sizeof(double) * (size_t)S);
+    for (int c = 0; c < S; ++c) {
+        int t0 = (int)((long long)c * n / S), t1 = (int)((long long)(c + 1) * n / S);
+        double m = -INFINITY;
+        for (int t = t0; t < t1; ++t)
+            if (s[t] > m) m = s[t];
+        m_c[c] = m;
+        if (m > M) M = m;
+    }
+    /* Each piece: its own softmax numerator/denominator against its own max,
+       then rescaled by exp(m_c - M) into the merged result. */
+    for (int c = 0; c < S; ++c) {
+        int t0 = (int)((long long)c * n / S), t1 = (int)((long long)(c + 1) * n / S);
+        if (t1 <= t0) continue;
+        double l_c = 0.0;
+        for (int d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int t = t0; t < t1; ++t) {
+            double e = exp(s[t] - m_c[c]);
+            l_c += e;
+            size_t vo = (((size_t)b * J->cap + (size_t)vis[t]) * J->Hkv + g) * (size_t)D;
+            for (int d = 0; d < D; ++d) acc[d] += e * bf16_to_f64(J->v[vo + d]);
+        }
+        double w = exp(m_c[c] - M);
+        den += w * l_c;
+        for (int d = 0; d < D; ++d) o[d] += w * acc[d];
+    }
+    free(m_c);
+    for (int d = 0; d < D; ++d) o[d] /= den;
+    if (lse) *lse = M + log(den);
+}
+
+static void *worker_main(void *arg) {
+    worker_t *w = (worker_t *)arg;
+    const job_t *J = w->job;
+    size_t vis_cap = J->idx ? (size_t)J->W : (size_t)J->cap;
+    if (vis_cap == 0) vis_cap = 1;
+    int32_t *vis = (int32_t *)malloc(sizeof(int32_t) * vis_cap);
+    double *s = (double *)malloc(sizeof(double) * vis_cap);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)J->D);
+    double *qrow = (double *)malloc(sizeof(double) * (size_t)J->D);
+    if (!vis || !s || !acc || !qrow) {
+        w->status = ORACLE_ERR_NOMEM;
+    } else {
+        for (long long u = w->unit_begin; u < w->unit_end; ++u) one_unit(J, u, vis, s, acc, qrow);
+        w->status = ORACLE_OK;
+    }
+    free(vis);
+    free(s);
+    free(acc);
+    free(qrow);
+    return NULL;
+}
+
+int ck_oracle_nthreads_default(void) {
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+/*
+ * q  [B, n_q, Hq, D], k/v [B, cap, Hkv, D]: bf16 bit patterns, contiguous.
+ * kv_lens [B] (host).  keep_mask [B, n_q, Hkv, cap] or NULL.
+ * idx: NULL for the dense definition; else int32 lists of width W laid out
+ * [B, n_q, Hkv, idx_head_stride] (idx_head_stride >= W) or, with
+ * idx_head_stride == 0, one list per query shared by all its heads
+ * [B, n_q, W].  out [B, n_q, Hq, D] fp64; lse [B, n_q, Hq] fp64 or NULL.
+ * nthreads <= 0 uses every online host core.  Returns 0 or a negative code.
+ */
+int ck_oracle_attn(int B, int n_q, int Hq, int Hkv, int D, int cap, const uint16_t *q,
+                   const uint16_t *k, const uint16_t *v, const int32_t *kv_lens, float scale,
+                   int causal, const uint8_t *keep_mask, const int32_t *idx, int W,
+                   long long idx_head_stride, int num_splits, double *out, double *lse,
+                   int nthreads) {
+    if (B < 1 || n_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || cap < 1) return ORACLE_ERR_ARG;
+    if (Hq % Hkv != 0) return ORACLE_ERR_ARG;
+    if (!q || !k || !v || !kv_lens || !out) return ORACLE_ERR_ARG;
+    if (idx && (W < 1 || (idx_head_stride != 0 && idx_head_stride < W))) return ORACLE_ERR_ARG;
+    if (idx && keep_mask) return ORACLE_ERR_ARG;
+    if (num_splits < 0) return ORACLE_ERR_ARG;
+
+    job_t J = {B, n_q, Hq, Hkv, D, cap, q, k, v, kv_lens, (double)scale, causal ? 1 : 0,
+               keep_mask, idx, W, idx_head_stride, num_splits, out, lse};
+    long long units = (long long)B * n_q * Hq;
+    if (nthreads <= 0) nthreads = ck_oracle_nthreads_default();
+    if (nthreads > units) nthreads = (int)units;
+    if (nthreads < 1) nthreads = 1;
+
+    worker_t *ws = (worker_t *)calloc((size_t)nthreads, sizeof(worker_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!ws || !th) {
+        free(ws);
+        free(th);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        ws[t].job = &J;
+        ws[t].unit_begin = units * t / nthreads;
+        ws[t].unit_end = units * (t + 1) / nthreads;
+    }
+    int status = ORACLE_OK;
+    if (nthreads == 1) {
+        worker_main(&ws[0]);
+        status = ws[0].status;
+    } else {
+        int started = 0;
+        for (int t = 0; t < nthreads; ++t) {
+            if (pthread_create(&th[t], NULL, worker_main, &ws[t]) != 0) break;
+            ++started;
+        }
+        for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+        /* Any unit range whose thread failed to start runs here. */
+        for (int t = started; t < nthreads; ++t) worker_main(&ws[t]);
+        for (int t = 0; t < nthreads; ++t)
+            if (ws[t].status != ORACLE_OK) status = ws[t].status;
+    }
+    free(ws);
+    free(th);
+    return status;
+}

@@ -1,0 +1,258 @@
+"""Independent checks that pin the CPU oracle (shared by the oracle tests and
+the mutation test, which runs them against deliberately broken copies).
+
+Nothing here re-types the oracle's formula.  Each check compares it with
+something fixed from outside it:
+  * torch's scaled_dot_product_attention and logsumexp in float64 (a library
+    routine) with an explicit boolean mask, K/V expanded over the GQA group;
+  * closed forms (uniform V, one visible key, K = 0, two keys);
+  * invariants (split count, gather vs mask, causal row vs a shorter plain
+    decode, head permutation within a group, duplicate cells).
+Every check returns the largest deviation it saw, so a caller can assert a
+bound or, for a planted mistake, that some bound is broken.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_flash_amd import synth
+
+TOL = 1e-12
+
+
+def f64(x: torch.Tensor) -> torch.Tensor:
+    return x.to(torch.float64)
+
+
+def sdpa_reference(q, k, v, kv_lens, scale, causal, keep_mask=None, idx=None, bias=None):
+    """Attention by torch SDPA (float64, CPU) with an explicit boolean mask.
+
+    Returns (out [B, n_q, Hq, D], lse [B, n_q, Hq]) with fully masked rows set
+    to 0 / -inf (SDPA itself yields NaN there).  ``idx`` lists must hold
+    distinct cells, since a boolean mask can express a set only; ``bias`` is
+    an optional float tensor [B, n_q, Hq, cap] added to visible scores.
+    """
+    B, n_q, Hq, D = q.shape
+    _, cap, Hkv, _ = k.shape
+    G = Hq // Hkv
+    qd = f64(q).permute(0, 2, 1, 3)                                    # B,Hq,n_q,D
+    kd = f64(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)        # B,Hq,cap,D
+    vd = f64(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    lens = torch.as_tensor(np.asarray(kv_lens), dtype=torch.int64).clamp(0, cap)
+    j = torch.arange(cap).view(1, 1, cap)
+    i = torch.arange(n_q).view(1, n_q, 1)
+    L = lens.view(B, 1, 1)
+    lim = (L - n_q + i + 1).clamp(min=0) if causal else L.expand(B, n_q, 1)
+    lim = torch.minimum(lim, L)
+    vis = (j < lim)                                                    # B,n_q,cap
+    # cells at or past L may hold garbage (NaN/Inf): give the library zeros
+    # there, since a masked weight of 0 times NaN would still be NaN
+    filled = (torch.arange(cap).view(1, 1, cap, 1) < lens.view(B, 1, 1, 1))
+    kd = torch.where(filled, kd, torch.zeros_like(kd))
+    vd = torch.where(filled, vd, torch.zeros_like(vd))
+    vis = vis.view(B, 1, n_q, cap).expand(B, Hq, n_q, cap).clone()
+    if keep_mask is not None:
+        km = torch.as_tensor(np.asarray(keep_mask)).bool()           # B,n_q,Hkv,cap
+        km = km.permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+        vis &= km
+    if idx is not None:
+        idx = np.asarray(idx)
+        sel = torch.zeros((B, Hq, n_q, cap), dtype=torch.bool)
+        for b in range(B):
+            for ii in range(n_q):
+                for h in range(Hq):
+                    lst = idx[b, ii] if idx.ndim == 3 else idx[b, ii, h // G]
+                    lst = lst[(lst >= 0) & (lst < cap)]
+                    sel[b, h, ii, torch.as_tensor(lst, dtype=torch.int64)] = True
+        vis &= sel
+    mask = vis
+    if bias is not None:
+        fb = f64(torch.as_tensor(bias)).permute(0, 2, 1, 3)
+        mask = torch.where(vis, fb, torch.full_like(fb, -math.inf))
+    out = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask,
+                                                         scale=float(scale))
+    scores = torch.matmul(qd, kd.transpose(-1, -2).contiguous()) * float(scale)
+    if bias is not None:
+        scores = scores + torch.where(vis, fb, torch.zeros_like(fb))
+    scores = scores.masked_fill(~vis, -math.inf)
+    lse = torch.logsumexp(scores, dim=-1)
+    empty = ~vis.any(dim=-1)
+    out = torch.where(empty.unsqueeze(-1), torch.zeros_like(out), out)
+    lse = torch.where(empty, torch.full_like(lse, -math.inf), lse)
+    return out.permute(0, 2, 1, 3).numpy(), lse.permute(0, 2, 1).numpy()
+
+
+def max_dev(a, b) -> float:
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    both_ninf = np.isneginf(a) & np.isneginf(b)
+    if np.any(np.isnan(a)) or np.any(np.isnan(b)):
+        return math.inf
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_ninf, 0.0, np.abs(a - b))
+    return float(np.max(d)) if d.size else 0.0
+
+
+def small_case(B=2, n_q=3, Hq=4, Hkv=2, D=16, cap=40, lens=(37, 5), seed=0, garbage=True):
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, seed, garbage=garbage)
+    q = synth.queries(B, n_q, Hq, D, seed)
+    return q, k, v, np.asarray(lens, dtype=np.int32)
+
+
+# ---------------------------------------------------------------- checks ----
+
+def check_sdpa_dense(lib) -> float:
+    worst = 0.0
+    for causal in (False, True):
+        for D in (4, 16):
+            q, k, v, lens = small_case(D=D, lens=(37, 2), seed=D + causal)
+            scale = 1.0 / math.sqrt(D)
+            o, l = oracle.attn(q, k, v, lens, scale, causal, lib=lib)
+            ro, rl = sdpa_reference(q, k, v, lens, np.float32(scale), causal)
+            worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    return worst
+
+
+def check_sdpa_mask(lib) -> float:
+    q, k, v, lens = small_case(seed=3)
+    rng = np.random.default_rng(3)
+    km = (rng.random((2, 3, 2, 40)) < 0.5).astype(np.uint8)
+    worst = 0.0
+    for causal in (False, True):
+        o, l = oracle.attn(q, k, v, lens, 0.25, causal, keep_mask=km, lib=lib)
+        ro, rl = sdpa_reference(q, k, v, lens, np.float32(0.25), causal, keep_mask=km)
+        worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    return worst
+
+
+def gather_lists(B, n_q, Hkv, cap, W, seed, shared=False):
+    """Distinct cells per list, including out-of-range entries (-3, cap + 2)
+    and the boundary cells 0, L-1 and L of a causal limit."""
+    rng = np.random.default_rng(seed)
+    shape = (B, n_q, W) if shared else (B, n_q, Hkv, W)
+    out = np.empty(shape, dtype=np.int32)
+    for pos in np.ndindex(*shape[:-1]):
+        cells = rng.choice(cap, size=W - 2, replace=False).astype(np.int32)
+        out[pos] = np.concatenate([cells, np.array([-3, cap + 2], dtype=np.int32)])
+        rng.shuffle(out[pos])
+    return out
+
+
+def check_sdpa_gather(lib) -> float:
+    q, k, v, lens = small_case(seed=5)
+    worst = 0.0
+    for shared in (False, True):
+        for causal in (False, True):
+            idx = gather_lists(2, 3, 2, 40, 12, seed=7 + shared, shared=shared)
+            o, l = oracle.attn(q, k, v, lens, 0.3, causal, idx=idx, lib=lib)
+            ro, rl = sdpa_reference(q, k, v, lens, np.float32(0.3), causal, idx=idx)
+            worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    # a list that names every cell up to and including the causal limit of
+    # each query: the entry at the limit itself must be dropped
+    B, n_q, cap = 1, 3, 40
+    q1, k1, v1, _ = small_case(B=1, lens=(20,), seed=11)
+    lens1 = np.array([20], dtype=np.int32)
+    idx = np.tile(np.arange(0, 24, dtype=np.int32), (1, n_q, 2, 1))
+    o, l = oracle.attn(q1, k1, v1, lens1, 0.3, True, idx=idx, lib=lib)
+    ro, rl = sdpa_reference(q1, k1, v1, lens1, np.float32(0.3), True, idx=idx)
+    return max(worst, max_dev(o, ro), max_dev(l, rl))
+
+
+def check_duplicates(lib) -> float:
+    """A cell listed twice weighs twice: the same as adding ln 2 to its score."""
+    q, k, v, lens = small_case(B=1, lens=(30,), seed=13)
+    lens = np.array([30], dtype=np.int32)
+    base = np.array([1, 4, 9, 16, 25, 29], dtype=np.int32)
+    lst = np.concatenate([base, base[[2]]])
+    idx = np.tile(lst, (1, 3, 2, 1))
+    o, l = oracle.attn(q, k, v, lens, 0.3, False, idx=idx, lib=lib)
+    bias = np.zeros((1, 3, 4, 40))
+    bias[..., 9] = math.log(2.0)
+    ro, rl = sdpa_reference(q, k, v, lens, np.float32(0.3), False,
+                            idx=np.tile(base, (1, 3, 2, 1)), bias=bias)
+    return max(max_dev(o, ro), max_dev(l, rl))
+
+
+def check_closed_forms(lib) -> float:
+    worst = 0.0
+    B, n_q, Hq, Hkv, D, cap = 1, 2, 4, 2, 8, 16
+    q = synth.queries(B, n_q, Hq, D, 21)
+    k, _ = synth.kv_cache(B, cap, Hkv, D, [12], 21)
+    lens = np.array([12], dtype=np.int32)
+    # uniform V: every visible row equals the same vector -> output is that vector
+    row = synth.bf16_normal((Hkv, D), synth.generator(5))
+    v = row.view(1, 1, Hkv, D).expand(B, cap, Hkv, D).contiguous()
+    o, _ = oracle.attn(q, k, v, lens, 0.5, True, lib=lib)
+    expect = f64(row).repeat_interleave(Hq // Hkv, dim=0).numpy()
+    worst = max(worst, max_dev(o[0, 0], expect), max_dev(o[0, 1], expect))
+    # one visible key: output is exactly its V row, lse is exactly its score
+    k2, v2 = synth.kv_cache(B, cap, Hkv, D, [1], 22)
+    o, l = oracle.attn(q, k2, v2, np.array([1], np.int32), 0.5, False, lib=lib)
+    for h in range(Hq):
+        worst = max(worst, max_dev(o[0, 0, h], f64(v2[0, 0, h // 2]).numpy()))
+        sc = 0.5 * float(np.dot(f64(q[0, 0, h]).numpy(), f64(k2[0, 0, h // 2]).numpy()))
+        worst = max(worst, abs(l[0, 0, h] - sc))
+    # K = 0: uniform weights -> mean of the visible V rows, lse = ln(n)
+    kz = torch.zeros_like(k)
+    _, v3 = synth.kv_cache(B, cap, Hkv, D, [12], 23)
+    o, l = oracle.attn(q, kz, v3, lens, 0.5, False, lib=lib)
+    mean = f64(v3[0, :12]).mean(dim=0).repeat_interleave(2, dim=0).numpy()
+    worst = max(worst, max_dev(o[0, 0], mean), float(np.max(np.abs(l - math.log(12)))))
+    # two keys with score gap delta: o = sigma(delta) v1 + (1 - sigma(delta)) v2
+    o, l = oracle.attn(q, k, v3, np.array([2], np.int32), 0.5, False, lib=lib)
+    for h in range(Hq):
+        qh = f64(q[0, 0, h]).numpy()
+        s1 = 0.5 * float(np.dot(qh, f64(k[0, 0, h // 2]).numpy()))
+        s2 = 0.5 * float(np.dot(qh, f64(k[0, 1, h // 2]).numpy()))
+        sig = 1.0 / (1.0 + math.exp(-(s1 - s2)))
+        exp_o = sig * f64(v3[0, 0, h // 2]).numpy() + (1 - sig) * f64(v3[0, 1, h // 2]).numpy()
+        worst = max(worst, max_dev(o[0, 0, h], exp_o))
+        lse2 = max(s1, s2) + math.log1p(math.exp(-abs(s1 - s2)))
+        worst = max(worst, abs(l[0, 0, h] - lse2))
+    return worst
+
+
+def check_split_invariance(lib) -> float:
+    q, k, v, lens = small_case(D=16, lens=(37, 29), seed=31)
+    ref, rl = oracle.attn(q, k, v, lens, 0.25, True, lib=lib)
+    worst = 0.0
+    for S in (1, 2, 7, 64):
+        o, l = oracle.attn(q, k, v, lens, 0.25, True, num_splits=S, lib=lib)
+        worst = max(worst, max_dev(o, ref), max_dev(l, rl))
+    return worst
+
+
+def check_causal_rows(lib) -> float:
+    """Causal row i equals a plain single-query decode of length L - n_q + i + 1."""
+    q, k, v, lens = small_case(D=16, lens=(37, 5), seed=41)
+    n_q = q.shape[1]
+    o, l = oracle.attn(q, k, v, lens, 0.25, True, lib=lib)
+    worst = 0.0
+    for i in range(n_q):
+        li = np.maximum(lens - n_q + i + 1, 0).astype(np.int32)
+        oi, lsi = oracle.attn(q[:, i:i + 1].contiguous(), k, v, li, 0.25, False, lib=lib)
+        worst = max(worst, max_dev(o[:, i], oi[:, 0]), max_dev(l[:, i], lsi[:, 0]))
+    return worst
+
+
+def check_head_permutation(lib) -> float:
+    q, k, v, lens = small_case(Hq=6, Hkv=2, D=8, seed=51)
+    o, _ = oracle.attn(q, k, v, lens, 0.3, False, lib=lib)
+    perm = torch.tensor([2, 0, 1, 4, 5, 3])            # permutes within each group of 3
+    op, _ = oracle.attn(q[:, :, perm].contiguous(), k, v, lens, 0.3, False, lib=lib)
+    return max_dev(op, o[:, :, perm.numpy()])
+
+
+ALL_CHECKS = {
+    "sdpa_dense": check_sdpa_dense,
+    "sdpa_mask": check_sdpa_mask,
+    "sdpa_gather": check_sdpa_gather,
+    "duplicates": check_duplicates,
+    "closed_forms": check_closed_forms,
+    "split_invariance": check_split_invariance,
+    "causal_rows": check_causal_rows,
+    "head_permutation": check_head_permutation,
+}
