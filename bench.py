@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Headline workload: a full-attention layer of the Hq=16 / Hkv=4 / head_dim 256
+shape at batch 1, one query, cache capacity 24007, kv_len 8000 (the shortest
+length at which the dense path is held to 70 % of HBM peak).  A timed step
+is one decode step through a stack of `layers` such layers, each with its own
+KV cache, replayed from one HIP graph; `layers` is chosen so that a step reads
+at least 1 GiB, which keeps the caches out of the 256 MB Infinity Cache.
+value = microseconds per layer-step.  The kv_len sweep, the capacity sweep,
+the causal window, the ragged batch and the gathered/masked sparse decode are
+reported in the same JSON line under "sweep".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode-attn µs/layer-step and achieved HBM GB/s (KV bytes read) vs kv_len"
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def layers_for(bytes_per_launch: int) -> int:
+    return int(min(256, max(4, math.ceil((1 << 30) / max(1, bytes_per_launch)))))
+
+
+class Stack:
+    """`n` layers of K/V caches [B, cap, Hkv, D] bf16 ~ N(0, 1), on the device."""
+
+    def __init__(self, n, B, cap, Hkv, D, seed):
+        import torch
+        self.k, self.v = [], []
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        for _ in range(n):
+            self.k.append(torch.randn((B, cap, Hkv, D), generator=g, device="cuda",
+                                      dtype=torch.bfloat16))
+            self.v.append(torch.randn((B, cap, Hkv, D), generator=g, device="cuda",
+                                      dtype=torch.bfloat16))
+
+
+def time_graph(launch_layer, n_layers, steps, warmup):
+    """Capture n_layers launches in one graph; time `steps` replays.
+    Returns (ms per replay, us per layer)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for l in range(n_layers):
+            launch_layer(l)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(n_layers):
+            launch_layer(l)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graph
+    return ms, ms * 1000.0 / n_layers
+
+
+def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_layers=None,
+               masks=None):
+    import torch
+    import decode_attention_flash_amd as ck
+    from decode_attention_flash_amd import synth
+    kv_bytes = int(sum(4 * Hkv * D * min(int(L), stack.k[0].shape[1]) for L in lens))
+    if masks is not None:
+        kv_bytes_mask = int(sum(n_q * Hkv * int(L) for L in lens))
+    else:
+        kv_bytes_mask = 0
+    n = n_layers or layers_for(kv_bytes)
+    n = min(n, len(stack.k))
+    qs = [synth.queries(B, n_q, Hq, D, 7 + l, device="cuda") for l in range(n)]
+    outs = [torch.empty((B, n_q, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
+    shape = ck.shape_of(qs[0], stack.k[0])
+    ws = ck.new_workspace(shape)
+
+    def launch(l):
+        ck.decode_attn(qs[l], stack.k[l], stack.v[l], lens_d, causal=causal, out=outs[l],
+                       workspace=ws, keep_mask=None if masks is None else masks[l])
+
+    ms, us = time_graph(launch, n, steps, warmup)
+    algo = kv_bytes + kv_bytes_mask + 2 * B * n_q * Hq * D + 4 * B * n_q * Hq * D + 4 * B
+    return dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, algo_bytes=algo,
+                kv_gbs=kv_bytes / us / 1e3, algo_gbs=algo / us / 1e3,
+                frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
+
+
+def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None):
+    import numpy as np
+    import torch
+    import decode_attention_flash_amd as ck
+    from decode_attention_flash_amd import synth
+    B, n_q, Hq, Hkv, D = 1, 1, 16, 2, 128
+    W = W_sel + tail
+    kv_bytes = B * n_q * Hkv * W * 4 * D
+    n = min(n_layers or layers_for(kv_bytes), len(stack.k))
+    qs = [synth.queries(B, n_q, Hq, D, 11 + l, device="cuda") for l in range(n)]
+    outs = [torch.empty((B, n_q, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+    idxs = [torch.from_numpy(synth.topk_lists(B, n_q, Hkv, n_kv, W_sel, tail, seed=5000 + n_kv + l))
+            .to("cuda") for l in range(n)]
+    lens_d = torch.full((B,), n_kv, dtype=torch.int32, device="cuda")
+    shape = ck.shape_of(qs[0], stack.k[0])
+    ws = ck.new_workspace(shape, W=W)
+
+    def launch(l):
+        ck.decode_attn_gather(qs[l], stack.k[l], stack.v[l], lens_d, idxs[l], out=outs[l],
+                              workspace=ws)
+
+    ms, us = time_graph(launch, n, steps, warmup)
+    algo = kv_bytes + 4 * W * Hkv + 6 * B * n_q * Hq * D + 4
+    return dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, algo_bytes=algo,
+                kv_gbs=kv_bytes / us / 1e3, frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS), idxs
+
+
+def cpu_baseline(seconds: float):
+    """The oracle on the host cores: full layer-steps of the headline workload."""
+    import numpy as np
+    import oracle
+    from decode_attention_flash_amd import synth
+    B, n_q, Hq, Hkv, D, cap, L = 1, 1, 16, 4, 256, 24007, 8000
+    k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1002)
+    q = synth.queries(B, n_q, Hq, D, 1002)
+    lens = np.array([L], dtype=np.int32)
+    threads = min(B * n_q * Hq, oracle.default_threads())
+    oracle.attn(q, k, v, lens, 1 / math.sqrt(D), nthreads=threads)  # warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attn(q, k, v, lens, 1 / math.sqrt(D), nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": el / reps * 1e6, "unit": "us/layer-step", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full layer-steps of the headline workload (B=1, Hq=16, Hkv=4, "
+                      f"D=256, kv_len={L}, cap={cap}), fp64, {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kv-len", type=int, default=8000)
+    ap.add_argument("--headline-only", action="store_true", help="skip the sweeps and the CPU leg")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library's kernels run on a single device "
+              "and there is no multi-GPU path to time (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_flash_amd as ck
+    ck.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    Hq, Hkv, D, cap = 16, 4, 256, 24007
+    L0 = args.kv_len
+    lens_sweep = [1000, 3000, 8000, 24000]
+    n_max = 4 if args.headline_only else max(layers_for(4 * Hkv * D * L) for L in lens_sweep + [L0])
+    n_max = max(n_max, layers_for(4 * Hkv * D * L0))
+    log(f"allocating {n_max} layer caches of capacity {cap}")
+    stack = Stack(n_max, 1, cap, Hkv, D, 1002)
+
+    log(f"headline: kv_len={L0}")
+    head = dense_case(stack, 1, 1, Hq, Hkv, D, [L0], args.steps, args.warmup)
+    log(f"headline: {head['us']:.2f} us/layer-step, {head['kv_gbs']:.0f} GB/s on KV bytes")
+
+    sweep = {}
+    if not args.headline_only:
+        sweep["kv_len"] = []
+        for L in lens_sweep:
+            r = dense_case(stack, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup)
+            log(f"kv_len {L}: {r['us']:.2f} us, {r['kv_gbs']:.0f} GB/s")
+            sweep["kv_len"].append(dict(kv_len=L, cap=cap, **r))
+        sweep["causal_window"] = []
+        for L in (2000, 4000):
+            for n_q in (3, 4, 5, 6):
+                r = dense_case(stack, 1, n_q, Hq, Hkv, D, [L], args.steps, args.warmup, causal=True)
+                log(f"window n_q={n_q} L={L}: {r['us']:.2f} us")
+                sweep["causal_window"].append(dict(kv_len=L, n_q=n_q, **r))
+        del stack
+        torch.cuda.empty_cache()
+        sweep["capacity"] = []
+        for c in (8199, 16263, 24007):
+            n = layers_for(4 * Hkv * D * 3000)
+            st = Stack(n, 1, c, Hkv, D, 2000 + c)
+            r = dense_case(st, 1, 1, Hq, Hkv, D, [3000], args.steps, args.warmup)
+            log(f"cap {c} L=3000: {r['us']:.2f} us")
+            sweep["capacity"].append(dict(kv_len=3000, cap=c, **r))
+            del st
+            torch.cuda.empty_cache()
+        # ragged batch: B=32, Hq=32, Hkv=8, D=128, capacity 32768
+        from decode_attention_flash_amd import synth
+        lens = synth.ragged_lens(32, 512, 32768, 4000)
+        st = Stack(4, 32, 32768, 8, 128, 1004)
+        r = dense_case(st, 32, 1, 32, 8, 128, lens.tolist(), max(3, args.steps // 4), 2, n_layers=4)
+        log(f"ragged B=32: {r['us']:.1f} us, {r['kv_gbs']:.0f} GB/s")
+        sweep["ragged_batch"] = dict(B=32, sum_kv_len=int(lens.sum()), **r)
+        del st
+        torch.cuda.empty_cache()
+        # sparse: gathered top-k lists vs the masked full-window scan
+        sweep["sparse"] = []
+        for n_kv in (32768, 65536, 131072):
+            W_sel, tail = 2048, 64
+            n_g = layers_for(2 * (W_sel + tail) * 4 * 128)
+            n_m = layers_for(4 * 2 * 128 * n_kv)
+            st = Stack(max(n_g, n_m), 1, n_kv, 2, 128, 1005)
+            rg, idxs = gather_case(st, n_kv, W_sel, tail, args.steps, args.warmup)
+            masks = [torch.from_numpy(synth.mask_from_lists(idxs[l].cpu().numpy(), n_kv)).to("cuda")
+                     for l in range(n_m)]
+            rm = dense_case(st, 1, 1, 16, 2, 128, [n_kv], args.steps, args.warmup, n_layers=n_m,
+                            masks=masks)
+            log(f"sparse n_kv={n_kv}: gather {rg['us']:.2f} us, masked {rm['us']:.2f} us")
+            sweep["sparse"].append(dict(n_kv=n_kv, gather=rg, masked=rm))
+            del st, masks
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu and not args.headline_only:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["us"], 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_replay"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode layer B=1 n_q=1 Hq={Hq} Hkv={Hkv} D={D} cap={cap} "
+                               f"kv_len={L0}, {head['layers']} layer caches per step (cold)",
+                   "B": 1, "n_q": 1, "Hq": Hq, "Hkv": Hkv, "D": D, "cap": cap, "kv_len": L0,
+                   "layers_per_step": head["layers"], "parallelism": "none"},
+        "hbm_gbs_kv": round(head["kv_gbs"], 1),
+        "frac_of_peak_kv": round(head["frac_kv"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(head["algo_gbs"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(head["algo_gbs"] / PEAK_HBM_GBS, 4),
+                     "traffic": None, "kernel": "decode_kernel<256,1,0>",
+                     "algo_bytes_per_launch": head["algo_bytes"]},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

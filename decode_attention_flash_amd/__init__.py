@@ -1,0 +1,228 @@
+"""Python binding of the ck_decode_attn C ABI (argument marshalling only).
+
+Every step of the attention runs in the HIP kernels of
+``libck_decode_attn.so``; torch only supplies device memory and the current
+stream.  There is no fallback: if the library is missing, importing the
+entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libck_decode_attn.so")
+
+CK_DT_F32 = 0
+CK_DT_BF16 = 1
+CK_MAX_NQ = 6
+CK_MAX_SPLITS = 256
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misaligned pointer",
+          -4: "workspace missing or too small", -5: "HIP runtime error"}
+EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_workspace_size",
+           "ck_decode_attn_plan", "ck_status_string")
+
+
+class CkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("n_q", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("cap", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("units", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("split_target", ctypes.c_int32), ("chunk_max", ctypes.c_int32),
+                ("granule", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("row_groups", ctypes.c_int32), ("rows_per_group", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run decode_attention_flash_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sp = ctypes.POINTER(Shape)
+        L.ck_decode_attn_plan.argtypes = [sp, i32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Plan)]
+        L.ck_decode_attn_plan.restype = ctypes.c_int
+        L.ck_decode_attn_workspace_size.argtypes = [sp, i32, ctypes.c_int, ctypes.POINTER(sz)]
+        L.ck_decode_attn_workspace_size.restype = ctypes.c_int
+        L.ck_decode_attn.argtypes = [sp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
+                                     ctypes.c_int, vp, vp, sz, ctypes.c_int, vp]
+        L.ck_decode_attn.restype = ctypes.c_int
+        L.ck_decode_attn_gather.argtypes = [sp, vp, vp, vp, vp, vp, i32, i64, ctypes.c_float,
+                                            ctypes.c_int, vp, ctypes.c_int, vp, vp, sz,
+                                            ctypes.c_int, vp]
+        L.ck_decode_attn_gather.restype = ctypes.c_int
+        L.ck_status_string.argtypes = [ctypes.c_int]
+        L.ck_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def shape_of(q: torch.Tensor, k_cache: torch.Tensor) -> Shape:
+    B, n_q, Hq, D = q.shape
+    Bk, cap, Hkv, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k_cache {tuple(k_cache.shape)} disagree")
+    return Shape(B, n_q, Hq, Hkv, D, cap)
+
+
+def plan(shape: Shape, W: int = 0, num_splits: int = 0, num_cus: int | None = None) -> dict:
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    p = Plan()
+    st = lib().ck_decode_attn_plan(ctypes.byref(shape), W, num_splits, num_cus, ctypes.byref(p))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn_plan")
+    return p.as_dict()
+
+
+def workspace_size(shape: Shape, W: int = 0, num_splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().ck_decode_attn_workspace_size(ctypes.byref(shape), W, num_splits, ctypes.byref(n))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn_workspace_size")
+    return n.value
+
+
+def new_workspace(shape: Shape, W: int = 0, num_splits: int = 0, device=None) -> torch.Tensor | None:
+    """A zeroed workspace for this plan (None when none is needed).  Keep one
+    per stream and plan: launches leave its counters zeroed, so it can be
+    reused and captured, but another plan needs its own (or a re-zeroed) one."""
+    n = workspace_size(shape, W, num_splits)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
+_ws_cache: dict = {}
+
+
+def _cached_workspace(shape: Shape, W: int, num_splits: int, device) -> torch.Tensor | None:
+    n = workspace_size(shape, W, num_splits)
+    if n == 0:
+        return None
+    # a workspace belongs to one plan: its counters are laid out for it
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream,
+           tuple(getattr(shape, f) for f, _ in Shape._fields_), W, num_splits)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.zeros(n, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _check(t: torch.Tensor, name: str, dtype) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse):
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    _check(q, "q", torch.bfloat16)
+    _check(k_cache, "k_cache", torch.bfloat16)
+    _check(v_cache, "v_cache", torch.bfloat16)
+    _check(kv_lens, "kv_lens", torch.int32)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    shape = shape_of(q, k_cache)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _check(out, "out", out_dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check(lse, "lse", torch.float32)
+    odt = CK_DT_BF16 if out_dtype == torch.bfloat16 else CK_DT_F32
+    return shape, out, lse, odt
+
+
+def decode_attn(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, causal: bool = False,
+                keep_mask=None, out_dtype=torch.float32, out=None, lse=None, return_lse=False,
+                workspace=None, num_splits: int = 0, stream=None):
+    """Dense length-aware decode attention (``ck_decode_attn``).
+
+    q [B, n_q, Hq, D] bf16, k_cache / v_cache [B, cap, Hkv, D] bf16,
+    kv_lens [B] int32 (device), keep_mask [B, n_q, Hkv, cap] uint8 or None.
+    Returns out (and lse [B, n_q, Hq] fp32 when return_lse or lse is given).
+    """
+    shape, out, lse, odt = _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse)
+    if keep_mask is not None:
+        _check(keep_mask, "keep_mask", torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if workspace is None:
+        workspace = _cached_workspace(shape, 0, num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().ck_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(kv_lens), ctypes.c_float(scale), 1 if causal else 0,
+                              _ptr(keep_mask), _ptr(out), odt, _ptr(lse), _ptr(workspace),
+                              ws_bytes, num_splits, ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_attn_gather(q, k_cache, v_cache, kv_lens, idx, *, scale: float | None = None,
+                       causal: bool = False, out_dtype=torch.float32, out=None, lse=None,
+                       return_lse=False, workspace=None, num_splits: int = 0, stream=None):
+    """Gathered decode attention over per-query index lists
+    (``ck_decode_attn_gather``).  idx is int32 [B, n_q, Hkv, W] (one list per
+    query and KV head) or [B, n_q, W] (one list per query, shared by heads)."""
+    shape, out, lse, odt = _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse)
+    _check(idx, "idx", torch.int32)
+    if idx.dim() == 4:
+        if tuple(idx.shape[:3]) != (shape.B, shape.n_q, shape.Hkv):
+            raise ValueError("idx must be [B, n_q, Hkv, W]")
+        W = idx.shape[3]
+        head_stride = W
+    elif idx.dim() == 3:
+        if tuple(idx.shape[:2]) != (shape.B, shape.n_q):
+            raise ValueError("shared idx must be [B, n_q, W]")
+        W = idx.shape[2]
+        head_stride = 0
+    else:
+        raise ValueError("idx must be 3-D or 4-D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if workspace is None:
+        workspace = _cached_workspace(shape, W, num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().ck_decode_attn_gather(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(kv_lens), _ptr(idx), W, head_stride,
+                                     ctypes.c_float(scale), 1 if causal else 0, _ptr(out), odt,
+                                     _ptr(lse), _ptr(workspace), ws_bytes, num_splits,
+                                     ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn_gather")
+    return (out, lse) if (return_lse or lse is not None) else out

@@ -1,0 +1,778 @@
+// Length-aware split-KV GQA decode attention for gfx950 (MI355X).
+//
+// One workgroup (4 waves of 64 lanes) takes one (unit, split): a unit is a
+// (sequence, [query,] KV head, row group), a split is a contiguous range of
+// cache positions (dense) or of index-list entries (gather).  The query
+// rows of the unit -- the GQA group's query heads times the causal window's
+// queries -- ride as the N side of 16x16x32 bf16 MFMAs against 16-token
+// tiles of K, so every K/V byte is read once for all of them (comfy-kitchen
+// PR "Performance improvements for qwen 3.x LLM (Part 1)", GQA decode).
+// Only positions below the device-side length are read (ComfyUI issue
+// "Qwen3.5 text generation attends over the full KV capacity every step…",
+// Feature Idea), an online softmax runs per split, and the workgroup that
+// finishes a unit's last split merges the splits in the same launch (same
+// comfy-kitchen PR, GQA decode), so the launch has a fixed shape.
+//
+// Per wave and tile (TT tokens, TT*D*2 = 16 KiB of K):
+//   K   : buffer loads straight into MFMA A-operand registers (lane l holds
+//         token l%16 of a 16-token block, 8 consecutive head-dim values);
+//         rows past the split or the visible limit come back as zeros from
+//         the buffer range check, so garbage is never read.
+//   S^T = K Q^T on MFMA, C layout: lane l holds query row l%16 and tokens
+//         4*(l/16)+0..3 of each 16-token block.
+//   softmax on those registers; P^T for PV is the same registers rounded to
+//         bf16 (token order inside the 32-token k-block is permuted the same
+//         way on both operands, which leaves the contraction unchanged).
+//   V   : row-major buffer loads, staged in LDS, read back transposed
+//         (lane: head-dim column l%16, 8 tokens) as the A operand of
+//         O^T += V^T P^T, whose C layout again gives lane l query row l%16.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "ck_decode_attn.h"
+
+namespace ckda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer descriptor, dword data format
+constexpr uint32_t kOOB = 0x80000000u;        // an offset beyond every range we build
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int D>
+struct Geo {
+    static constexpr int TT = 16384 / (2 * D);  // tokens per wave tile
+    static constexpr int MB = TT / 16;          // 16-token blocks per tile (QK M side)
+    static constexpr int KS = D / 32;           // k-steps of the QK contraction
+    static constexpr int KB = TT / 32;          // 32-token k-blocks of PV
+    static constexpr int NB = D / 16;           // 16-wide head-dim blocks of PV
+    static constexpr int CPR = D / 8;           // 16-byte chunks per cache row
+    static constexpr int RPI = 64 / CPR;        // cache rows per V load instruction
+    static constexpr int VI = TT / RPI;         // V load instructions per tile
+    static constexpr int RS = 2 * D + 8;        // LDS row stride in bytes (bank skew)
+    static constexpr int VBYTES = TT * RS;      // LDS bytes per wave for staged V
+};
+
+struct KParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* kv_lens;
+    const uint8_t* keep_mask;
+    const int32_t* idx;
+    void* out;
+    float* lse;
+    float* ws_o;
+    float* ws_ml;
+    int32_t* ws_cnt;
+    int32_t B, n_q, Hq, Hkv, G, cap;
+    int32_t R, RG, rows_alloc;
+    int32_t splits;  // grid splits per unit
+    int32_t S_target, c_max, gran;
+    int32_t W;
+    int64_t idx_head_stride;  // 0: one list per query shared by its heads
+    float scale_log2;         // softmax scale times log2(e)
+    int32_t causal, out_bf16;
+    uint32_t row_bytes;  // bytes between consecutive positions of one head
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Orders this wave's LDS writes before its later LDS reads (and the reverse)
+// without waiting on outstanding global loads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Length of the range one split takes; the same arithmetic runs in every
+// workgroup of a unit, so they agree on the split count.  It never yields
+// more splits than the grid holds.
+__device__ __forceinline__ int chunk_len(int span, const KParams& p) {
+    int c = (span + p.S_target - 1) / p.S_target;
+    c = (c + p.gran - 1) / p.gran * p.gran;
+    if (c < p.gran) c = p.gran;
+    if (p.c_max > 0 && c > p.c_max) c = p.c_max;
+    int need = (span + p.splits - 1) / p.splits;
+    need = (need + p.gran - 1) / p.gran * p.gran;
+    return c < need ? need : c;
+}
+
+template <int D, int RT>
+struct Acc {
+    f32x4 o[RT][D / 16];
+    float m[RT], l[RT];
+};
+
+// Merge a second softmax state (m2, l2, o2) into (m, l, o); both are in the
+// log2 domain.  Fully masked states have m = -inf and contribute nothing.
+__device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float& w2, float& m) {
+    m = fmaxf(m1, m2);
+    float mu = (m == -INFINITY) ? 0.f : m;
+    w1 = fast_exp2(m1 - mu);
+    w2 = fast_exp2(m2 - mu);
+}
+
+// Output row for packed row r of this unit: returns the flat (b, i, h) index.
+__device__ __forceinline__ size_t out_row(const KParams& p, int b, int g, int r, int iq, bool gather) {
+    int i = gather ? iq : r / p.G;
+    int j = gather ? r : r % p.G;
+    int h = g * p.G + j;
+    return ((size_t)b * p.n_q + i) * p.Hq + h;
+}
+
+template <int D>
+__device__ __forceinline__ void store4(const KParams& p, size_t row, int d, f32x4 v) {
+    if (p.out_bf16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 h;
+        h[0] = (__bf16)v[0];
+        h[1] = (__bf16)v[1];
+        h[2] = (__bf16)v[2];
+        h[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.out) + row * D + d) = h;
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + d) = v;
+    }
+}
+
+// MODE 0: dense, 1: dense with keep_mask, 2: gather.
+template <int D, int RT, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
+    using Gm = Geo<D>;
+    constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
+    constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS;
+    constexpr bool GATHER = (MODE == 2);
+    static_assert(2 * RT * NB * 64 * 16 <= kWaves * Gm::VBYTES, "merge area exceeds LDS");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::VBYTES];
+    __shared__ float s_ml[2][RT][64][2];
+    __shared__ float s_rowM[32], s_rowDen[32];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int s = blockIdx.x % p.splits;
+    const int unit = blockIdx.x / p.splits;
+    int t = unit;
+    const int rg = t % p.RG;
+    t /= p.RG;
+    const int g = t % p.Hkv;
+    t /= p.Hkv;
+    int b, iq = 0;
+    if constexpr (GATHER) {
+        iq = t % p.n_q;
+        b = t / p.n_q;
+    } else {
+        b = t;
+    }
+
+    int L = p.kv_lens[b];
+    L = L < 0 ? 0 : (L > p.cap ? p.cap : L);
+    const int span = GATHER ? p.W : L;
+    const int C = chunk_len(span, p);
+    const int n_active = span > 0 ? (span + C - 1) / C : 1;
+    if (s >= n_active) return;
+    const int pos_begin = s * C;
+    const int pos_end = min(pos_begin + C, span);
+
+    const int row0 = rg * p.rows_alloc;
+    const int nrows = min(p.rows_alloc, p.R - row0);
+
+    // ---- per-lane query rows --------------------------------------------
+    int lim_r[RT];
+    int i_r[RT];
+    bf16x8 qreg[RT][KS];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rr = rt * 16 + l16;
+        const bool ok = rr < nrows;
+        const int r = row0 + rr;
+        const int i = GATHER ? iq : r / p.G;
+        int lim = L;
+        if (p.causal) {
+            lim = L - p.n_q + i + 1;
+            lim = lim < 0 ? 0 : (lim > L ? L : lim);
+        }
+        lim_r[rt] = ok ? lim : 0;
+        i_r[rt] = i;
+        const uint16_t* qrow = p.q + out_row(p, b, g, ok ? r : row0, iq, GATHER) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ok) {
+                qreg[rt][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * q4);
+            } else {
+                qreg[rt][ks] = bf16x8{};
+            }
+        }
+    }
+
+    // ---- cache views ------------------------------------------------------
+    const size_t head_off = ((size_t)b * p.cap * p.Hkv + g) * D;
+    int rows_lim;  // rows [0, rows_lim) of this head may be read
+    int lim_g = L;
+    const int32_t* list = nullptr;
+    if constexpr (GATHER) {
+        if (p.causal) {
+            lim_g = L - p.n_q + iq + 1;
+            lim_g = lim_g < 0 ? 0 : (lim_g > L ? L : lim_g);
+        }
+        rows_lim = lim_g;
+        const int64_t hs = p.idx_head_stride;
+        list = p.idx + ((size_t)b * p.n_q + iq) * (size_t)(hs == 0 ? (int64_t)p.W : (int64_t)p.Hkv * hs) +
+               (size_t)(hs == 0 ? 0 : (int64_t)g * hs);
+    } else {
+        rows_lim = pos_end;
+    }
+    const uint32_t kv_bytes = rows_lim > 0 ? (uint32_t)(rows_lim - 1) * p.row_bytes + 2u * D : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, kv_bytes);
+    const size_t mask_per_b = (size_t)p.n_q * p.Hkv * p.cap;
+    const __amdgpu_buffer_rsrc_t rm = MODE == 1 ? make_rsrc(p.keep_mask + (size_t)b * mask_per_b, (uint32_t)mask_per_b)
+                                                : make_rsrc(p.k, 0u);
+
+    Acc<D, RT> st;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        st.m[rt] = -INFINITY;
+        st.l[rt] = 0.f;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) st.o[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    unsigned char* vlds = smem + wave * Gm::VBYTES;
+    const int ntiles = (pos_end - pos_begin + TT - 1) / TT;
+
+    for (int tile = wave; tile < ntiles; tile += kWaves) {
+        const int tb = pos_begin + tile * TT;
+
+        // -- row offsets of this tile's positions ----------------------------
+        uint32_t koff[MB];
+        uint32_t voff[VI];
+        uint64_t gvalid = 0;
+        if constexpr (GATHER) {
+            const int pe = tb + lane;
+            int jv = -1;
+            if (lane < TT && pe < pos_end) jv = list[pe];
+            const bool ok = jv >= 0 && jv < lim_g;
+            const uint32_t off = ok ? (uint32_t)jv * p.row_bytes : kOOB;
+            gvalid = __ballot(ok);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) koff[mb] = __shfl(off, 16 * mb + l16);
+#pragma unroll
+            for (int n = 0; n < VI; ++n) voff[n] = __shfl(off, n * RPI + lane / CPR);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) koff[mb] = (uint32_t)(tb + 16 * mb + l16) * p.row_bytes;
+#pragma unroll
+            for (int n = 0; n < VI; ++n) voff[n] = (uint32_t)(tb + n * RPI + lane / CPR) * p.row_bytes;
+        }
+
+        // -- issue every load of the tile ------------------------------------
+        u32x4 vreg[VI];
+#pragma unroll
+        for (int n = 0; n < VI; ++n) vreg[n] = bload128(rv, voff[n] + (uint32_t)(lane % CPR) * 16u);
+        bf16x8 kreg[MB][KS];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kreg[mb][ks] = __builtin_bit_cast(bf16x8, bload128(rk, koff[mb] + (uint32_t)(32 * ks + 8 * q4) * 2u));
+        uint32_t mbits[RT][MB];
+        if constexpr (MODE == 1) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const uint32_t off = (rt * 16 + l16) < nrows
+                                             ? (uint32_t)(i_r[rt] * p.Hkv + g) * (uint32_t)p.cap +
+                                                   (uint32_t)(tb + 16 * mb + 4 * q4)
+                                             : kOOB;
+                    uint32_t bits = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bits |= (uint32_t)(__builtin_amdgcn_raw_buffer_load_b8(rm, off + e, 0, 0) != 0) << e;
+                    mbits[rt][mb] = bits;
+                }
+        }
+
+        // -- stage V rows in LDS ------------------------------------------
+#pragma unroll
+        for (int n = 0; n < VI; ++n) {
+            unsigned char* dst = vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16;
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            reinterpret_cast<u32x2*>(dst)[0] = u32x2{vreg[n][0], vreg[n][1]};
+            reinterpret_cast<u32x2*>(dst)[1] = u32x2{vreg[n][2], vreg[n][3]};
+        }
+
+        // -- S^T = K Q^T ---------------------------------------------------
+        f32x4 sc[RT][MB];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) a = mfma(kreg[mb][ks], qreg[rt][ks], a);
+                sc[rt][mb] = a;
+            }
+
+        // -- online softmax (log2 domain) -----------------------------------
+        bf16x8 pb[RT][KB];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int lim = GATHER ? 0 : min(lim_r[rt], pos_end);
+            const bool row_ok = (rt * 16 + l16) < nrows;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int off = 16 * mb + 4 * q4 + e;
+                    bool ok;
+                    if constexpr (GATHER) {
+                        ok = row_ok && ((gvalid >> off) & 1ull);
+                    } else {
+                        ok = tb + off < lim;
+                        if constexpr (MODE == 1) ok = ok && ((mbits[rt][mb] >> e) & 1u);
+                    }
+                    const float x = ok ? sc[rt][mb][e] * p.scale_log2 : -INFINITY;
+                    sc[rt][mb][e] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(st.m[rt], mx);
+            const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(st.m[rt] - mu);
+            float lsum = 0.f;
+            __bf16 ph[MB][4];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const __bf16 h = (__bf16)fast_exp2(sc[rt][mb][e] - mu);
+                    ph[mb][e] = h;
+                    lsum += (float)h;
+                }
+            st.l[rt] = st.l[rt] * alpha + lsum;
+            st.m[rt] = m_new;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) st.o[rt][n] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pb[rt][kb][e] = e < 4 ? ph[2 * kb][e] : ph[2 * kb + 1][e - 4];
+        }
+
+        // -- O^T += V^T P^T -------------------------------------------------
+        wave_lds_sync();
+        const __bf16* vl = reinterpret_cast<const __bf16*>(vlds);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                bf16x8 va;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tl = 32 * kb + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
+                    va[e] = vl[tl * (RS / 2) + 16 * n + l16];
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) st.o[rt][n] = mfma(va, pb[rt][kb], st.o[rt][n]);
+            }
+        wave_lds_sync();
+    }
+
+    // Row sums were kept per lane (each lane saw 4 of every 16 tokens).
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        st.l[rt] += __shfl_xor(st.l[rt], 16);
+        st.l[rt] += __shfl_xor(st.l[rt], 32);
+    }
+
+    // ---- merge the four waves' states through LDS -------------------------
+    f32x4* dump = reinterpret_cast<f32x4*>(smem);
+    auto dump_state = [&](int slot) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) dump[((slot * RT + rt) * NB + n) * 64 + lane] = st.o[rt][n];
+            s_ml[slot][rt][lane][0] = st.m[rt];
+            s_ml[slot][rt][lane][1] = st.l[rt];
+        }
+    };
+    auto merge_state = [&](int slot) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float w1, w2, m;
+            merge_scale(st.m[rt], s_ml[slot][rt][lane][0], w1, w2, m);
+            st.m[rt] = m;
+            st.l[rt] = w1 * st.l[rt] + w2 * s_ml[slot][rt][lane][1];
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                st.o[rt][n] = w1 * st.o[rt][n] + w2 * dump[((slot * RT + rt) * NB + n) * 64 + lane];
+        }
+    };
+    __syncthreads();
+    if (wave >= 2) dump_state(wave - 2);
+    __syncthreads();
+    if (wave < 2) merge_state(wave);
+    __syncthreads();
+    if (wave == 1) dump_state(0);
+    __syncthreads();
+    if (wave == 0) merge_state(0);
+
+    // ---- single split: write the result directly ---------------------------
+    if (n_active == 1) {
+        if (wave == 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int rr = rt * 16 + l16;
+                if (rr >= nrows) continue;
+                const size_t orow = out_row(p, b, g, row0 + rr, iq, GATHER);
+                const float l = st.l[rt];
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+                for (int n = 0; n < NB; ++n) store4<D>(p, orow, 16 * n + 4 * q4, st.o[rt][n] * inv);
+                if (p.lse != nullptr && q4 == 0)
+                    p.lse[orow] = l > 0.f ? (st.m[rt] + __log2f(l)) * kLn2 : -INFINITY;
+            }
+        }
+        return;
+    }
+
+    // ---- several splits: publish this split's partial -----------------------
+    const size_t part0 = ((size_t)unit * p.splits + s) * p.rows_alloc;
+    if (wave == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int rr = rt * 16 + l16;
+            if (rr >= nrows) continue;
+            float* dst = p.ws_o + (part0 + rr) * D;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) *reinterpret_cast<f32x4*>(dst + 16 * n + 4 * q4) = st.o[rt][n];
+            if (q4 == 0) {
+                p.ws_ml[(part0 + rr) * 2 + 0] = st.m[rt];
+                p.ws_ml[(part0 + rr) * 2 + 1] = st.l[rt];
+            }
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const int prev = atomicAdd(p.ws_cnt + unit, 1);
+        s_last = (prev == n_active - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    // ---- last split of the unit: merge all partials ------------------------
+    float* sm = reinterpret_cast<float*>(smem);   // [n_active][rows_alloc] m, then weight
+    float* sl = sm + n_active * p.rows_alloc;      // [n_active][rows_alloc] l
+    const size_t base0 = (size_t)unit * p.splits * p.rows_alloc;
+    for (int k = tid; k < n_active * nrows; k += kThreads) {
+        const int s2 = k / nrows, rr = k % nrows;
+        const size_t pi = base0 + (size_t)s2 * p.rows_alloc + rr;
+        sm[s2 * p.rows_alloc + rr] = p.ws_ml[pi * 2 + 0];
+        sl[s2 * p.rows_alloc + rr] = p.ws_ml[pi * 2 + 1];
+    }
+    __syncthreads();
+    if (tid < nrows) {
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < n_active; ++s2) M = fmaxf(M, sm[s2 * p.rows_alloc + tid]);
+        const float mu = (M == -INFINITY) ? 0.f : M;
+        float den = 0.f;
+        for (int s2 = 0; s2 < n_active; ++s2) {
+            const float w = fast_exp2(sm[s2 * p.rows_alloc + tid] - mu);
+            sm[s2 * p.rows_alloc + tid] = w;
+            den += w * sl[s2 * p.rows_alloc + tid];
+        }
+        s_rowM[tid] = M;
+        s_rowDen[tid] = den;
+    }
+    __syncthreads();
+    constexpr int D4 = D / 4;
+    for (int k = tid; k < nrows * D4; k += kThreads) {
+        const int rr = k / D4, d = (k % D4) * 4;
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        const float* src = p.ws_o + (base0 + rr) * D + d;
+        const size_t sstride = (size_t)p.rows_alloc * D;
+        int s2 = 0;
+        for (; s2 + 4 <= n_active; s2 += 4) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 0) * sstride);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 1) * sstride);
+            const f32x4 x2 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 2) * sstride);
+            const f32x4 x3 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 3) * sstride);
+            a += sm[(s2 + 0) * p.rows_alloc + rr] * x0;
+            a += sm[(s2 + 1) * p.rows_alloc + rr] * x1;
+            a += sm[(s2 + 2) * p.rows_alloc + rr] * x2;
+            a += sm[(s2 + 3) * p.rows_alloc + rr] * x3;
+        }
+        for (; s2 < n_active; ++s2)
+            a += sm[s2 * p.rows_alloc + rr] * *reinterpret_cast<const f32x4*>(src + (size_t)s2 * sstride);
+        const float den = s_rowDen[rr];
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const size_t orow = out_row(p, b, g, row0 + rr, iq, GATHER);
+        store4<D>(p, orow, d, a * inv);
+        if (d == 0 && p.lse != nullptr)
+            p.lse[orow] = den > 0.f ? (s_rowM[rr] + __log2f(den)) * kLn2 : -INFINITY;
+    }
+    if (tid == 0) __hip_atomic_store(p.ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ host ----
+
+constexpr int kWgPerCu = 1;
+
+static int tile_tokens(int D) { return D == 256 ? 32 : 64; }
+static int chunk_max_tokens(int D) { return D == 256 ? 512 : 1024; }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int num_cus,
+                     ck_decode_plan* pl) {
+    if (!s || !pl) return CK_ERR_ARG;
+    if (s->B < 1 || s->n_q < 1 || s->Hq < 1 || s->Hkv < 1 || s->cap < 1) return CK_ERR_ARG;
+    if (s->Hq % s->Hkv != 0) return CK_ERR_ARG;
+    if (s->D != 128 && s->D != 256) return CK_ERR_UNSUPPORTED;
+    if (s->n_q > CK_MAX_NQ) return CK_ERR_UNSUPPORTED;
+    if (W < 0 || num_splits < 0 || num_splits > CK_MAX_SPLITS || num_cus < 1) return CK_ERR_ARG;
+    const int64_t G = s->Hq / s->Hkv;
+    const int TT = tile_tokens(s->D);
+    // 32-bit buffer offsets: a whole head's cache, plus one tile of overhang.
+    const int64_t row_bytes = (int64_t)s->Hkv * s->D * 2;
+    if ((int64_t)(s->cap + TT) * row_bytes >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+    if (W == 0 && (int64_t)s->n_q * s->Hkv * s->cap + TT >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+    const int64_t R = W > 0 ? G : (int64_t)s->n_q * G;
+    const int rows_per_group = R <= 16 ? 16 : 32;
+    const int64_t RG = (R + rows_per_group - 1) / rows_per_group;
+    const int64_t units = (W > 0 ? (int64_t)s->B * s->n_q : (int64_t)s->B) * s->Hkv * RG;
+    const int64_t span_max = W > 0 ? W : s->cap;
+    int64_t target, cmax;
+    if (num_splits == 0) {
+        target = ((int64_t)num_cus * kWgPerCu + units - 1) / units;
+        cmax = chunk_max_tokens(s->D);
+    } else {
+        target = num_splits;
+        cmax = 0;
+    }
+    if (target < 1) target = 1;
+    if (target > CK_MAX_SPLITS) target = CK_MAX_SPLITS;
+    int64_t splits = target;
+    if (cmax > 0) {
+        const int64_t need = (span_max + cmax - 1) / cmax;
+        if (need > splits) splits = need;
+    }
+    const int64_t most = (span_max + TT - 1) / TT;
+    if (splits > most) splits = most;
+    if (splits > CK_MAX_SPLITS) splits = CK_MAX_SPLITS;
+    if (splits < 1) splits = 1;
+    if (units * splits >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+
+    pl->units = (int32_t)units;
+    pl->splits = (int32_t)splits;
+    pl->split_target = (int32_t)target;
+    pl->chunk_max = (int32_t)cmax;
+    pl->granule = TT;
+    pl->rows = (int32_t)R;
+    pl->row_groups = (int32_t)RG;
+    pl->rows_per_group = rows_per_group;
+    if (splits == 1) {
+        pl->workspace_bytes = 0;
+    } else {
+        const size_t parts = (size_t)units * (size_t)splits * (size_t)rows_per_group;
+        pl->workspace_bytes = align256(parts * s->D * sizeof(float)) + align256(parts * 2 * sizeof(float)) +
+                              align256((size_t)units * sizeof(int32_t));
+    }
+    return CK_OK;
+}
+
+static std::atomic<int> g_cus[64];
+
+static int device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CK_ERR_HIP;
+    if (dev >= 0 && dev < 64) {
+        int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return CK_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+        return CK_ERR_HIP;
+    if (dev >= 0 && dev < 64) g_cus[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return CK_OK;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+template <int D, int RT, int MODE>
+static hipError_t launch_one(const KParams& kp, int grid, hipStream_t st) {
+    void* args[] = {const_cast<KParams*>(&kp)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE>), dim3(grid),
+                           dim3(kThreads), args, 0, st);
+}
+
+template <int MODE>
+static hipError_t launch_mode(int D, int RT, const KParams& kp, int grid, hipStream_t st) {
+    if (D == 128) return RT == 1 ? launch_one<128, 1, MODE>(kp, grid, st) : launch_one<128, 2, MODE>(kp, grid, st);
+    return RT == 1 ? launch_one<256, 1, MODE>(kp, grid, st) : launch_one<256, 2, MODE>(kp, grid, st);
+}
+
+static int run(const ck_decode_shape* s, const void* q, const void* k, const void* v, const int32_t* kv_lens,
+               const uint8_t* keep_mask, const int32_t* idx, int32_t W, int64_t idx_head_stride, float scale,
+               int causal, void* out, int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+               int num_splits, void* stream) {
+    if (!s) return CK_ERR_ARG;
+    ck_decode_plan pl;
+    int st = plan_impl(s, W, num_splits, 1, &pl);  // shape checks only
+    if (st != CK_OK) return st;
+    if (!q || !k || !v || !kv_lens || !out) return CK_ERR_ARG;
+    if (W > 0 && !idx) return CK_ERR_ARG;
+    if (W > 0 && idx_head_stride != 0 && idx_head_stride < W) return CK_ERR_ARG;
+    if (out_dtype != CK_DT_F32 && out_dtype != CK_DT_BF16) return CK_ERR_ARG;
+    if (!isfinite(scale)) return CK_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return CK_ERR_ALIGN;
+    if (!aligned(kv_lens, 4) || (lse && !aligned(lse, 4)) || (idx && !aligned(idx, 4))) return CK_ERR_ALIGN;
+
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != CK_OK) return st;
+    st = plan_impl(s, W, num_splits, cus, &pl);
+    if (st != CK_OK) return st;
+    if (pl.workspace_bytes > 0) {
+        if (!workspace) return CK_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return CK_ERR_ALIGN;
+        if (workspace_bytes < pl.workspace_bytes) return CK_ERR_WORKSPACE;
+    }
+
+    KParams kp{};
+    kp.q = static_cast<const uint16_t*>(q);
+    kp.k = static_cast<const uint16_t*>(k);
+    kp.v = static_cast<const uint16_t*>(v);
+    kp.kv_lens = kv_lens;
+    kp.keep_mask = keep_mask;
+    kp.idx = idx;
+    kp.out = out;
+    kp.lse = lse;
+    if (pl.workspace_bytes > 0) {
+        const size_t parts = (size_t)pl.units * pl.splits * pl.rows_per_group;
+        char* w = static_cast<char*>(workspace);
+        kp.ws_cnt = reinterpret_cast<int32_t*>(w);
+        w += align256((size_t)pl.units * sizeof(int32_t));
+        kp.ws_o = reinterpret_cast<float*>(w);
+        w += align256(parts * s->D * sizeof(float));
+        kp.ws_ml = reinterpret_cast<float*>(w);
+    }
+    kp.B = s->B;
+    kp.n_q = s->n_q;
+    kp.Hq = s->Hq;
+    kp.Hkv = s->Hkv;
+    kp.G = s->Hq / s->Hkv;
+    kp.cap = s->cap;
+    kp.R = pl.rows;
+    kp.RG = pl.row_groups;
+    kp.rows_alloc = pl.rows_per_group;
+    kp.splits = pl.splits;
+    kp.S_target = pl.split_target;
+    kp.c_max = pl.chunk_max;
+    kp.gran = pl.granule;
+    kp.W = W;
+    kp.idx_head_stride = idx_head_stride;
+    kp.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    kp.causal = causal ? 1 : 0;
+    kp.out_bf16 = out_dtype == CK_DT_BF16 ? 1 : 0;
+    kp.row_bytes = (uint32_t)(s->Hkv * s->D * 2);
+
+    const int RT = pl.rows_per_group / 16;
+    const int grid = pl.units * pl.splits;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (W > 0)
+        e = launch_mode<2>(s->D, RT, kp, grid, hs);
+    else if (keep_mask)
+        e = launch_mode<1>(s->D, RT, kp, grid, hs);
+    else
+        e = launch_mode<0>(s->D, RT, kp, grid, hs);
+    return e == hipSuccess ? CK_OK : CK_ERR_HIP;
+}
+
+}  // namespace ckda
+
+extern "C" {
+
+int ck_decode_attn_plan(const ck_decode_shape* shape, int32_t W, int num_splits, int num_cus,
+                        ck_decode_plan* plan) {
+    return ckda::plan_impl(shape, W, num_splits, num_cus, plan);
+}
+
+int ck_decode_attn_workspace_size(const ck_decode_shape* shape, int32_t W, int num_splits, size_t* bytes) {
+    if (!bytes) return CK_ERR_ARG;
+    ck_decode_plan pl;
+    int st = ckda::plan_impl(shape, W, num_splits, 1, &pl);
+    if (st != CK_OK) return st;
+    int cus = 0;
+    st = ckda::device_cus(&cus);
+    if (st != CK_OK) return st;
+    st = ckda::plan_impl(shape, W, num_splits, cus, &pl);
+    if (st != CK_OK) return st;
+    *bytes = pl.workspace_bytes;
+    return CK_OK;
+}
+
+int ck_decode_attn(const ck_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* kv_lens, float scale, int causal, const uint8_t* keep_mask, void* out,
+                   int out_dtype, float* lse, void* workspace, size_t workspace_bytes, int num_splits,
+                   void* stream) {
+    return ckda::run(shape, q, k_cache, v_cache, kv_lens, keep_mask, nullptr, 0, 0, scale, causal, out,
+                     out_dtype, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* kv_lens, const int32_t* idx, int32_t W,
+                          int64_t idx_head_stride, float scale, int causal, void* out, int out_dtype,
+                          float* lse, void* workspace, size_t workspace_bytes, int num_splits, void* stream) {
+    if (W < 1) return CK_ERR_ARG;
+    return ckda::run(shape, q, k_cache, v_cache, kv_lens, nullptr, idx, W, idx_head_stride, scale, causal, out,
+                     out_dtype, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+const char* ck_status_string(int status) {
+    switch (status) {
+        case CK_OK: return "ok";
+        case CK_ERR_ARG: return "invalid argument";
+        case CK_ERR_UNSUPPORTED: return "unsupported shape";
+        case CK_ERR_ALIGN: return "misaligned pointer";
+        case CK_ERR_WORKSPACE: return "workspace missing or too small";
+        case CK_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+/*
+ * ck_decode_attn — length-aware split-KV GQA decode attention for AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: device pointers, sizes, an int
+ * status.  No C++ types, no exceptions and no framework types cross it.
+ *
+ * The operation (ComfyUI issue "Qwen3.5 text generation attends over the
+ * full KV capacity every step, so decode speed drops with max_length",
+ * sections Feature Idea and Existing Solutions): every decode step attends
+ * each query only over the filled prefix of a preallocated KV cache, whose
+ * length is read on the device from kv_lens, so the cost follows the tokens
+ * generated rather than the capacity.  The query heads of one KV head are
+ * packed as rows against each KV tile (the GQA group), up to 6 queries per
+ * sequence may form a bottom-right aligned causal window (MTP
+ * verification), and head_dim is 128 or 256.
+ *
+ * For batch entry b, query i < n_q and query head h < Hq, with G = Hq/Hkv:
+ *   g   = h / G                                (consecutive heads share a KV head)
+ *   L   = clamp(kv_lens[b], 0, cap)
+ *   lim = causal ? clamp(L - n_q + i + 1, 0, L) : L
+ *   visible cells: dense  -> j in [0, lim), and keep_mask[b,i,g,j] != 0 if a
+ *                            mask is given
+ *                  gather -> idx[...][t] for t < W with 0 <= idx < lim, in
+ *                            list order (a cell listed twice counts twice)
+ *   out[b,i,h,:] = sum_j softmax_j(scale * q.K[b,j,g,:]) * V[b,j,g,:]
+ *   lse[b,i,h]   = ln sum_j exp(scale * q.K[b,j,g,:])
+ * A query with no visible cell gets out = 0 and lse = -inf.  Cells that are
+ * not visible are never read, so they may hold any bits (NaN/Inf included).
+ *
+ * Layouts (all contiguous, row-major, bf16 = IEEE binary16 brain float):
+ *   q        [B, n_q, Hq, D]   bf16
+ *   k_cache  [B, cap, Hkv, D]  bf16
+ *   v_cache  [B, cap, Hkv, D]  bf16
+ *   kv_lens  [B]               int32, device memory, read by the kernel
+ *   out      [B, n_q, Hq, D]   fp32 or bf16 (round to nearest even)
+ *   lse      [B, n_q, Hq]      fp32 natural log, optional (NULL)
+ *
+ * Ownership: every pointer is a device pointer owned by the caller.  The
+ * library never allocates, frees or synchronizes and never reads device
+ * memory from the host, so kv_lens and idx are not checked on the host: the
+ * clamp and validity rules above define every value.  Calls are stream
+ * ordered on `stream` (a hipStream_t; NULL is the default stream).
+ *
+ * Workspace: when the plan splits the KV range (see
+ * ck_decode_attn_workspace_size) the caller passes a device buffer of at
+ * least that many bytes, 256-byte aligned.  It starts with one int32
+ * completion counter per unit, which must be zero when a launch starts;
+ * every launch leaves its counters at zero again (the partial results after
+ * them are scratch).  So a buffer ZEROED ONCE serves any number of launches
+ * of the same plan (same shape, W, num_splits and device), eager or replayed
+ * from a captured HIP graph without a memset node.  A buffer used for one
+ * plan must be zeroed again before it serves a different plan, and launches
+ * that may run concurrently (different streams) need different workspaces.
+ *
+ * Launch shape depends only on the shape, W, num_splits and the device, never
+ * on kv_lens or idx contents, so one captured launch stays valid while the
+ * lengths and index lists change between replays.
+ *
+ * Errors: a negative status is returned synchronously and nothing is
+ * launched.  CK_ERR_HIP reports a failure of the HIP launch itself.  Faults
+ * inside a kernel surface at the caller's next synchronization.
+ */
+#ifndef CK_DECODE_ATTN_H
+#define CK_DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ck_decode_shape {
+    int32_t B;    /* sequences                                   >= 1        */
+    int32_t n_q;  /* queries per sequence (causal window rows)   1..6        */
+    int32_t Hq;   /* query heads                                 multiple of Hkv */
+    int32_t Hkv;  /* KV heads                                    >= 1        */
+    int32_t D;    /* head dim                                    128 or 256  */
+    int32_t cap;  /* cache capacity (slots per sequence)         >= 1        */
+} ck_decode_shape;
+
+enum {
+    CK_DT_F32 = 0,
+    CK_DT_BF16 = 1
+};
+
+enum {
+    CK_OK = 0,
+    CK_ERR_ARG = -1,          /* null pointer, bad count or enum, bad stride */
+    CK_ERR_UNSUPPORTED = -2,  /* D not 128/256, n_q > 6, cache too large     */
+    CK_ERR_ALIGN = -3,        /* pointer misaligned (see each argument)      */
+    CK_ERR_WORKSPACE = -4,    /* workspace missing or too small              */
+    CK_ERR_HIP = -5           /* the HIP runtime rejected the query/launch   */
+};
+
+#define CK_MAX_NQ 6
+#define CK_MAX_SPLITS 256
+
+/* Launch plan, exposed so that callers and tests can see how a shape is cut.
+ * units = independent (sequence, [query,] KV head, row group) work items;
+ * splits = workgroups per unit along the KV range (grid = splits x units);
+ * rows = packed query rows per unit (n_q*G dense, G gather). */
+typedef struct ck_decode_plan {
+    int32_t units;
+    int32_t splits;          /* grid splits per unit                         */
+    int32_t split_target;    /* splits aimed for when the range is long      */
+    int32_t chunk_max;       /* longest range one split takes (0: no limit)  */
+    int32_t granule;         /* split ranges are multiples of this           */
+    int32_t rows;            /* query rows per unit                          */
+    int32_t row_groups;      /* units per (sequence, query, KV head)         */
+    int32_t rows_per_group;  /* rows handled by one workgroup (16 or 32)     */
+    size_t workspace_bytes;  /* 0 when no launch of this plan can split      */
+} ck_decode_plan;
+
+/* Plan for `shape` on a device with `num_cus` compute units.  W = 0 plans the
+ * dense entry, W >= 1 the gather entry.  num_splits = 0 picks the split count
+ * automatically, otherwise it is used as given (1..CK_MAX_SPLITS).  Pure host
+ * arithmetic: no HIP call.  Returns CK_OK or an argument error. */
+int ck_decode_attn_plan(const ck_decode_shape* shape, int32_t W, int num_splits, int num_cus,
+                        ck_decode_plan* plan);
+
+/* Workspace bytes needed by ck_decode_attn (W = 0) or ck_decode_attn_gather
+ * (W >= 1) for `shape` and `num_splits` on the current HIP device.
+ * 0 means no workspace is needed (NULL may be passed). */
+int ck_decode_attn_workspace_size(const ck_decode_shape* shape, int32_t W, int num_splits,
+                                  size_t* bytes);
+
+/* Dense decode over the filled prefix (see the definition above).
+ *   q, k_cache, v_cache, out : 16-byte aligned.  kv_lens, lse : 4-byte aligned.
+ *   scale      : softmax scale (finite), typically 1/sqrt(D).
+ *   causal     : nonzero for the bottom-right aligned causal window.
+ *   keep_mask  : NULL, or uint8 [B, n_q, Hkv, cap]; cells with 0 are excluded
+ *                (the masked full-window scan the gather entry replaces:
+ *                llama.cpp PR "qwen4exp: attend the selected cells instead of
+ *                masking the window", PR body).  Only [0, lim) is scanned.
+ *   out_dtype  : CK_DT_F32 or CK_DT_BF16.
+ *   num_splits : 0 = automatic, else 1..CK_MAX_SPLITS. */
+int ck_decode_attn(const ck_decode_shape* shape, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* kv_lens, float scale, int causal,
+                   const uint8_t* keep_mask, void* out, int out_dtype, float* lse,
+                   void* workspace, size_t workspace_bytes, int num_splits, void* stream);
+
+/* Gathered decode: each query attends a list of W selected cells read in
+ * place from the cache, instead of masking the whole window (llama.cpp PR
+ * "qwen4exp: attend the selected cells instead of masking the window", PR
+ * body and Additional information; llama.cpp PR "qwen4exp : gather-based
+ * sparse attention for QSA decode", Overview; per-token lists for MTP
+ * verification in that PR's discussion).  The selected K/V rows move once,
+ * straight from the cache: there is no compacted copy.
+ *   idx             : int32, 4-byte aligned.  idx_head_stride == 0: one list
+ *                     per query shared by its heads, layout [B, n_q, W];
+ *                     idx_head_stride >= W: layout [B, n_q, Hkv,
+ *                     idx_head_stride] with the list in the first W entries.
+ *   W               : list length >= 1.
+ * Entries < 0 or >= lim are skipped; other arguments as ck_decode_attn. */
+int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* kv_lens, const int32_t* idx,
+                          int32_t W, int64_t idx_head_stride, float scale, int causal, void* out,
+                          int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                          int num_splits, void* stream);
+
+/* Static text for a status code. */
+const char* ck_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CK_DECODE_ATTN_H */

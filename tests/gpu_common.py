@@ -1,0 +1,78 @@
+"""Helpers shared by the GPU tests: run the HIP library and the oracle on the
+same seeded inputs and compare them to the stated tolerances."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import decode_attention_flash_amd as ck
+import oracle
+
+# Tolerances for N(0, 1) inputs: max |delta| against the fp64 oracle.
+TOL_F32 = 4e-3     # fp32 output
+TOL_BF16 = 1.6e-2  # bf16 output (one bf16 rounding of values of magnitude < 4)
+# lse: the row sum adds bf16-rounded weights (relative error <= 2^-8 each), so
+# ln of it can move by at most ln(1 + 2^-8) < 4e-3.
+TOL_LSE = 4e-3
+
+DEV = torch.device("cuda", 0)
+
+
+def note(msg: str) -> None:
+    """Name the case before the GPU runs it (flushes through pytest capture)."""
+    sys.__stdout__.write(f"[case] {msg}\n")
+    sys.__stdout__.flush()
+
+
+def dense_gpu(q, k, v, lens, *, causal=False, keep_mask=None, out_dtype=torch.float32,
+              num_splits=0, scale=None, device_inputs=None):
+    D = q.shape[-1]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    if device_inputs is None:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    else:
+        qd, kd, vd = device_inputs
+    lens_d = torch.as_tensor(np.asarray(lens), dtype=torch.int32).to(DEV)
+    mask_d = None if keep_mask is None else torch.as_tensor(np.asarray(keep_mask)).to(DEV)
+    out, lse = ck.decode_attn(qd, kd, vd, lens_d, scale=scale, causal=causal, keep_mask=mask_d,
+                              out_dtype=out_dtype, return_lse=True, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def gather_gpu(q, k, v, lens, idx, *, causal=False, out_dtype=torch.float32, num_splits=0,
+               scale=None):
+    D = q.shape[-1]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    lens_d = torch.as_tensor(np.asarray(lens), dtype=torch.int32).to(DEV)
+    idx_d = torch.as_tensor(np.asarray(idx), dtype=torch.int32).to(DEV)
+    out, lse = ck.decode_attn_gather(q.to(DEV), k.to(DEV), v.to(DEV), lens_d, idx_d, scale=scale,
+                                     causal=causal, out_dtype=out_dtype, return_lse=True,
+                                     num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_ref(q, k, v, lens, *, causal=False, keep_mask=None, idx=None, scale=None):
+    D = q.shape[-1]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    return oracle.attn(q, k, v, np.asarray(lens, dtype=np.int32), scale, causal,
+                       keep_mask=keep_mask, idx=idx)
+
+
+def assert_close(gpu, ref, out_dtype=torch.float32, what=""):
+    go, gl = gpu
+    ro, rl = ref
+    tol = TOL_BF16 if out_dtype == torch.bfloat16 else TOL_F32
+    assert np.all(np.isfinite(go)), f"{what}: non-finite output"
+    d = float(np.max(np.abs(go - ro))) if go.size else 0.0
+    assert d <= tol, f"{what}: max|delta| {d:.3e} > {tol}"
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(gl), empty), f"{what}: empty-row lse mismatch"
+    if np.any(~empty):
+        dl = float(np.max(np.abs(gl[~empty] - rl[~empty])))
+        assert dl <= TOL_LSE, f"{what}: lse max|delta| {dl:.3e}"
+    return d

@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, plans launches by its documented rules, and rejects bad
+arguments before any HIP call (so no GPU is needed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_flash_amd as ck
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ck_decode_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ck_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(ck.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(ck.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = ck.lib()
+    for code, text in ck.STATUS.items():
+        assert L.ck_status_string(code).decode() == text
+
+
+def shape(B=1, n_q=1, Hq=16, Hkv=4, D=256, cap=24007):
+    return ck.Shape(B, n_q, Hq, Hkv, D, cap)
+
+
+def test_plan_fills_the_chip_at_batch_one():
+    p = ck.plan(shape(), num_cus=256)
+    assert p["units"] == 4 and p["split_target"] == 64 and p["splits"] == 64
+    assert p["rows"] == 4 and p["rows_per_group"] == 16 and p["row_groups"] == 1
+    assert p["workspace_bytes"] > 0
+
+
+def test_plan_does_not_depend_on_capacity_for_split_target():
+    a = ck.plan(shape(cap=8199), num_cus=256)
+    b = ck.plan(shape(cap=24007), num_cus=256)
+    assert a["split_target"] == b["split_target"] and a["chunk_max"] == b["chunk_max"]
+    assert a["granule"] == b["granule"]
+
+
+def test_plan_batched_uses_chunk_limit():
+    p = ck.plan(shape(B=32, Hq=32, Hkv=8, D=128, cap=32768), num_cus=256)
+    assert p["units"] == 256 and p["split_target"] == 1
+    assert p["chunk_max"] == 1024 and p["splits"] == 32
+
+
+def test_plan_causal_window_row_groups():
+    p = ck.plan(shape(n_q=6), num_cus=256)
+    assert p["rows"] == 24 and p["rows_per_group"] == 32 and p["row_groups"] == 1
+    p = ck.plan(shape(n_q=6, Hq=32, Hkv=4), num_cus=256)  # 48 rows -> two groups
+    assert p["rows"] == 48 and p["row_groups"] == 2 and p["units"] == 8
+
+
+def test_plan_gather_units_per_query():
+    p = ck.plan(shape(Hq=16, Hkv=2, D=128, cap=131072, n_q=2), W=2112, num_cus=256)
+    assert p["rows"] == 8 and p["units"] == 4
+    assert p["splits"] <= (2112 + 63) // 64
+
+
+def test_plan_forced_splits_and_single_split():
+    p = ck.plan(shape(), num_splits=7, num_cus=256)
+    assert p["splits"] == 7 and p["chunk_max"] == 0
+    p = ck.plan(shape(), num_splits=1, num_cus=256)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+    p = ck.plan(shape(cap=10), num_cus=256)  # one tile at most
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), -2), (dict(D=129), -2), (dict(n_q=7), -2), (dict(n_q=0), -1),
+    (dict(Hq=6, Hkv=4), -1), (dict(B=0), -1), (dict(cap=0), -1),
+    (dict(Hkv=8, Hq=8, D=256, cap=600000), -2),
+])
+def test_plan_rejects(kw, status):
+    p = ck.Plan()
+    st = ck.lib().ck_decode_attn_plan(ctypes.byref(shape(**kw)), 0, 0, 256, ctypes.byref(p))
+    assert st == status
+
+
+def _call_dense(sh, q=16, k=16, v=16, lens=16, out=16, out_dtype=0, scale=0.1, num_splits=0,
+                lse=None):
+    V = lambda x: None if x is None else ctypes.c_void_p(x)
+    return ck.lib().ck_decode_attn(ctypes.byref(sh), V(q), V(k), V(v), V(lens),
+                                   ctypes.c_float(scale), 0, None, V(out), out_dtype, V(lse),
+                                   None, 0, num_splits, None)
+
+
+def test_dense_argument_errors_before_any_hip_call():
+    sh = shape()
+    big = 1 << 20
+    assert _call_dense(sh, q=None) == -1
+    assert _call_dense(sh, out=None) == -1
+    assert _call_dense(sh, lens=None) == -1
+    assert _call_dense(sh, out_dtype=7) == -1
+    assert _call_dense(sh, scale=float("nan")) == -1
+    assert _call_dense(sh, num_splits=-1) == -1
+    assert _call_dense(sh, num_splits=257) == -1
+    assert _call_dense(sh, q=big + 8) == -3
+    assert _call_dense(sh, out=big + 4) == -3
+    assert _call_dense(sh, lens=big + 2) == -3
+    assert _call_dense(sh, lse=big + 1) == -3
+    assert _call_dense(shape(D=64)) == -2
+    assert ck.lib().ck_decode_attn(None, None, None, None, None, ctypes.c_float(1.0), 0, None,
+                                   None, 0, None, None, 0, 0, None) == -1
+
+
+def test_gather_argument_errors_before_any_hip_call():
+    sh = shape(Hkv=2, D=128, cap=4096)
+    V = ctypes.c_void_p
+    L = ck.lib()
+    args = lambda W, idx, hs: (ctypes.byref(sh), V(16), V(16), V(16), V(16), idx, W, hs,
+                               ctypes.c_float(0.1), 0, V(16), 0, None, None, 0, 0, None)
+    assert L.ck_decode_attn_gather(*args(0, V(16), 0)) == -1          # W < 1
+    assert L.ck_decode_attn_gather(*args(64, None, 0)) == -1          # no list
+    assert L.ck_decode_attn_gather(*args(64, V(16), 10)) == -1        # head stride < W
+    assert L.ck_decode_attn_gather(*args(64, V(18), 64)) == -3        # misaligned list
+
+
+def test_workspace_size_rejects_bad_shape():
+    n = ctypes.c_size_t(0)
+    assert ck.lib().ck_decode_attn_workspace_size(ctypes.byref(shape(D=64)), 0, 0,
+                                                   ctypes.byref(n)) == -2
+    assert ck.lib().ck_decode_attn_workspace_size(ctypes.byref(shape()), 0, 0, None) == -1

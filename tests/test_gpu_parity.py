@@ -1,0 +1,362 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded
+inputs, for every decode workload shape, plus the exactness properties
+(garbage and capacity invariance, bit-exact index and mask handling)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_flash_amd as ck
+from decode_attention_flash_amd import synth
+from gpu_common import (DEV, TOL_F32, assert_close, dense_gpu, gather_gpu, note, oracle_ref)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------ workload configurations ----
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_tiny_dense(out_dtype):
+    """B=1, Hq=8, Hkv=2, D=128, one query, capacity 1024, 300 filled, garbage after."""
+    note(f"tiny dense {out_dtype}")
+    B, n_q, Hq, Hkv, D, cap, L = 1, 1, 8, 2, 128, 1024, 300
+    k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1001)
+    q = synth.queries(B, n_q, Hq, D, 1001)
+    gpu = dense_gpu(q, k, v, [L], out_dtype=out_dtype)
+    assert_close(gpu, oracle_ref(q, k, v, [L]), out_dtype, "tiny")
+
+
+@pytest.fixture(scope="module")
+def layer_d256():
+    """Hq=16, Hkv=4, D=256 layer with capacity 24007 filled to 24000."""
+    B, Hq, Hkv, D, cap = 1, 16, 4, 256, 24007
+    k, v = synth.kv_cache(B, cap, Hkv, D, [24000], 1002)
+    return k, v, (k.to(DEV), v.to(DEV))
+
+
+@pytest.mark.parametrize("L", [1000, 3000, 8000, 24000])
+def test_d256_kv_len_sweep(layer_d256, L):
+    note(f"D=256 plain decode L={L}")
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, 1, 16, 256, 1002)
+    gpu = dense_gpu(q, k, v, [L], device_inputs=(q.to(DEV), kd, vd))
+    assert_close(gpu, oracle_ref(q, k, v, [L]), what=f"L={L}")
+
+
+def test_d256_capacity_sweep_bit_identical():
+    """kv_len 3000 at capacities 8199, 16263, 24007: same filled prefix,
+    different garbage after it; the outputs are bit-identical."""
+    q = synth.queries(1, 1, 16, 256, 1002)
+    outs = []
+    for cap in (8199, 16263, 24007):
+        note(f"capacity sweep cap={cap}")
+        k, v = synth.kv_cache(1, cap, 4, 256, [3000], 1002 + cap)
+        k[:, :3000], v[:, :3000] = synth.kv_cache(1, 3000, 4, 256, [3000], 1002)
+        gpu = dense_gpu(q, k, v, [3000])
+        outs.append(gpu)
+    ref = oracle_ref(q, k, v, [3000])
+    assert_close(outs[0], ref, what="cap sweep")
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+
+
+@pytest.mark.parametrize("n_q", [3, 4, 5, 6])
+@pytest.mark.parametrize("L", [2000, 4000])
+def test_d256_causal_window(layer_d256, n_q, L):
+    note(f"causal window n_q={n_q} L={L}")
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, n_q, 16, 256, 1003 + n_q)
+    gpu = dense_gpu(q, k, v, [L], causal=True, device_inputs=(q.to(DEV), kd, vd))
+    assert_close(gpu, oracle_ref(q, k, v, [L], causal=True), what=f"n_q={n_q} L={L}")
+
+
+def test_d256_causal_window_bf16_out(layer_d256):
+    note("causal window bf16 out")
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, 5, 16, 256, 1013)
+    gpu = dense_gpu(q, k, v, [2000], causal=True, out_dtype=torch.bfloat16,
+                    device_inputs=(q.to(DEV), kd, vd))
+    assert_close(gpu, oracle_ref(q, k, v, [2000], causal=True), torch.bfloat16, "bf16 window")
+
+
+def test_causal_rows_equal_shorter_plain_decode(layer_d256):
+    """Causal row i equals a single-query decode of length L - n_q + i + 1."""
+    k, v, (kd, vd) = layer_d256
+    n_q, L = 6, 4000
+    q = synth.queries(1, n_q, 16, 256, 1023)
+    note("causal rows vs plain")
+    full, _ = dense_gpu(q, k, v, [L], causal=True, device_inputs=(q.to(DEV), kd, vd))
+    for i in range(n_q):
+        qi = q[:, i:i + 1].contiguous()
+        row, _ = dense_gpu(qi, k, v, [L - n_q + i + 1], device_inputs=(qi.to(DEV), kd, vd))
+        assert np.max(np.abs(row[:, 0] - full[:, i])) <= TOL_F32
+
+
+# ------------------------------------------------------------- batched ----
+
+def test_batched_ragged_graph_replay():
+    """B=32, Hq=32, Hkv=8, D=128, capacity 32768, lengths uniform in
+    [512, 32768]; one captured launch replayed with new lengths each time."""
+    B, Hq, Hkv, D, cap = 32, 32, 8, 128, 32768
+    note("batched ragged: generating caches on the device")
+    k, v = synth.kv_cache(B, cap, Hkv, D, [cap] * B, 1004, device=DEV, garbage=False)
+    q = synth.queries(B, 1, Hq, D, 1004, device=DEV)
+    lens_d = torch.zeros(B, dtype=torch.int32, device=DEV)
+    shape = ck.shape_of(q, k)
+    ws = ck.new_workspace(shape)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=DEV)
+    lens_d.copy_(torch.from_numpy(synth.ragged_lens(B, 512, cap, 3999)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ck.decode_attn(q, k, v, lens_d, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note("batched ragged: capture")
+    with torch.cuda.graph(graph):
+        ck.decode_attn(q, k, v, lens_d, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    sample = [0, 7, 19, 31]
+    for r in range(3):
+        lens = synth.ragged_lens(B, 512, cap, 4000 + r)
+        lens_d.copy_(torch.from_numpy(lens))
+        note(f"batched ragged: replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        ls = lse.cpu().numpy()
+        assert np.all(np.isfinite(o))
+        # eager launch on the same lengths gives the same bits as the replay
+        eo, el = ck.decode_attn(q, k, v, lens_d, return_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(eo.cpu().numpy(), o) and np.array_equal(el.cpu().numpy(), ls)
+        for b in sample:
+            kb, vb = k[b:b + 1].cpu(), v[b:b + 1].cpu()
+            ref = oracle_ref(q[b:b + 1].cpu(), kb, vb, lens[b:b + 1])
+            assert_close((o[b:b + 1], ls[b:b + 1]), ref, what=f"replay {r} b={b} L={lens[b]}")
+    # the counters are back at zero after the last replay
+    pl = ck.plan(shape)
+    cnt = ws[:pl["units"] * 4].view(torch.int32)
+    assert int(cnt.abs().sum().item()) == 0
+
+
+# -------------------------------------------------------------- gather ----
+
+@pytest.fixture(scope="module", params=[32768, 65536, 131072])
+def sparse_case(request):
+    n_kv = request.param
+    B, n_q, Hq, Hkv, D = 1, 1, 16, 2, 128
+    k, v = synth.kv_cache(B, n_kv, Hkv, D, [n_kv], 1005)
+    q = synth.queries(B, n_q, Hq, D, 1005)
+    idx = synth.topk_lists(B, n_q, Hkv, n_kv, 2048, 64, seed=5000 + n_kv)
+    return n_kv, q, k, v, idx
+
+
+def test_gather_matches_oracle(sparse_case):
+    n_kv, q, k, v, idx = sparse_case
+    note(f"gather n_kv={n_kv}")
+    gpu = gather_gpu(q, k, v, [n_kv], idx)
+    assert_close(gpu, oracle_ref(q, k, v, [n_kv], idx=idx), what=f"gather {n_kv}")
+
+
+def test_masked_scan_matches_oracle_and_gather(sparse_case):
+    n_kv, q, k, v, idx = sparse_case
+    mask = synth.mask_from_lists(idx, n_kv)
+    note(f"masked scan n_kv={n_kv}")
+    masked = dense_gpu(q, k, v, [n_kv], keep_mask=mask)
+    assert_close(masked, oracle_ref(q, k, v, [n_kv], keep_mask=mask), what=f"masked {n_kv}")
+    gathered = gather_gpu(q, k, v, [n_kv], idx)
+    assert np.max(np.abs(gathered[0] - masked[0])) <= TOL_F32
+    assert np.max(np.abs(gathered[1] - masked[1])) <= 4e-3
+
+
+def test_gather_lists_edge_entries():
+    """Invalid entries (< 0, >= limit, >= capacity), duplicates, shared
+    lists, per-query lists under a causal window, ragged list length."""
+    B, n_q, Hq, Hkv, D, cap = 2, 3, 8, 2, 128, 700
+    lens = np.array([650, 40], dtype=np.int32)
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 77)
+    q = synth.queries(B, n_q, Hq, D, 77)
+    rng = np.random.default_rng(77)
+    W = 101
+    idx = rng.integers(-5, cap + 5, size=(B, n_q, Hkv, W), dtype=np.int64).astype(np.int32)
+    idx[..., :5] = idx[..., 5:10]        # duplicates
+    idx[..., 10] = lens.reshape(B, 1, 1) - 1
+    idx[..., 11] = lens.reshape(B, 1, 1)
+    for causal in (False, True):
+        note(f"gather edge entries causal={causal}")
+        gpu = gather_gpu(q, k, v, lens, idx, causal=causal)
+        assert_close(gpu, oracle_ref(q, k, v, lens, idx=idx, causal=causal), what="edge lists")
+        shared = idx[:, :, 0, :].copy()
+        gpu = gather_gpu(q, k, v, lens, shared, causal=causal)
+        assert_close(gpu, oracle_ref(q, k, v, lens, idx=shared, causal=causal), what="shared")
+
+
+# ------------------------------------------------------- exactness checks ----
+
+def counting_case(n_q, Hq, Hkv, D, cap, lens, seed, nbits=17):
+    B = len(lens)
+    k, _ = synth.kv_cache(B, cap, Hkv, D, lens, seed)
+    v1 = synth.counting_values(cap, Hkv, D, nbits)
+    v = v1.expand(B, cap, Hkv, D).contiguous()
+    for b, L in enumerate(lens):
+        k[b, :L] = 0
+        v[b, L:] = float("nan")
+        k[b, L:] = float("nan")
+    q = synth.queries(B, n_q, Hq, D, seed)
+    return q, k, v
+
+
+def check_counts(out, visible_sets, G, nbits=17):
+    """out [B, n_q, Hq, D] fp32; visible_sets[b][i][g] = array of cells."""
+    B, n_q, Hq, _ = out.shape
+    for b in range(B):
+        for i in range(n_q):
+            for h in range(Hq):
+                cells = np.asarray(visible_sets[b][i][h // G], dtype=np.int64)
+                n = len(cells)
+                if n == 0:
+                    assert np.all(out[b, i, h] == 0.0)
+                    continue
+                o = out[b, i, h].astype(np.float64)
+                assert abs(o[nbits] - 1.0) < 1e-6
+                counts = np.array([np.sum((cells >> d) & 1) for d in range(nbits)])
+                got = n * o[:nbits]
+                assert np.max(np.abs(got - counts)) < 0.01, (b, i, h)
+                assert np.array_equal(np.rint(got).astype(np.int64), counts), (b, i, h)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(n_q=1, Hq=8, Hkv=2, D=128, cap=1024, lens=[300], causal=False),
+    dict(n_q=1, Hq=16, Hkv=4, D=256, cap=24007, lens=[3000], causal=False),
+    dict(n_q=4, Hq=16, Hkv=4, D=256, cap=4096, lens=[2000], causal=True),
+    dict(n_q=6, Hq=16, Hkv=4, D=256, cap=4096, lens=[4000], causal=True),
+    dict(n_q=1, Hq=32, Hkv=8, D=128, cap=32768, lens=[512, 32768, 20000, 777], causal=False),
+    dict(n_q=3, Hq=8, Hkv=2, D=128, cap=256, lens=[0, 1, 2, 65, 255], causal=True),
+], ids=["tiny", "d256", "window4", "window6", "ragged", "short"])
+def test_dense_index_handling_bit_exact(cfg):
+    """K = 0 on visible cells (uniform weights) and V[j, d] = bit d of j:
+    n * out[d] must round to exactly the number of visible cells with bit d
+    set.  NaN fills every cell past the length."""
+    note(f"dense bit-exact {cfg}")
+    n_q, Hq, Hkv, D, cap, lens, causal = (cfg[x] for x in ("n_q", "Hq", "Hkv", "D", "cap", "lens", "causal"))
+    q, k, v = counting_case(n_q, Hq, Hkv, D, cap, lens, 11)
+    out, _ = dense_gpu(q, k, v, lens, causal=causal)
+    sets = []
+    for L in lens:
+        per_i = []
+        for i in range(n_q):
+            lim = max(0, min(L, L - n_q + i + 1)) if causal else L
+            per_i.append([np.arange(lim)] * Hkv)
+        sets.append(per_i)
+    check_counts(out, sets, Hq // Hkv)
+
+
+@pytest.mark.parametrize("n_kv", [32768, 131072])
+def test_gather_and_mask_index_handling_bit_exact(n_kv):
+    """The same counting construction through both entries of the sparse
+    workload: both recover exactly the listed cell set."""
+    Hq, Hkv, D = 16, 2, 128
+    q, k, v = counting_case(1, Hq, Hkv, D, n_kv, [n_kv], 12)
+    idx = synth.topk_lists(1, 1, Hkv, n_kv, 2048, 64, seed=5000 + n_kv)
+    mask = synth.mask_from_lists(idx, n_kv)
+    note(f"gather/mask bit-exact n_kv={n_kv}")
+    og, _ = gather_gpu(q, k, v, [n_kv], idx)
+    om, _ = dense_gpu(q, k, v, [n_kv], keep_mask=mask)
+    sets = [[[idx[0, 0, g] for g in range(Hkv)]]]
+    check_counts(og, sets, Hq // Hkv)
+    check_counts(om, sets, Hq // Hkv)
+
+
+def test_garbage_past_length_is_never_read():
+    """Two caches with the same prefix and different garbage (NaN/Inf bit
+    patterns included) give bit-identical outputs."""
+    B, n_q, Hq, Hkv, D, cap = 2, 4, 16, 4, 256, 3000
+    lens = [2500, 777]
+    q = synth.queries(B, n_q, Hq, D, 21)
+    k1, v1 = synth.kv_cache(B, cap, Hkv, D, lens, 21)
+    k2, v2 = k1.clone(), v1.clone()
+    g = synth.generator(99)
+    for b, L in enumerate(lens):
+        k2[b, L:] = synth.bf16_garbage((cap - L, Hkv, D), g)
+        v2[b, L:] = synth.bf16_garbage((cap - L, Hkv, D), g)
+    note("garbage invariance")
+    a = dense_gpu(q, k1, v1, lens, causal=True)
+    b_ = dense_gpu(q, k2, v2, lens, causal=True)
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
+    assert_close(a, oracle_ref(q, k1, v1, lens, causal=True), what="garbage")
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 0, 256])
+def test_split_count_does_not_change_result(layer_d256, num_splits):
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, 3, 16, 256, 31)
+    note(f"split invariance S={num_splits}")
+    gpu = dense_gpu(q, k, v, [3000], causal=True, num_splits=num_splits,
+                    device_inputs=(q.to(DEV), kd, vd))
+    assert_close(gpu, oracle_ref(q, k, v, [3000], causal=True), what=f"S={num_splits}")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_edge_lengths(D):
+    """Empty, single-cell, tile-boundary, full and out-of-range lengths in
+    one batch, with a causal window longer than some sequences."""
+    cap = 300
+    lens = np.array([0, 1, 2, 31, 32, 33, 63, 64, 65, 299, 300, 305, -3], dtype=np.int32)
+    B, n_q, Hq, Hkv = len(lens), 3, 8, 2
+    k, v = synth.kv_cache(B, cap, Hkv, D, np.clip(lens, 0, cap), 41)
+    q = synth.queries(B, n_q, Hq, D, 41)
+    for causal in (False, True):
+        for num_splits in (0, 1, 3):
+            note(f"edge lengths D={D} causal={causal} S={num_splits}")
+            gpu = dense_gpu(q, k, v, lens, causal=causal, num_splits=num_splits)
+            assert_close(gpu, oracle_ref(q, k, v, lens, causal=causal), what="edges")
+
+
+@pytest.mark.parametrize("Hq,Hkv,n_q", [(8, 8, 1), (4, 1, 6), (32, 2, 3), (64, 4, 2)])
+def test_group_shapes(Hq, Hkv, n_q):
+    """Group sizes 1 to 16 and packed row counts from 1 up to 48 (two row
+    groups)."""
+    D, cap = 128, 900
+    lens = [850, 333]
+    k, v = synth.kv_cache(2, cap, Hkv, D, lens, 51)
+    q = synth.queries(2, n_q, Hq, D, 51)
+    note(f"group shapes Hq={Hq} Hkv={Hkv} n_q={n_q}")
+    gpu = dense_gpu(q, k, v, lens, causal=True)
+    assert_close(gpu, oracle_ref(q, k, v, lens, causal=True), what="groups")
+
+
+def test_head_permutation_within_group(layer_d256):
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, 2, 16, 256, 61)
+    perm = torch.tensor([1, 3, 0, 2, 7, 6, 5, 4, 8, 9, 10, 11, 15, 12, 13, 14])
+    note("head permutation")
+    a, _ = dense_gpu(q, k, v, [5000], causal=True, device_inputs=(q.to(DEV), kd, vd))
+    qp = q[:, :, perm].contiguous()
+    b, _ = dense_gpu(qp, k, v, [5000], causal=True, device_inputs=(qp.to(DEV), kd, vd))
+    assert np.max(np.abs(b - a[:, :, perm.numpy()])) <= 1e-6
+
+
+# ------------------------------------------------------------ boundary ----
+
+def test_workspace_errors_on_device():
+    B, n_q, Hq, Hkv, D, cap = 1, 1, 16, 4, 256, 24007
+    q = torch.zeros((B, n_q, Hq, D), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((B, cap, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    lens = torch.full((B,), 5000, dtype=torch.int32, device=DEV)
+    need = ck.workspace_size(ck.shape_of(q, k))
+    assert need > 0
+    small = torch.zeros(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ck.CkError) as e:
+        ck.decode_attn(q, k, k, lens, workspace=small)
+    assert e.value.status == -4
+    ws = torch.zeros(need + 512, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ck.CkError) as e:
+        ck.decode_attn(q, k, k, lens, workspace=ws[16:])
+    assert e.value.status == -3
+    out = ck.decode_attn(q, k, k, lens, workspace=ws[256:])
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
