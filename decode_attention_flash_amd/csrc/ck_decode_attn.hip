@@ -45,6 +45,11 @@ constexpr uint32_t kOOB = 0x80000000u;        // an offset beyond every range we
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994530942f;
+// Completion counters of one unit live in their own 1 KiB block: the started,
+// arrived and finished counters on separate cache lines, then one claim flag
+// per merge slice.
+constexpr int kCntStride = 256, kStarted = 0, kArrived = 32, kFinished = 64, kSliceFlag = 96;
+constexpr int kMaxSlices = 64;
 
 template <int D>
 struct Geo {
@@ -56,8 +61,10 @@ struct Geo {
     static constexpr int CPR = D / 8;           // 16-byte chunks per cache row
     static constexpr int RPI = 64 / CPR;        // cache rows per V load instruction
     static constexpr int VI = TT / RPI;         // V load instructions per tile
-    static constexpr int RS = 2 * D + 8;        // LDS row stride in bytes (bank skew)
-    static constexpr int VBYTES = TT * RS;      // LDS bytes per wave for staged V
+    // LDS row stride of the staged V tile: 32 bytes of skew puts the four rows
+    // a 16-lane group reads in one transposed load on disjoint bank ranges.
+    static constexpr int RS = 2 * D + 32;
+    static constexpr int VBYTES = TT * RS;  // LDS bytes per wave for staged V
 };
 
 struct KParams {
@@ -71,11 +78,12 @@ struct KParams {
     float* lse;
     float* ws_o;
     float* ws_ml;
-    int32_t* ws_cnt;
+    int32_t* ws_cnt;  // per unit kCntStride ints: counters and slice claim flags
     int32_t B, n_q, Hq, Hkv, G, cap;
     int32_t R, RG, rows_alloc;
     int32_t splits;  // grid splits per unit
     int32_t S_target, c_max, gran;
+    int32_t slices;  // column slices of the merge
     int32_t W;
     int64_t idx_head_stride;  // 0: one list per query shared by its heads
     float scale_log2;         // softmax scale times log2(e)
@@ -88,9 +96,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              (int)kRsrcWord3);
 }
 
+// 16-byte buffer load; out-of-range offsets read as zero.  aux 2 marks the
+// access non-temporal (streamed once).
+template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
 }
+
+// Device-coherent accesses (cache policy sc1): stores write through to the
+// point of coherence of the whole device and loads are served from there, so
+// workgroups on different XCDs (each with its own L2) see each other's data.
+// They are the instructions the compiler itself uses for agent-scope relaxed
+// atomic stores and loads.
+constexpr int kAuxDevice = 16;
+
+template <typename T>
+__device__ __forceinline__ void store_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, T v);
+template <>
+__device__ __forceinline__ void store_dev<f32x4>(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAuxDevice);
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <>
+__device__ __forceinline__ void store_dev<f32x2>(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kAuxDevice);
+}
+__device__ __forceinline__ f32x4 load_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxDevice));
+}
+__device__ __forceinline__ f32x2 load_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAuxDevice));
+}
+// Wait until every store this wave issued has completed (vmcnt = 0; the
+// expcnt and lgkmcnt fields are left at their maxima).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -98,12 +138,28 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
+
+// Transposed LDS read (gfx950): within each 16-lane group, lane j receives
+// element j%4 of the 64-bit words read by lanes 4e+j/4, e = 0..3.
+__device__ __forceinline__ lds_bf16x4 lds_read_tr(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)(p)));
+}
+
 // Orders this wave's LDS writes before its later LDS reads (and the reverse)
 // without waiting on outstanding global loads.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int atomic_ld(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_st(int32_t* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Length of the range one split takes; the same arithmetic runs in every
@@ -125,8 +181,8 @@ struct Acc {
     float m[RT], l[RT];
 };
 
-// Merge a second softmax state (m2, l2, o2) into (m, l, o); both are in the
-// log2 domain.  Fully masked states have m = -inf and contribute nothing.
+// Weights that merge two softmax states (log2 domain) into one with max m.
+// Fully masked states have m = -inf and get weight 0.
 __device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float& w2, float& m) {
     m = fmaxf(m1, m2);
     float mu = (m == -INFINITY) ? 0.f : m;
@@ -134,7 +190,7 @@ __device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float
     w2 = fast_exp2(m2 - mu);
 }
 
-// Output row for packed row r of this unit: returns the flat (b, i, h) index.
+// Flat (b, i, h) index of packed row r of a unit.
 __device__ __forceinline__ size_t out_row(const KParams& p, int b, int g, int r, int iq, bool gather) {
     int i = gather ? iq : r / p.G;
     int j = gather ? r : r % p.G;
@@ -157,6 +213,106 @@ __device__ __forceinline__ void store4(const KParams& p, size_t row, int d, f32x
     }
 }
 
+struct MergeScratch {
+    float rowM[32], rowDen[32];
+    int flag;
+    int started_seen;
+    int owned[kMaxSlices];
+};
+
+// Merge column slice `c` of `ns` for one unit from the n_active published
+// partials: O = sum_s w_s acc_s / sum_s w_s l_s with w_s = 2^(m_s - max m).
+// Each output column group (row, 4 columns) is summed by TPP neighbouring
+// lanes, each over a strided subset of the splits, then reduced by shuffles.
+template <int D>
+__device__ void merge_slice(const KParams& p, unsigned char* smem, MergeScratch& ms, int unit, int n_active,
+                            int nrows, int c, int ns, int b, int g, int iq, bool gather, int row0) {
+    constexpr int D4 = D / 4;
+    const int tid = threadIdx.x;
+    const int col_lo = c * D4 / ns, col_hi = (c + 1) * D4 / ns;
+    const int ncol = col_hi - col_lo;
+    const int P = nrows * ncol;
+    int TPP = 1;
+    while (TPP < 64 && 2 * TPP * P <= kThreads) TPP *= 2;
+    const int per_pass = kThreads / TPP;
+    float* sm = reinterpret_cast<float*>(smem);  // [n_active][rows_alloc]: m, then the weight
+    float* sl = sm + n_active * p.rows_alloc;     // [n_active][rows_alloc]: l
+    const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
+    const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
+    const uint32_t sstride = (uint32_t)p.rows_alloc * D * 4u;  // bytes between splits
+
+    // Partials of the first pass are loaded together with the (m, l) pairs.
+    constexpr int PRE = 8;
+    const int j = tid % TPP;
+    int pos = tid / TPP;
+    f32x4 pre[PRE];
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const int s2 = j + u * TPP;
+        pre[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (pos < P && s2 < n_active) {
+            const int rr = pos / ncol, col = col_lo + pos % ncol;
+            pre[u] = load_dev4(ro, (uint32_t)(rr * D + 4 * col) * 4u + (uint32_t)s2 * sstride);
+        }
+    }
+    for (int k = tid; k < n_active * nrows; k += kThreads) {
+        const int s2 = k / nrows, rr = k % nrows;
+        const f32x2 ml = load_dev2(rml, (uint32_t)(s2 * p.rows_alloc + rr) * 8u);
+        sm[s2 * p.rows_alloc + rr] = ml[0];
+        sl[s2 * p.rows_alloc + rr] = ml[1];
+    }
+    __syncthreads();
+    if (tid < nrows) {
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < n_active; ++s2) M = fmaxf(M, sm[s2 * p.rows_alloc + tid]);
+        const float mu = (M == -INFINITY) ? 0.f : M;
+        float den = 0.f;
+        for (int s2 = 0; s2 < n_active; ++s2) {
+            const float w = fast_exp2(sm[s2 * p.rows_alloc + tid] - mu);
+            sm[s2 * p.rows_alloc + tid] = w;
+            den += w * sl[s2 * p.rows_alloc + tid];
+        }
+        ms.rowM[tid] = M;
+        ms.rowDen[tid] = den;
+    }
+    __syncthreads();
+    for (int pass = 0; pass * per_pass < P; ++pass) {
+        pos = pass * per_pass + tid / TPP;
+        const bool act = pos < P;
+        const int rr = act ? pos / ncol : 0;
+        const int col = act ? col_lo + pos % ncol : 0;
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        if (act) {
+            const uint32_t src = (uint32_t)(rr * D + 4 * col) * 4u;
+            int s2 = j;
+            if (pass == 0) {
+#pragma unroll
+                for (int u = 0; u < PRE; ++u)
+                    if (j + u * TPP < n_active) a += sm[(j + u * TPP) * p.rows_alloc + rr] * pre[u];
+                s2 = j + PRE * TPP;
+            }
+            for (; s2 < n_active; s2 += TPP)
+                a += sm[s2 * p.rows_alloc + rr] * load_dev4(ro, src + (uint32_t)s2 * sstride);
+        }
+        for (int off = TPP / 2; off >= 1; off /= 2) {
+            a[0] += __shfl_xor(a[0], off);
+            a[1] += __shfl_xor(a[1], off);
+            a[2] += __shfl_xor(a[2], off);
+            a[3] += __shfl_xor(a[3], off);
+        }
+        if (act && j == 0) {
+            const float den = ms.rowDen[rr];
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            const size_t orow = out_row(p, b, g, row0 + rr, iq, gather);
+            store4<D>(p, orow, 4 * col, a * inv);
+            if (col == 0 && p.lse != nullptr)
+                p.lse[orow] = den > 0.f ? (ms.rowM[rr] + __log2f(den)) * kLn2 : -INFINITY;
+        }
+    }
+    __syncthreads();  // the LDS tables are reused by the next slice
+}
+
 // MODE 0: dense, 1: dense with keep_mask, 2: gather.
 template <int D, int RT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
@@ -165,11 +321,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS;
     constexpr bool GATHER = (MODE == 2);
     static_assert(2 * RT * NB * 64 * 16 <= kWaves * Gm::VBYTES, "merge area exceeds LDS");
+    static_assert(CK_MAX_SPLITS * 32 * 2 * 4 <= kWaves * Gm::VBYTES, "merge tables exceed LDS");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::VBYTES];
     __shared__ float s_ml[2][RT][64][2];
-    __shared__ float s_rowM[32], s_rowDen[32];
-    __shared__ int s_last;
+    __shared__ MergeScratch ms;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -187,45 +343,48 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     } else {
         b = t;
     }
+    const int row0 = rg * p.rows_alloc;
+    const int nrows = min(p.rows_alloc, p.R - row0);
 
-    int L = p.kv_lens[b];
-    L = L < 0 ? 0 : (L > p.cap ? p.cap : L);
+    // ---- prologue: the length and the query rows, loaded together ----------
+    const int L_raw = p.kv_lens[b];
+    bf16x8 qreg[RT][KS];
+    int i_r[RT];
+    {
+        const uint32_t q_bytes = (uint32_t)(p.n_q * p.Hq * D * 2);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)b * p.n_q * p.Hq * D, q_bytes);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int rr = rt * 16 + l16;
+            const int r = row0 + rr;
+            const int i = GATHER ? iq : r / p.G;
+            const int j = GATHER ? r : r % p.G;
+            i_r[rt] = i;
+            const uint32_t qoff =
+                rr < nrows ? (uint32_t)((i * p.Hq + g * p.G + j) * D + 8 * q4) * 2u : kOOB;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qreg[rt][ks] = __builtin_bit_cast(bf16x8, bload128(rq, qoff + 64u * ks));
+        }
+    }
+    const int L = L_raw < 0 ? 0 : (L_raw > p.cap ? p.cap : L_raw);
     const int span = GATHER ? p.W : L;
     const int C = chunk_len(span, p);
     const int n_active = span > 0 ? (span + C - 1) / C : 1;
     if (s >= n_active) return;
+    int32_t* cnt = p.ws_cnt + kCntStride * unit;
+    if (n_active > 1 && tid == 0) atomicAdd(cnt + kStarted, 1);  // this split has started
     const int pos_begin = s * C;
     const int pos_end = min(pos_begin + C, span);
 
-    const int row0 = rg * p.rows_alloc;
-    const int nrows = min(p.rows_alloc, p.R - row0);
-
-    // ---- per-lane query rows --------------------------------------------
     int lim_r[RT];
-    int i_r[RT];
-    bf16x8 qreg[RT][KS];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int rr = rt * 16 + l16;
-        const bool ok = rr < nrows;
-        const int r = row0 + rr;
-        const int i = GATHER ? iq : r / p.G;
         int lim = L;
         if (p.causal) {
-            lim = L - p.n_q + i + 1;
+            lim = L - p.n_q + i_r[rt] + 1;
             lim = lim < 0 ? 0 : (lim > L ? L : lim);
         }
-        lim_r[rt] = ok ? lim : 0;
-        i_r[rt] = i;
-        const uint16_t* qrow = p.q + out_row(p, b, g, ok ? r : row0, iq, GATHER) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ok) {
-                qreg[rt][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * q4);
-            } else {
-                qreg[rt][ks] = bf16x8{};
-            }
-        }
+        lim_r[rt] = (rt * 16 + l16) < nrows ? lim : 0;
     }
 
     // ---- cache views ------------------------------------------------------
@@ -264,17 +423,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     unsigned char* vlds = smem + wave * Gm::VBYTES;
     const int ntiles = (pos_end - pos_begin + TT - 1) / TT;
 
-    for (int tile = wave; tile < ntiles; tile += kWaves) {
-        const int tb = pos_begin + tile * TT;
+    // Gather: list entry of this lane for a tile (one entry per lane).
+    auto list_entry = [&](int tile) -> int {
+        const int pe = pos_begin + tile * TT + lane;
+        return (tile < ntiles && lane < TT && pe < pos_end) ? list[pe] : -1;
+    };
 
-        // -- row offsets of this tile's positions ----------------------------
-        uint32_t koff[MB];
-        uint32_t voff[VI];
-        uint64_t gvalid = 0;
+    // Issue the K and V loads (and mask loads) of one tile.
+    bf16x8 kreg[MB][KS];
+    u32x4 vreg[VI];
+    uint32_t mbits[RT][MB];
+    uint64_t gvalid = 0;
+    auto issue = [&](int tile, int jv) {
+        const int tb = pos_begin + tile * TT;
+        uint32_t koff[MB], voff[VI];
         if constexpr (GATHER) {
-            const int pe = tb + lane;
-            int jv = -1;
-            if (lane < TT && pe < pos_end) jv = list[pe];
             const bool ok = jv >= 0 && jv < lim_g;
             const uint32_t off = ok ? (uint32_t)jv * p.row_bytes : kOOB;
             gvalid = __ballot(ok);
@@ -288,18 +451,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 #pragma unroll
             for (int n = 0; n < VI; ++n) voff[n] = (uint32_t)(tb + n * RPI + lane / CPR) * p.row_bytes;
         }
-
-        // -- issue every load of the tile ------------------------------------
-        u32x4 vreg[VI];
-#pragma unroll
-        for (int n = 0; n < VI; ++n) vreg[n] = bload128(rv, voff[n] + (uint32_t)(lane % CPR) * 16u);
-        bf16x8 kreg[MB][KS];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kreg[mb][ks] = __builtin_bit_cast(bf16x8, bload128(rk, koff[mb] + (uint32_t)(32 * ks + 8 * q4) * 2u));
-        uint32_t mbits[RT][MB];
+                kreg[mb][ks] = __builtin_bit_cast(bf16x8, bload128<2>(rk, koff[mb] + (uint32_t)(32 * ks + 8 * q4) * 2u));
+#pragma unroll
+        for (int n = 0; n < VI; ++n) vreg[n] = bload128<2>(rv, voff[n] + (uint32_t)(lane % CPR) * 16u);
         if constexpr (MODE == 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -316,15 +474,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                     mbits[rt][mb] = bits;
                 }
         }
+    };
+
+    int jv_next = 0;
+    if (wave < ntiles) {
+        if constexpr (GATHER) jv_next = list_entry(wave);
+        issue(wave, jv_next);
+        if constexpr (GATHER) jv_next = list_entry(wave + kWaves);
+    }
+
+    for (int tile = wave; tile < ntiles; tile += kWaves) {
+        const int tb = pos_begin + tile * TT;
+        const uint64_t tvalid = gvalid;
+        uint32_t tmbits[RT][MB];
+        if constexpr (MODE == 1) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) tmbits[rt][mb] = mbits[rt][mb];
+        }
 
         // -- stage V rows in LDS ------------------------------------------
 #pragma unroll
-        for (int n = 0; n < VI; ++n) {
-            unsigned char* dst = vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16;
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            reinterpret_cast<u32x2*>(dst)[0] = u32x2{vreg[n][0], vreg[n][1]};
-            reinterpret_cast<u32x2*>(dst)[1] = u32x2{vreg[n][2], vreg[n][3]};
-        }
+        for (int n = 0; n < VI; ++n)
+            *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vreg[n];
 
         // -- S^T = K Q^T ---------------------------------------------------
         f32x4 sc[RT][MB];
@@ -337,6 +510,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 for (int ks = 0; ks < KS; ++ks) a = mfma(kreg[mb][ks], qreg[rt][ks], a);
                 sc[rt][mb] = a;
             }
+
+        // -- next tile's loads go out while this one finishes ---------------
+        const int next = tile + kWaves;
+        if (next < ntiles) {
+            issue(next, jv_next);
+            if constexpr (GATHER) jv_next = list_entry(next + kWaves);
+        }
 
         // -- online softmax (log2 domain) -----------------------------------
         bf16x8 pb[RT][KB];
@@ -352,10 +532,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                     const int off = 16 * mb + 4 * q4 + e;
                     bool ok;
                     if constexpr (GATHER) {
-                        ok = row_ok && ((gvalid >> off) & 1ull);
+                        ok = row_ok && ((tvalid >> off) & 1ull);
                     } else {
                         ok = tb + off < lim;
-                        if constexpr (MODE == 1) ok = ok && ((mbits[rt][mb] >> e) & 1u);
+                        if constexpr (MODE == 1) ok = ok && ((tmbits[rt][mb] >> e) & 1u);
                     }
                     const float x = ok ? sc[rt][mb][e] * p.scale_log2 : -INFINITY;
                     sc[rt][mb][e] = x;
@@ -378,32 +558,41 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 }
             st.l[rt] = st.l[rt] * alpha + lsum;
             st.m[rt] = m_new;
+            if (__any(alpha != 1.f)) {
 #pragma unroll
-            for (int n = 0; n < NB; ++n) st.o[rt][n] *= alpha;
+                for (int n = 0; n < NB; ++n) st.o[rt][n] *= alpha;
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pb[rt][kb][e] = e < 4 ? ph[2 * kb][e] : ph[2 * kb + 1][e - 4];
         }
 
-        // -- O^T += V^T P^T -------------------------------------------------
+        // -- O^T += V^T P^T with V^T read transposed from LDS ---------------
+        // Lane (group q4, k = l16) reads 4 head-dim values of token row
+        // 32kb + 4q4 + k/4 (and + 16 for the upper half of the k-slots).
         wave_lds_sync();
-        const __bf16* vl = reinterpret_cast<const __bf16*>(vlds);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            const unsigned char* row_lo = vlds + (32 * kb + 4 * q4 + (l16 >> 2)) * RS + (l16 & 3) * 8;
+            const unsigned char* row_hi = row_lo + 16 * RS;
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
-                bf16x8 va;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tl = 32 * kb + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
-                    va[e] = vl[tl * (RS / 2) + 16 * n + l16];
-                }
+                const lds_bf16x4 lo = lds_read_tr(row_lo + 32 * n);
+                const lds_bf16x4 hi = lds_read_tr(row_hi + 32 * n);
+                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) st.o[rt][n] = mfma(va, pb[rt][kb], st.o[rt][n]);
             }
+        }
         wave_lds_sync();
     }
+
+    // Whether every split of the unit has started; read now so the round trip
+    // overlaps the merge below.  The count only grows until the unit's last
+    // arrival, which cannot precede this split's own arrival.
+    int started_seen = 0;
+    if (n_active > 1 && tid == 0) started_seen = atomic_ld(cnt + kStarted);
 
     // Row sums were kept per lane (each lane saw 4 of every 16 tokens).
 #pragma unroll
@@ -464,83 +653,77 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     }
 
     // ---- several splits: publish this split's partial -----------------------
-    const size_t part0 = ((size_t)unit * p.splits + s) * p.rows_alloc;
+    // Wave 0 writes it with device-coherent stores and waits for them to
+    // complete before its thread 0 announces the arrival, so whichever
+    // workgroup sees the arrival count reach n_active reads complete partials
+    // with device-coherent loads (no L2 writeback or invalidate is needed).
     if (wave == 0) {
+        const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
+        const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int rr = rt * 16 + l16;
             if (rr >= nrows) continue;
-            float* dst = p.ws_o + (part0 + rr) * D;
+            const uint32_t prow = (uint32_t)(s * p.rows_alloc + rr);
 #pragma unroll
-            for (int n = 0; n < NB; ++n) *reinterpret_cast<f32x4*>(dst + 16 * n + 4 * q4) = st.o[rt][n];
-            if (q4 == 0) {
-                p.ws_ml[(part0 + rr) * 2 + 0] = st.m[rt];
-                p.ws_ml[(part0 + rr) * 2 + 1] = st.l[rt];
-            }
+            for (int n = 0; n < NB; ++n) store_dev<f32x4>(ro, (prow * D + 16 * n + 4 * q4) * 4u, st.o[rt][n]);
+            if (q4 == 0) store_dev<f32x2>(rml, prow * 8u, f32x2{st.m[rt], st.l[rt]});
         }
+        wait_stores();
     }
-    __threadfence();
+    if (tid == 0) ms.flag = atomicAdd(cnt + kArrived, 1);  // arrival rank
     __syncthreads();
-    if (tid == 0) {
-        const int prev = atomicAdd(p.ws_cnt + unit, 1);
-        s_last = (prev == n_active - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    const int rank = ms.flag;
 
-    // ---- last split of the unit: merge all partials ------------------------
-    float* sm = reinterpret_cast<float*>(smem);   // [n_active][rows_alloc] m, then weight
-    float* sl = sm + n_active * p.rows_alloc;      // [n_active][rows_alloc] l
-    const size_t base0 = (size_t)unit * p.splits * p.rows_alloc;
-    for (int k = tid; k < n_active * nrows; k += kThreads) {
-        const int s2 = k / nrows, rr = k % nrows;
-        const size_t pi = base0 + (size_t)s2 * p.rows_alloc + rr;
-        sm[s2 * p.rows_alloc + rr] = p.ws_ml[pi * 2 + 0];
-        sl[s2 * p.rows_alloc + rr] = p.ws_ml[pi * 2 + 1];
-    }
-    __syncthreads();
-    if (tid < nrows) {
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < n_active; ++s2) M = fmaxf(M, sm[s2 * p.rows_alloc + tid]);
-        const float mu = (M == -INFINITY) ? 0.f : M;
-        float den = 0.f;
-        for (int s2 = 0; s2 < n_active; ++s2) {
-            const float w = fast_exp2(sm[s2 * p.rows_alloc + tid] - mu);
-            sm[s2 * p.rows_alloc + tid] = w;
-            den += w * sl[s2 * p.rows_alloc + tid];
+    // ---- merge: the unit's last split and the ns-1 splits that arrived just
+    // before it share the ns column slices.  The last split always takes slice
+    // 0; the split of rank n_active-1-c may take slice c, by winning that
+    // slice's claim flag, but only if every split of the unit was already
+    // running, so its wait for the other arrivals can never depend on a
+    // workgroup that has not been scheduled.  After its own slice the last
+    // split claims and merges whatever slice is still unclaimed.
+    const int ns = min(p.slices, n_active);
+    const bool last = rank == n_active - 1;
+    const bool helper = !last && rank >= n_active - ns;
+    if (!last && !helper) return;
+    __syncthreads();  // everyone has read ms.flag
+    if (last) {
+        merge_slice<D>(p, smem, ms, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
+        if (tid >= 1 && tid < ns) ms.owned[tid] = atomicExch(cnt + kSliceFlag + tid, 1) == 0;
+        __syncthreads();
+        for (int c = 1; c < ns; ++c)
+            if (ms.owned[c]) merge_slice<D>(p, smem, ms, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+    } else {
+        const int c = n_active - 1 - rank;
+        if (tid == 0) {
+            int ok = 0;
+            if (started_seen == n_active && atomicExch(cnt + kSliceFlag + c, 1) == 0) {
+                ok = 1;
+                int spins = 0;
+                while (atomic_ld(cnt + kArrived) < n_active) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins > (1 << 22)) {  // cannot happen while every split runs
+                        ok = 0;
+                        break;
+                    }
+                }
+            }
+            ms.flag = ok;
         }
-        s_rowM[tid] = M;
-        s_rowDen[tid] = den;
+        __syncthreads();
+        if (ms.flag) merge_slice<D>(p, smem, ms, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
     }
-    __syncthreads();
-    constexpr int D4 = D / 4;
-    for (int k = tid; k < nrows * D4; k += kThreads) {
-        const int rr = k / D4, d = (k % D4) * 4;
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        const float* src = p.ws_o + (base0 + rr) * D + d;
-        const size_t sstride = (size_t)p.rows_alloc * D;
-        int s2 = 0;
-        for (; s2 + 4 <= n_active; s2 += 4) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 0) * sstride);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 1) * sstride);
-            const f32x4 x2 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 2) * sstride);
-            const f32x4 x3 = *reinterpret_cast<const f32x4*>(src + (size_t)(s2 + 3) * sstride);
-            a += sm[(s2 + 0) * p.rows_alloc + rr] * x0;
-            a += sm[(s2 + 1) * p.rows_alloc + rr] * x1;
-            a += sm[(s2 + 2) * p.rows_alloc + rr] * x2;
-            a += sm[(s2 + 3) * p.rows_alloc + rr] * x3;
+    if (tid == 0) {
+        // The ns participants each report once; the final report returns the
+        // unit's counters and claim flags to zero for the next launch.
+        if (atomicAdd(cnt + kFinished, 1) == ns - 1) {
+            atomic_st(cnt + kStarted, 0);
+            atomic_st(cnt + kArrived, 0);
+            atomic_st(cnt + kFinished, 0);
+            for (int c = 1; c < ns; ++c) atomic_st(cnt + kSliceFlag + c, 0);
         }
-        for (; s2 < n_active; ++s2)
-            a += sm[s2 * p.rows_alloc + rr] * *reinterpret_cast<const f32x4*>(src + (size_t)s2 * sstride);
-        const float den = s_rowDen[rr];
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        const size_t orow = out_row(p, b, g, row0 + rr, iq, GATHER);
-        store4<D>(p, orow, d, a * inv);
-        if (d == 0 && p.lse != nullptr)
-            p.lse[orow] = den > 0.f ? (s_rowM[rr] + __log2f(den)) * kLn2 : -INFINITY;
     }
-    if (tid == 0) __hip_atomic_store(p.ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ host ----
@@ -566,6 +749,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     const int64_t row_bytes = (int64_t)s->Hkv * s->D * 2;
     if ((int64_t)(s->cap + TT) * row_bytes >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     if (W == 0 && (int64_t)s->n_q * s->Hkv * s->cap + TT >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+    if ((int64_t)s->n_q * s->Hq * s->D * 2 >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     const int64_t R = W > 0 ? G : (int64_t)s->n_q * G;
     const int rows_per_group = R <= 16 ? 16 : 32;
     const int64_t RG = (R + rows_per_group - 1) / rows_per_group;
@@ -600,12 +784,19 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     pl->rows = (int32_t)R;
     pl->row_groups = (int32_t)RG;
     pl->rows_per_group = rows_per_group;
+    // Column slices of the merge: about 16 KiB of partials each, at most one
+    // per 4 columns.
+    const int64_t rows_eff = R < rows_per_group ? R : rows_per_group;
+    const int64_t merge_bytes = splits * rows_eff * s->D * 4;
+    int64_t slices = 1;
+    while (slices * 16384 < merge_bytes && slices < s->D / 4 && slices < 64) slices *= 2;
+    pl->slices = (int32_t)slices;
     if (splits == 1) {
         pl->workspace_bytes = 0;
     } else {
         const size_t parts = (size_t)units * (size_t)splits * (size_t)rows_per_group;
-        pl->workspace_bytes = align256(parts * s->D * sizeof(float)) + align256(parts * 2 * sizeof(float)) +
-                              align256((size_t)units * sizeof(int32_t));
+        pl->workspace_bytes = align256((size_t)units * 256 * sizeof(int32_t)) +
+                              align256(parts * s->D * sizeof(float)) + align256(parts * 2 * sizeof(float));
     }
     return CK_OK;
 }
@@ -685,7 +876,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
         const size_t parts = (size_t)pl.units * pl.splits * pl.rows_per_group;
         char* w = static_cast<char*>(workspace);
         kp.ws_cnt = reinterpret_cast<int32_t*>(w);
-        w += align256((size_t)pl.units * sizeof(int32_t));
+        w += align256((size_t)pl.units * 256 * sizeof(int32_t));
         kp.ws_o = reinterpret_cast<float*>(w);
         w += align256(parts * s->D * sizeof(float));
         kp.ws_ml = reinterpret_cast<float*>(w);
@@ -703,6 +894,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.S_target = pl.split_target;
     kp.c_max = pl.chunk_max;
     kp.gran = pl.granule;
+    kp.slices = pl.slices;
     kp.W = W;
     kp.idx_head_stride = idx_head_stride;
     kp.scale_log2 = (float)((double)scale * 1.4426950408889634074);

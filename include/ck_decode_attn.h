@@ -42,8 +42,9 @@
  *
  * Workspace: when the plan splits the KV range (see
  * ck_decode_attn_workspace_size) the caller passes a device buffer of at
- * least that many bytes, 256-byte aligned.  It starts with one int32
- * completion counter per unit, which must be zero when a launch starts;
+ * least that many bytes, 256-byte aligned.  It starts with a 1 KiB block of
+ * int32 completion counters per unit, which must be zero when a launch
+ * starts;
  * every launch leaves its counters at zero again (the partial results after
  * them are scratch).  So a buffer ZEROED ONCE serves any number of launches
  * of the same plan (same shape, W, num_splits and device), eager or replayed
@@ -108,6 +109,7 @@ typedef struct ck_decode_plan {
     int32_t rows;            /* query rows per unit                          */
     int32_t row_groups;      /* units per (sequence, query, KV head)         */
     int32_t rows_per_group;  /* rows handled by one workgroup (16 or 32)     */
+    int32_t slices;          /* column slices the split merge is cut into    */
     size_t workspace_bytes;  /* 0 when no launch of this plan can split      */
 } ck_decode_plan;
 
