@@ -214,20 +214,30 @@ __device__ __forceinline__ void store4(const KParams& p, size_t row, int d, f32x
 }
 
 struct MergeScratch {
-    float rowM[32], rowDen[32];
     int flag;
-    int started_seen;
     int owned[kMaxSlices];
 };
 
 // Merge column slice `c` of `ns` for one unit from the n_active published
-// partials: O = sum_s w_s acc_s / sum_s w_s l_s with w_s = 2^(m_s - max m).
-// Each output column group (row, 4 columns) is summed by TPP neighbouring
-// lanes, each over a strided subset of the splits, then reduced by shuffles.
+// partials (acc_s, m_s, l_s):  O = sum_s w_s acc_s / sum_s w_s l_s with
+// w_s = 2^(m_s - max m).  Each output group (row, 4 columns) is taken by TPP
+// neighbouring lanes; a lane folds its strided subset of the splits into a
+// running (max, denominator, accumulator) with the online-softmax rule, and
+// the TPP lane states are then folded together by shuffles.  All loads of a
+// lane are issued before the first use, so the merge costs one round trip.
+__device__ __forceinline__ void fold(float& M, float& den, f32x4& acc, float m2, float l2, f32x4 a2) {
+    float w1, w2, m;
+    merge_scale(M, m2, w1, w2, m);
+    M = m;
+    den = w1 * den + w2 * l2;
+    acc = w1 * acc + w2 * a2;
+}
+
 template <int D>
-__device__ void merge_slice(const KParams& p, unsigned char* smem, MergeScratch& ms, int unit, int n_active,
-                            int nrows, int c, int ns, int b, int g, int iq, bool gather, int row0) {
+__device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows, int c, int ns, int b, int g,
+                            int iq, bool gather, int row0) {
     constexpr int D4 = D / 4;
+    constexpr int PRE = 8;
     const int tid = threadIdx.x;
     const int col_lo = c * D4 / ns, col_hi = (c + 1) * D4 / ns;
     const int ncol = col_hi - col_lo;
@@ -235,82 +245,51 @@ __device__ void merge_slice(const KParams& p, unsigned char* smem, MergeScratch&
     int TPP = 1;
     while (TPP < 64 && 2 * TPP * P <= kThreads) TPP *= 2;
     const int per_pass = kThreads / TPP;
-    float* sm = reinterpret_cast<float*>(smem);  // [n_active][rows_alloc]: m, then the weight
-    float* sl = sm + n_active * p.rows_alloc;     // [n_active][rows_alloc]: l
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
     const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
     const uint32_t sstride = (uint32_t)p.rows_alloc * D * 4u;  // bytes between splits
-
-    // Partials of the first pass are loaded together with the (m, l) pairs.
-    constexpr int PRE = 8;
     const int j = tid % TPP;
-    int pos = tid / TPP;
-    f32x4 pre[PRE];
-#pragma unroll
-    for (int u = 0; u < PRE; ++u) {
-        const int s2 = j + u * TPP;
-        pre[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (pos < P && s2 < n_active) {
-            const int rr = pos / ncol, col = col_lo + pos % ncol;
-            pre[u] = load_dev4(ro, (uint32_t)(rr * D + 4 * col) * 4u + (uint32_t)s2 * sstride);
-        }
-    }
-    for (int k = tid; k < n_active * nrows; k += kThreads) {
-        const int s2 = k / nrows, rr = k % nrows;
-        const f32x2 ml = load_dev2(rml, (uint32_t)(s2 * p.rows_alloc + rr) * 8u);
-        sm[s2 * p.rows_alloc + rr] = ml[0];
-        sl[s2 * p.rows_alloc + rr] = ml[1];
-    }
-    __syncthreads();
-    if (tid < nrows) {
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < n_active; ++s2) M = fmaxf(M, sm[s2 * p.rows_alloc + tid]);
-        const float mu = (M == -INFINITY) ? 0.f : M;
-        float den = 0.f;
-        for (int s2 = 0; s2 < n_active; ++s2) {
-            const float w = fast_exp2(sm[s2 * p.rows_alloc + tid] - mu);
-            sm[s2 * p.rows_alloc + tid] = w;
-            den += w * sl[s2 * p.rows_alloc + tid];
-        }
-        ms.rowM[tid] = M;
-        ms.rowDen[tid] = den;
-    }
-    __syncthreads();
     for (int pass = 0; pass * per_pass < P; ++pass) {
-        pos = pass * per_pass + tid / TPP;
+        const int pos = pass * per_pass + tid / TPP;
         const bool act = pos < P;
         const int rr = act ? pos / ncol : 0;
         const int col = act ? col_lo + pos % ncol : 0;
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        if (act) {
-            const uint32_t src = (uint32_t)(rr * D + 4 * col) * 4u;
-            int s2 = j;
-            if (pass == 0) {
+        const uint32_t xoff = (uint32_t)(rr * D + 4 * col) * 4u;
+        const uint32_t moff = (uint32_t)rr * 8u;
+        float M = -INFINITY, den = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 x[PRE];
+        f32x2 ml[PRE];
 #pragma unroll
-                for (int u = 0; u < PRE; ++u)
-                    if (j + u * TPP < n_active) a += sm[(j + u * TPP) * p.rows_alloc + rr] * pre[u];
-                s2 = j + PRE * TPP;
-            }
-            for (; s2 < n_active; s2 += TPP)
-                a += sm[s2 * p.rows_alloc + rr] * load_dev4(ro, src + (uint32_t)s2 * sstride);
+        for (int u = 0; u < PRE; ++u) {
+            const int s2 = j + u * TPP;
+            const bool ok = act && s2 < n_active;
+            x[u] = ok ? load_dev4(ro, xoff + (uint32_t)s2 * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+            ml[u] = ok ? load_dev2(rml, moff + (uint32_t)(s2 * p.rows_alloc) * 8u) : f32x2{-INFINITY, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) fold(M, den, acc, ml[u][0], ml[u][1], x[u]);
+        for (int s2 = j + PRE * TPP; act && s2 < n_active; s2 += TPP) {
+            const f32x2 m2 = load_dev2(rml, moff + (uint32_t)(s2 * p.rows_alloc) * 8u);
+            fold(M, den, acc, m2[0], m2[1], load_dev4(ro, xoff + (uint32_t)s2 * sstride));
         }
         for (int off = TPP / 2; off >= 1; off /= 2) {
-            a[0] += __shfl_xor(a[0], off);
-            a[1] += __shfl_xor(a[1], off);
-            a[2] += __shfl_xor(a[2], off);
-            a[3] += __shfl_xor(a[3], off);
+            const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(den, off);
+            f32x4 a2;
+            a2[0] = __shfl_xor(acc[0], off);
+            a2[1] = __shfl_xor(acc[1], off);
+            a2[2] = __shfl_xor(acc[2], off);
+            a2[3] = __shfl_xor(acc[3], off);
+            fold(M, den, acc, m2, l2, a2);
         }
         if (act && j == 0) {
-            const float den = ms.rowDen[rr];
             const float inv = den > 0.f ? 1.f / den : 0.f;
             const size_t orow = out_row(p, b, g, row0 + rr, iq, gather);
-            store4<D>(p, orow, 4 * col, a * inv);
-            if (col == 0 && p.lse != nullptr)
-                p.lse[orow] = den > 0.f ? (ms.rowM[rr] + __log2f(den)) * kLn2 : -INFINITY;
+            store4<D>(p, orow, 4 * col, acc * inv);
+            if (col == 0 && p.lse != nullptr) p.lse[orow] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
         }
     }
-    __syncthreads();  // the LDS tables are reused by the next slice
 }
 
 // MODE 0: dense, 1: dense with keep_mask, 2: gather.
@@ -321,7 +300,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS;
     constexpr bool GATHER = (MODE == 2);
     static_assert(2 * RT * NB * 64 * 16 <= kWaves * Gm::VBYTES, "merge area exceeds LDS");
-    static_assert(CK_MAX_SPLITS * 32 * 2 * 4 <= kWaves * Gm::VBYTES, "merge tables exceed LDS");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::VBYTES];
     __shared__ float s_ml[2][RT][64][2];
@@ -422,6 +400,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 
     unsigned char* vlds = smem + wave * Gm::VBYTES;
     const int ntiles = (pos_end - pos_begin + TT - 1) / TT;
+    // Whether every split of the unit has started: thread 0 reads the count
+    // after its first tile's data has arrived, so the round trip hides under
+    // the tile loop.  The count only grows until the unit's last arrival,
+    // which cannot precede this split's own arrival.
+    int started_seen = 0;
 
     // Gather: list entry of this lane for a tile (one entry per lane).
     auto list_entry = [&](int tile) -> int {
@@ -511,6 +494,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 sc[rt][mb] = a;
             }
 
+        if (tid == 0 && tile == 0 && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
+
         // -- next tile's loads go out while this one finishes ---------------
         const int next = tile + kWaves;
         if (next < ntiles) {
@@ -587,12 +572,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         }
         wave_lds_sync();
     }
-
-    // Whether every split of the unit has started; read now so the round trip
-    // overlaps the merge below.  The count only grows until the unit's last
-    // arrival, which cannot precede this split's own arrival.
-    int started_seen = 0;
-    if (n_active > 1 && tid == 0) started_seen = atomic_ld(cnt + kStarted);
 
     // Row sums were kept per lane (each lane saw 4 of every 16 tokens).
 #pragma unroll
@@ -681,19 +660,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     // 0; the split of rank n_active-1-c may take slice c, by winning that
     // slice's claim flag, but only if every split of the unit was already
     // running, so its wait for the other arrivals can never depend on a
-    // workgroup that has not been scheduled.  After its own slice the last
-    // split claims and merges whatever slice is still unclaimed.
+    // workgroup that has not been scheduled.  After slice 0 the last split
+    // claims and merges every slice no helper took.
     const int ns = min(p.slices, n_active);
     const bool last = rank == n_active - 1;
     const bool helper = !last && rank >= n_active - ns;
     if (!last && !helper) return;
     __syncthreads();  // everyone has read ms.flag
     if (last) {
-        merge_slice<D>(p, smem, ms, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
+        merge_slice<D>(p, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
         if (tid >= 1 && tid < ns) ms.owned[tid] = atomicExch(cnt + kSliceFlag + tid, 1) == 0;
         __syncthreads();
         for (int c = 1; c < ns; ++c)
-            if (ms.owned[c]) merge_slice<D>(p, smem, ms, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+            if (ms.owned[c]) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
     } else {
         const int c = n_active - 1 - rank;
         if (tid == 0) {
@@ -712,7 +691,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
             ms.flag = ok;
         }
         __syncthreads();
-        if (ms.flag) merge_slice<D>(p, smem, ms, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+        if (ms.flag) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
     }
     if (tid == 0) {
         // The ns participants each report once; the final report returns the
