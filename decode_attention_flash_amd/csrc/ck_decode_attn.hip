@@ -299,10 +299,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS;
     constexpr bool GATHER = (MODE == 2);
-    static_assert(2 * RT * NB * 64 * 16 <= kWaves * Gm::VBYTES, "merge area exceeds LDS");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::VBYTES];
-    __shared__ float s_ml[2][RT][64][2];
+    __shared__ float s_ml[kWaves][RT][64][2];
     __shared__ MergeScratch ms;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -580,77 +579,75 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         st.l[rt] += __shfl_xor(st.l[rt], 32);
     }
 
-    // ---- merge the four waves' states through LDS -------------------------
+    // ---- merge the four waves' states and publish ---------------------------
+    // Every wave dumps its (m, l, acc) to LDS in its MFMA register layout; then
+    // each thread merges a few (row, 4 columns) output groups of the valid
+    // rows across the four waves and writes them: the final output when the
+    // unit has a single split, else this split's partial (unnormalised acc,
+    // m, l) with device-coherent stores.  Row tiles are dumped in rounds when
+    // all of them do not fit in LDS at once.
+    constexpr int RT_ROUND = (kWaves * RT * NB * 64 * 16 <= kWaves * Gm::VBYTES) ? RT : 1;
+    static_assert(kWaves * RT_ROUND * NB * 64 * 16 <= kWaves * Gm::VBYTES, "merge area exceeds LDS");
     f32x4* dump = reinterpret_cast<f32x4*>(smem);
-    auto dump_state = [&](int slot) {
+    const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
+    const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
+        s_ml[wave][rt][lane][0] = st.m[rt];
+        s_ml[wave][rt][lane][1] = st.l[rt];
+    }
 #pragma unroll
-            for (int n = 0; n < NB; ++n) dump[((slot * RT + rt) * NB + n) * 64 + lane] = st.o[rt][n];
-            s_ml[slot][rt][lane][0] = st.m[rt];
-            s_ml[slot][rt][lane][1] = st.l[rt];
-        }
-    };
-    auto merge_state = [&](int slot) {
+    for (int rt0 = 0; rt0 < RT; rt0 += RT_ROUND) {
+        __syncthreads();  // the V staging area (or the previous round) is free
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            float w1, w2, m;
-            merge_scale(st.m[rt], s_ml[slot][rt][lane][0], w1, w2, m);
-            st.m[rt] = m;
-            st.l[rt] = w1 * st.l[rt] + w2 * s_ml[slot][rt][lane][1];
+        for (int rl = 0; rl < RT_ROUND; ++rl)
 #pragma unroll
-            for (int n = 0; n < NB; ++n)
-                st.o[rt][n] = w1 * st.o[rt][n] + w2 * dump[((slot * RT + rt) * NB + n) * 64 + lane];
-        }
-    };
-    __syncthreads();
-    if (wave >= 2) dump_state(wave - 2);
-    __syncthreads();
-    if (wave < 2) merge_state(wave);
-    __syncthreads();
-    if (wave == 1) dump_state(0);
-    __syncthreads();
-    if (wave == 0) merge_state(0);
-
-    // ---- single split: write the result directly ---------------------------
-    if (n_active == 1) {
-        if (wave == 0) {
+            for (int n = 0; n < NB; ++n) dump[((wave * RT_ROUND + rl) * NB + n) * 64 + lane] = st.o[rt0 + rl][n];
+        __syncthreads();
+        constexpr int D4 = D / 4;
+        const int rows_here = min(nrows - rt0 * 16, RT_ROUND * 16);
+        for (int k = tid; k < rows_here * D4; k += kThreads) {
+            const int rl16 = k / D4, d4 = k % D4;
+            const int rl = rl16 >> 4, r16 = rl16 & 15;
+            const int rr = rt0 * 16 + rl16;
+            const int src = (d4 & 3) * 16 + r16;  // lane holding (row, 4 columns)
+            float mw[kWaves], M = -INFINITY;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const int rr = rt * 16 + l16;
-                if (rr >= nrows) continue;
+            for (int w = 0; w < kWaves; ++w) {
+                mw[w] = s_ml[w][rt0 + rl][r16][0];
+                M = fmaxf(M, mw[w]);
+            }
+            const float mu = (M == -INFINITY) ? 0.f : M;
+            float den = 0.f;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float wt = fast_exp2(mw[w] - mu);
+                den += wt * s_ml[w][rt0 + rl][r16][1];
+                a += wt * dump[((w * RT_ROUND + rl) * NB + (d4 >> 2)) * 64 + src];
+            }
+            if (n_active == 1) {
                 const size_t orow = out_row(p, b, g, row0 + rr, iq, GATHER);
-                const float l = st.l[rt];
-                const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-                for (int n = 0; n < NB; ++n) store4<D>(p, orow, 16 * n + 4 * q4, st.o[rt][n] * inv);
-                if (p.lse != nullptr && q4 == 0)
-                    p.lse[orow] = l > 0.f ? (st.m[rt] + __log2f(l)) * kLn2 : -INFINITY;
+                const float inv = den > 0.f ? 1.f / den : 0.f;
+                store4<D>(p, orow, 4 * d4, a * inv);
+                if (d4 == 0 && p.lse != nullptr) p.lse[orow] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+            } else {
+                const uint32_t prow = (uint32_t)(s * p.rows_alloc + rr);
+                store_dev<f32x4>(ro, (prow * D + 4 * d4) * 4u, a);
+                if (d4 == 0) store_dev<f32x2>(rml, prow * 8u, f32x2{M, den});
             }
         }
-        return;
     }
+    if (n_active == 1) return;
 
-    // ---- several splits: publish this split's partial -----------------------
-    // Wave 0 writes it with device-coherent stores and waits for them to
-    // complete before its thread 0 announces the arrival, so whichever
+    // ---- several splits: announce the arrival -----------------------------
+    // Each wave waits for its own partial stores to complete before the
+    // barrier, and thread 0 announces the arrival after it, so whichever
     // workgroup sees the arrival count reach n_active reads complete partials
     // with device-coherent loads (no L2 writeback or invalidate is needed).
-    if (wave == 0) {
-        const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
-        const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
-        const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int rr = rt * 16 + l16;
-            if (rr >= nrows) continue;
-            const uint32_t prow = (uint32_t)(s * p.rows_alloc + rr);
-#pragma unroll
-            for (int n = 0; n < NB; ++n) store_dev<f32x4>(ro, (prow * D + 16 * n + 4 * q4) * 4u, st.o[rt][n]);
-            if (q4 == 0) store_dev<f32x2>(rml, prow * 8u, f32x2{st.m[rt], st.l[rt]});
-        }
-        wait_stores();
-    }
+    wait_stores();
+    __syncthreads();
     if (tid == 0) ms.flag = atomicAdd(cnt + kArrived, 1);  // arrival rank
     __syncthreads();
     const int rank = ms.flag;
