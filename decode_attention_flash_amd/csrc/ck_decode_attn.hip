@@ -81,6 +81,7 @@ struct KParams {
     int32_t* ws_cnt;  // per unit kCntStride ints: counters and slice claim flags
     int32_t B, n_q, Hq, Hkv, G, cap;
     int32_t R, RG, rows_alloc;
+    int32_t units;   // work units (grid = splits x units)
     int32_t splits;  // grid splits per unit
     int32_t S_target, c_max, gran;
     int32_t slices;  // column slices of the merge
@@ -306,8 +307,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int s = blockIdx.x % p.splits;
-    const int unit = blockIdx.x / p.splits;
+    // Split-major numbering: the units' first splits come first and the
+    // (often inactive) high splits last; workgroups are dealt round-robin to
+    // the XCDs, so a unit's splits share the XCD of index unit % 8 whenever
+    // the unit count is a multiple of 8.
+    const int unit = blockIdx.x % p.units;
+    const int s = blockIdx.x / p.units;
     int t = unit;
     const int rg = t % p.RG;
     t /= p.RG;
@@ -866,6 +871,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.R = pl.rows;
     kp.RG = pl.row_groups;
     kp.rows_alloc = pl.rows_per_group;
+    kp.units = pl.units;
     kp.splits = pl.splits;
     kp.S_target = pl.split_target;
     kp.c_max = pl.chunk_max;
