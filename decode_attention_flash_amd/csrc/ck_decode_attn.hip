@@ -303,16 +303,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::VBYTES];
     __shared__ float s_ml[kWaves][RT][64][2];
+    __shared__ bf16x8 q_lds[RT * KS * 64];
     __shared__ MergeScratch ms;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    // Split-major numbering: the units' first splits come first and the
-    // (often inactive) high splits last; workgroups are dealt round-robin to
-    // the XCDs, so a unit's splits share the XCD of index unit % 8 whenever
-    // the unit count is a multiple of 8.
-    const int unit = blockIdx.x % p.units;
+    // Split-major numbering: every unit's first split comes first and the
+    // (often inactive) high splits last.  Workgroups are dealt round-robin to
+    // the 8 XCDs; rotating the unit by the split index moves consecutive
+    // splits of one unit to different XCDs, so each XCD gets a fair share of
+    // long and short sequences.
     const int s = blockIdx.x / p.units;
+    const int unit = (blockIdx.x % p.units + s) % p.units;
     int t = unit;
     const int rg = t % p.RG;
     t /= p.RG;
@@ -329,24 +331,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     const int nrows = min(p.rows_alloc, p.R - row0);
 
     // ---- prologue: the length and the query rows, loaded together ----------
+    // The query rows are the B operand of every QK^T MFMA.  They are the same
+    // for the four waves, so the workgroup loads them once, cooperatively, into
+    // LDS in operand order ([row tile][k-step][lane], 16 bytes each).
     const int L_raw = p.kv_lens[b];
-    bf16x8 qreg[RT][KS];
-    int i_r[RT];
+    constexpr int QF = RT * KS * 64 / kThreads;  // fragments per thread
+    bf16x8 qfrag[QF];
     {
         const uint32_t q_bytes = (uint32_t)(p.n_q * p.Hq * D * 2);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)b * p.n_q * p.Hq * D, q_bytes);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int rr = rt * 16 + l16;
+        for (int u = 0; u < QF; ++u) {
+            const int f = tid + u * kThreads;
+            const int rt = f / (KS * 64), ks = (f / 64) % KS, fl = f % 64;
+            const int rr = rt * 16 + (fl & 15);
             const int r = row0 + rr;
             const int i = GATHER ? iq : r / p.G;
             const int j = GATHER ? r : r % p.G;
-            i_r[rt] = i;
             const uint32_t qoff =
-                rr < nrows ? (uint32_t)((i * p.Hq + g * p.G + j) * D + 8 * q4) * 2u : kOOB;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qreg[rt][ks] = __builtin_bit_cast(bf16x8, bload128(rq, qoff + 64u * ks));
+                rr < nrows ? (uint32_t)((i * p.Hq + g * p.G + j) * D + 32 * ks + 8 * (fl >> 4)) * 2u : kOOB;
+            qfrag[u] = __builtin_bit_cast(bf16x8, bload128(rq, qoff));
         }
+    }
+    int i_r[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = row0 + rt * 16 + l16;
+        i_r[rt] = GATHER ? iq : r / p.G;
     }
     const int L = L_raw < 0 ? 0 : (L_raw > p.cap ? p.cap : L_raw);
     const int span = GATHER ? p.W : L;
@@ -463,12 +474,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         }
     };
 
+    // Query fragments to LDS before the first tile's loads are issued (they
+    // arrived with the length), then an LDS-only barrier after the issue.
+#pragma unroll
+    for (int u = 0; u < QF; ++u) q_lds[tid + u * kThreads] = qfrag[u];
     int jv_next = 0;
     if (wave < ntiles) {
         if constexpr (GATHER) jv_next = list_entry(wave);
         issue(wave, jv_next);
         if constexpr (GATHER) jv_next = list_entry(wave + kWaves);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
     for (int tile = wave; tile < ntiles; tile += kWaves) {
         const int tb = pos_begin + tile * TT;
@@ -494,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
             for (int mb = 0; mb < MB; ++mb) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) a = mfma(kreg[mb][ks], qreg[rt][ks], a);
+                for (int ks = 0; ks < KS; ++ks) a = mfma(kreg[mb][ks], q_lds[(rt * KS + ks) * 64 + lane], a);
                 sc[rt][mb] = a;
             }
 
@@ -712,7 +730,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 constexpr int kWgPerCu = 1;
 
 static int tile_tokens(int D) { return D == 256 ? 32 : 64; }
-static int chunk_max_tokens(int D) { return D == 256 ? 512 : 1024; }
+// When the units alone fill the chip, a long sequence is still cut into
+// ranges of at most this many K+V bytes, so ragged batches balance over the
+// CUs; each split then streams enough to amortise its fixed costs.
+constexpr int64_t kChunkMaxBytes = 2 << 20;
+static int chunk_max_tokens(int D) { return (int)(kChunkMaxBytes / (4 * D)); }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -739,7 +761,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     int64_t target, cmax;
     if (num_splits == 0) {
         target = ((int64_t)num_cus * kWgPerCu + units - 1) / units;
-        cmax = chunk_max_tokens(s->D);
+        cmax = 2 * units >= num_cus ? chunk_max_tokens(s->D) : 0;
     } else {
         target = num_splits;
         cmax = 0;

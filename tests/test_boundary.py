@@ -46,6 +46,11 @@ def test_plan_fills_the_chip_at_batch_one():
     assert p["workspace_bytes"] > 0
 
 
+def test_plan_single_sequence_has_no_chunk_limit():
+    p = ck.plan(shape(), num_cus=256)
+    assert p["chunk_max"] == 0
+
+
 def test_plan_does_not_depend_on_capacity_for_split_target():
     a = ck.plan(shape(cap=8199), num_cus=256)
     b = ck.plan(shape(cap=24007), num_cus=256)
@@ -56,7 +61,7 @@ def test_plan_does_not_depend_on_capacity_for_split_target():
 def test_plan_batched_uses_chunk_limit():
     p = ck.plan(shape(B=32, Hq=32, Hkv=8, D=128, cap=32768), num_cus=256)
     assert p["units"] == 256 and p["split_target"] == 1
-    assert p["chunk_max"] == 1024 and p["splits"] == 32
+    assert p["chunk_max"] == 4096 and p["splits"] == 8
 
 
 def test_plan_causal_window_row_groups():
