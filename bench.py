@@ -141,6 +141,36 @@ def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None):
                 kv_gbs=kv_bytes / us / 1e3, frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS), idxs
 
 
+def calibrate_copy(nbytes: int = 1 << 28, reps: int = 3) -> None:
+    """A plain device copy of known size, so that a counter profile of this
+    run can scale its byte counters (FETCH_SIZE / WRITE_SIZE) against it."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "decode_attention_flash_amd", "csrc", "ck_decode_attn.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source for this workload; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_kernel_d256_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != kernel_source_digest() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(seconds: float):
     """The oracle on the host cores: full layer-steps of the headline workload."""
     import numpy as np
@@ -173,6 +203,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true", help="skip the sweeps and the CPU leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device copy (reference for counter profiles)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -200,6 +232,9 @@ def main():
     log(f"headline: kv_len={L0}")
     head = dense_case(stack, 1, 1, Hq, Hkv, D, [L0], args.steps, args.warmup)
     log(f"headline: {head['us']:.2f} us/layer-step, {head['kv_gbs']:.0f} GB/s on KV bytes")
+
+    if args.calibrate_copy:
+        calibrate_copy()
 
     sweep = {}
     if not args.headline_only:
@@ -256,6 +291,9 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(args.cpu_seconds)
 
+    workload = (f"decode layer B=1 n_q=1 Hq={Hq} Hkv={Hkv} D={D} cap={cap} kv_len={L0}, "
+                f"{head['layers']} layer caches per step (cold)")
+    traffic = measured_traffic(f"B=1 n_q=1 Hq={Hq} Hkv={Hkv} D={D} cap={cap} kv_len={L0}")
     line = {
         "metric": METRIC,
         "value": round(head["us"], 3),
@@ -269,15 +307,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"decode layer B=1 n_q=1 Hq={Hq} Hkv={Hkv} D={D} cap={cap} "
-                               f"kv_len={L0}, {head['layers']} layer caches per step (cold)",
+        "config": {"workload": workload,
                    "B": 1, "n_q": 1, "Hq": Hq, "Hkv": Hkv, "D": D, "cap": cap, "kv_len": L0,
                    "layers_per_step": head["layers"], "parallelism": "none"},
         "hbm_gbs_kv": round(head["kv_gbs"], 1),
         "frac_of_peak_kv": round(head["frac_kv"], 4),
         "roofline": {"bound": "hbm", "achieved": round(head["algo_gbs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(head["algo_gbs"] / PEAK_HBM_GBS, 4),
-                     "traffic": None, "kernel": "decode_kernel<256,1,0>",
+                     "traffic": traffic, "kernel": "decode_kernel<256,1,0>",
                      "algo_bytes_per_launch": head["algo_bytes"]},
         "cpu_baseline": cpu,
         "sweep": sweep,
