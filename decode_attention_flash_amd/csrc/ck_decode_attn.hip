@@ -13,11 +13,14 @@
 // finishes a unit's last split merges the splits in the same launch (same
 // comfy-kitchen PR, GQA decode), so the launch has a fixed shape.
 //
-// Per wave and tile (TT tokens, TT*D*2 = 16 KiB of K):
-//   K   : buffer loads straight into MFMA A-operand registers (lane l holds
-//         token l%16 of a 16-token block, 8 consecutive head-dim values);
-//         rows past the split or the visible limit come back as zeros from
-//         the buffer range check, so garbage is never read.
+// Per wave and tile (TT tokens, TT*D*2 = 16 KiB of K and as much of V):
+//   K,V : row-major buffer loads (each instruction reads whole cache rows,
+//         which streams faster than the 16-row x 64-byte pattern of an MFMA
+//         operand), staged in LDS; rows past the split or the visible limit
+//         come back as zeros from the buffer range check, so garbage is never
+//         read.  The next tile's loads go out as soon as this one is staged.
+//   K   : read back from LDS as the MFMA A operand (lane l holds token l%16
+//         of a 16-token block, 8 consecutive head-dim values).
 //   S^T = K Q^T on MFMA, C layout: lane l holds query row l%16 and tokens
 //         4*(l/16)+0..3 of each 16-token block.
 //   softmax on those registers; P^T for PV is the same registers rounded to
@@ -65,6 +68,11 @@ struct Geo {
     // a 16-lane group reads in one transposed load on disjoint bank ranges.
     static constexpr int RS = 2 * D + 32;
     static constexpr int VBYTES = TT * RS;  // LDS bytes per wave for staged V
+    // LDS row stride of the staged K tile: 16 bytes of skew puts the 16 rows
+    // that one A-operand read touches (same columns) on disjoint banks.
+    static constexpr int RSK = 2 * D + 16;
+    static constexpr int KBYTES = TT * RSK;
+    static constexpr int STAGE = KBYTES + VBYTES;  // LDS bytes per wave
 };
 
 struct KParams {
@@ -298,10 +306,10 @@ template <int D, int RT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     using Gm = Geo<D>;
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
-    constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS;
+    constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS, RSK = Gm::RSK;
     constexpr bool GATHER = (MODE == 2);
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::VBYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * Gm::STAGE];
     __shared__ float s_ml[kWaves][RT][64][2];
     __shared__ bf16x8 q_lds[RT * KS * 64];
     __shared__ MergeScratch ms;
@@ -413,7 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         for (int n = 0; n < NB; ++n) st.o[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    unsigned char* vlds = smem + wave * Gm::VBYTES;
+    unsigned char* klds = smem + wave * Gm::STAGE;
+    unsigned char* vlds = klds + Gm::KBYTES;
     const int ntiles = (pos_end - pos_begin + TT - 1) / TT;
     // Whether every split of the unit has started: thread 0 reads the count
     // after its first tile's data has arrived, so the round trip hides under
@@ -427,35 +436,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         return (tile < ntiles && lane < TT && pe < pos_end) ? list[pe] : -1;
     };
 
-    // Issue the K and V loads (and mask loads) of one tile.
-    bf16x8 kreg[MB][KS];
-    u32x4 vreg[VI];
+    // Issue the K and V loads (and mask loads) of one tile.  Load n of a lane
+    // reads 16 bytes of cache row n*RPI + lane/CPR, so one instruction covers
+    // RPI whole rows.
+    u32x4 kraw[VI], vraw[VI];
     uint32_t mbits[RT][MB];
     uint64_t gvalid = 0;
     auto issue = [&](int tile, int jv) {
         const int tb = pos_begin + tile * TT;
-        uint32_t koff[MB], voff[VI];
+        uint32_t roff[VI];
         if constexpr (GATHER) {
             const bool ok = jv >= 0 && jv < lim_g;
             const uint32_t off = ok ? (uint32_t)jv * p.row_bytes : kOOB;
             gvalid = __ballot(ok);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) koff[mb] = __shfl(off, 16 * mb + l16);
-#pragma unroll
-            for (int n = 0; n < VI; ++n) voff[n] = __shfl(off, n * RPI + lane / CPR);
+            for (int n = 0; n < VI; ++n) roff[n] = __shfl(off, n * RPI + lane / CPR);
         } else {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) koff[mb] = (uint32_t)(tb + 16 * mb + l16) * p.row_bytes;
-#pragma unroll
-            for (int n = 0; n < VI; ++n) voff[n] = (uint32_t)(tb + n * RPI + lane / CPR) * p.row_bytes;
+            for (int n = 0; n < VI; ++n) roff[n] = (uint32_t)(tb + n * RPI + lane / CPR) * p.row_bytes;
         }
+        const uint32_t coff = (uint32_t)(lane % CPR) * 16u;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rk, roff[n] + coff);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kreg[mb][ks] = __builtin_bit_cast(bf16x8, bload128<2>(rk, koff[mb] + (uint32_t)(32 * ks + 8 * q4) * 2u));
-#pragma unroll
-        for (int n = 0; n < VI; ++n) vreg[n] = bload128<2>(rv, voff[n] + (uint32_t)(lane % CPR) * 16u);
+        for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rv, roff[n] + coff);
         if constexpr (MODE == 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -499,31 +503,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 for (int mb = 0; mb < MB; ++mb) tmbits[rt][mb] = mbits[rt][mb];
         }
 
-        // -- stage V rows in LDS ------------------------------------------
+        // -- stage K and V rows in LDS, then send the next tile's loads -----
 #pragma unroll
         for (int n = 0; n < VI; ++n)
-            *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vreg[n];
+            *reinterpret_cast<u32x4*>(klds + (n * RPI + lane / CPR) * RSK + (lane % CPR) * 16) = kraw[n];
+#pragma unroll
+        for (int n = 0; n < VI; ++n)
+            *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vraw[n];
+        wave_lds_sync();
+        // The next tile's loads go out now, or after QK^T where the registers
+        // of two row tiles at D = 256 would not hold them during it.
+        constexpr bool kEarly = !(D == 256 && RT == 2);
+        const int next = tile + kWaves;
+        if (kEarly && next < ntiles) {
+            issue(next, jv_next);
+            if constexpr (GATHER) jv_next = list_entry(next + kWaves);
+        }
 
         // -- S^T = K Q^T ---------------------------------------------------
         f32x4 sc[RT][MB];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            for (int mb = 0; mb < MB; ++mb) sc[rt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) a = mfma(kreg[mb][ks], q_lds[(rt * KS + ks) * 64 + lane], a);
-                sc[rt][mb] = a;
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(klds + (16 * mb + l16) * RSK + 64 * ks + 16 * q4);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) sc[rt][mb] = mfma(ka, q_lds[(rt * KS + ks) * 64 + lane], sc[rt][mb]);
             }
 
-        if (tid == 0 && tile == 0 && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
-
-        // -- next tile's loads go out while this one finishes ---------------
-        const int next = tile + kWaves;
-        if (next < ntiles) {
+        if (!kEarly && next < ntiles) {
             issue(next, jv_next);
             if constexpr (GATHER) jv_next = list_entry(next + kWaves);
         }
+        if (tid == 0 && tile == 0 && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
 
         // -- online softmax (log2 domain) -----------------------------------
         bf16x8 pb[RT][KB];
@@ -609,8 +625,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     // unit has a single split, else this split's partial (unnormalised acc,
     // m, l) with device-coherent stores.  Row tiles are dumped in rounds when
     // all of them do not fit in LDS at once.
-    constexpr int RT_ROUND = (kWaves * RT * NB * 64 * 16 <= kWaves * Gm::VBYTES) ? RT : 1;
-    static_assert(kWaves * RT_ROUND * NB * 64 * 16 <= kWaves * Gm::VBYTES, "merge area exceeds LDS");
+    constexpr int RT_ROUND = (kWaves * RT * NB * 64 * 16 <= kWaves * Gm::STAGE) ? RT : 1;
+    static_assert(kWaves * RT_ROUND * NB * 64 * 16 <= kWaves * Gm::STAGE, "merge area exceeds LDS");
     f32x4* dump = reinterpret_cast<f32x4*>(smem);
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
@@ -622,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     }
 #pragma unroll
     for (int rt0 = 0; rt0 < RT; rt0 += RT_ROUND) {
-        __syncthreads();  // the V staging area (or the previous round) is free
+        __syncthreads();  // the staging area (or the previous round) is free
 #pragma unroll
         for (int rl = 0; rl < RT_ROUND; ++rl)
 #pragma unroll
