@@ -39,7 +39,8 @@ class Shape(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("units", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("split_target", ctypes.c_int32), ("chunk_max", ctypes.c_int32),
+                ("split_target", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
+                ("chunk_max", ctypes.c_int32),
                 ("granule", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("row_groups", ctypes.c_int32), ("rows_per_group", ctypes.c_int32),
                 ("slices", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]

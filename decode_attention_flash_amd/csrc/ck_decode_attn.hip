@@ -52,7 +52,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // arrived and finished counters on separate cache lines, then one claim flag
 // per merge slice.
 constexpr int kCntStride = 256, kStarted = 0, kArrived = 32, kFinished = 64, kSliceFlag = 96;
-constexpr int kMaxSlices = 64;
+constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
+static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 
 template <int D>
 struct Geo {
@@ -91,7 +92,7 @@ struct KParams {
     int32_t R, RG, rows_alloc;
     int32_t units;   // work units (grid = splits x units)
     int32_t splits;  // grid splits per unit
-    int32_t S_target, c_max, gran;
+    int32_t S_target, c_min, c_max, gran;
     int32_t slices;  // column slices of the merge
     int32_t W;
     int64_t idx_head_stride;  // 0: one list per query shared by its heads
@@ -177,7 +178,7 @@ __device__ __forceinline__ void atomic_st(int32_t* p, int v) {
 __device__ __forceinline__ int chunk_len(int span, const KParams& p) {
     int c = (span + p.S_target - 1) / p.S_target;
     c = (c + p.gran - 1) / p.gran * p.gran;
-    if (c < p.gran) c = p.gran;
+    if (c < p.c_min) c = p.c_min;
     if (p.c_max > 0 && c > p.c_max) c = p.c_max;
     int need = (span + p.splits - 1) / p.splits;
     need = (need + p.gran - 1) / p.gran * p.gran;
@@ -224,7 +225,7 @@ __device__ __forceinline__ void store4(const KParams& p, size_t row, int d, f32x
 
 struct MergeScratch {
     int flag;
-    int owned[kMaxSlices];
+    uint64_t owned;  // slices the unit's last split claimed (bit c = slice c)
 };
 
 // Merge column slice `c` of `ns` for one unit from the n_active published
@@ -232,8 +233,9 @@ struct MergeScratch {
 // w_s = 2^(m_s - max m).  Each output group (row, 4 columns) is taken by TPP
 // neighbouring lanes; a lane folds its strided subset of the splits into a
 // running (max, denominator, accumulator) with the online-softmax rule, and
-// the TPP lane states are then folded together by shuffles.  All loads of a
-// lane are issued before the first use, so the merge costs one round trip.
+// the TPP lane states are then folded together by shuffles.  TPP is large
+// enough that a lane has at most PRE splits, whose loads are all issued
+// before the first use, so each pass over the outputs costs one round trip.
 __device__ __forceinline__ void fold(float& M, float& den, f32x4& acc, float m2, float l2, f32x4 a2) {
     float w1, w2, m;
     merge_scale(M, m2, w1, w2, m);
@@ -246,13 +248,14 @@ template <int D>
 __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows, int c, int ns, int b, int g,
                             int iq, bool gather, int row0) {
     constexpr int D4 = D / 4;
-    constexpr int PRE = 8;
+    constexpr int PRE = 16;
     const int tid = threadIdx.x;
     const int col_lo = c * D4 / ns, col_hi = (c + 1) * D4 / ns;
     const int ncol = col_hi - col_lo;
     const int P = nrows * ncol;
     int TPP = 1;
     while (TPP < 64 && 2 * TPP * P <= kThreads) TPP *= 2;
+    while (TPP < 64 && TPP * PRE < n_active) TPP *= 2;
     const int per_pass = kThreads / TPP;
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
@@ -265,23 +268,21 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
         const int rr = act ? pos / ncol : 0;
         const int col = act ? col_lo + pos % ncol : 0;
         const uint32_t xoff = (uint32_t)(rr * D + 4 * col) * 4u;
-        const uint32_t moff = (uint32_t)rr * 8u;
+        const uint32_t moff = (uint32_t)(rr * p.splits) * 8u;
         float M = -INFINITY, den = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        f32x4 x[PRE];
-        f32x2 ml[PRE];
+        for (int s0 = j; s0 < n_active; s0 += PRE * TPP) {
+            f32x4 x[PRE];
+            f32x2 ml[PRE];
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            const int s2 = j + u * TPP;
-            const bool ok = act && s2 < n_active;
-            x[u] = ok ? load_dev4(ro, xoff + (uint32_t)s2 * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-            ml[u] = ok ? load_dev2(rml, moff + (uint32_t)(s2 * p.rows_alloc) * 8u) : f32x2{-INFINITY, 0.f};
-        }
+            for (int u = 0; u < PRE; ++u) {
+                const int s2 = s0 + u * TPP;
+                const bool ok = act && s2 < n_active;
+                x[u] = ok ? load_dev4(ro, xoff + (uint32_t)s2 * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+                ml[u] = ok ? load_dev2(rml, moff + (uint32_t)s2 * 8u) : f32x2{-INFINITY, 0.f};
+            }
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) fold(M, den, acc, ml[u][0], ml[u][1], x[u]);
-        for (int s2 = j + PRE * TPP; act && s2 < n_active; s2 += TPP) {
-            const f32x2 m2 = load_dev2(rml, moff + (uint32_t)(s2 * p.rows_alloc) * 8u);
-            fold(M, den, acc, m2[0], m2[1], load_dev4(ro, xoff + (uint32_t)s2 * sstride));
+            for (int u = 0; u < PRE; ++u) fold(M, den, acc, ml[u][0], ml[u][1], x[u]);
         }
         for (int off = TPP / 2; off >= 1; off /= 2) {
             const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(den, off);
@@ -642,7 +643,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 #pragma unroll
         for (int rl = 0; rl < RT_ROUND; ++rl)
 #pragma unroll
-            for (int n = 0; n < NB; ++n) dump[((wave * RT_ROUND + rl) * NB + n) * 64 + lane] = st.o[rt0 + rl][n];
+            for (int n = 0; n < NB; ++n)
+                dump[((wave * RT_ROUND + rl) * NB + n) * 64 + q4 * 16 + (l16 ^ ((4 * n + q4) & 15))] = st.o[rt0 + rl][n];
         __syncthreads();
         constexpr int D4 = D / 4;
         const int rows_here = min(nrows - rt0 * 16, RT_ROUND * 16);
@@ -650,7 +652,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
             const int rl16 = k / D4, d4 = k % D4;
             const int rl = rl16 >> 4, r16 = rl16 & 15;
             const int rr = rt0 * 16 + rl16;
-            const int src = (d4 & 3) * 16 + r16;  // lane holding (row, 4 columns)
+            // Slot of (row, 4 columns): the lane that held it, with the row index
+            // XOR-swizzled by the column group so that threads reading
+            // consecutive column groups of one row hit distinct banks.
+            const int src = (d4 & 3) * 16 + (r16 ^ (d4 & 15));
             float mw[kWaves], M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
@@ -674,7 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
             } else {
                 const uint32_t prow = (uint32_t)(s * p.rows_alloc + rr);
                 store_dev<f32x4>(ro, (prow * D + 4 * d4) * 4u, a);
-                if (d4 == 0) store_dev<f32x2>(rml, prow * 8u, f32x2{M, den});
+                if (d4 == 0) store_dev<f32x2>(rml, (uint32_t)(rr * p.splits + s) * 8u, f32x2{M, den});
             }
         }
     }
@@ -705,10 +710,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     __syncthreads();  // everyone has read ms.flag
     if (last) {
         merge_slice<D>(p, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
-        if (tid >= 1 && tid < ns) ms.owned[tid] = atomicExch(cnt + kSliceFlag + tid, 1) == 0;
+        // ns <= 64: lane c of wave 0 claims slice c, one ballot collects them.
+        if (wave == 0) {
+            const bool own = lane >= 1 && lane < ns && atomicExch(cnt + kSliceFlag + lane, 1) == 0;
+            const uint64_t mask = __ballot(own);
+            if (lane == 0) ms.owned = mask;
+        }
         __syncthreads();
-        for (int c = 1; c < ns; ++c)
-            if (ms.owned[c]) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+        for (uint64_t mask = ms.owned; mask != 0; mask &= mask - 1)
+            merge_slice<D>(p, unit, n_active, nrows, __builtin_ctzll(mask), ns, b, g, iq, GATHER, row0);
     } else {
         const int c = n_active - 1 - rank;
         if (tid == 0) {
@@ -751,6 +761,10 @@ static int tile_tokens(int D) { return D == 256 ? 32 : 64; }
 // CUs; each split then streams enough to amortise its fixed costs.
 constexpr int64_t kChunkMaxBytes = 2 << 20;
 static int chunk_max_tokens(int D) { return (int)(kChunkMaxBytes / (4 * D)); }
+// A split publishes rows*D fp32 partials that are written and read back once,
+// against 4*D bytes of K+V per token it streams: at least 5 tokens per packed
+// row keeps that round trip under 40 % of the split's cache traffic.
+constexpr int kTokensPerRow = 5;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -774,10 +788,12 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     const int64_t RG = (R + rows_per_group - 1) / rows_per_group;
     const int64_t units = (W > 0 ? (int64_t)s->B * s->n_q : (int64_t)s->B) * s->Hkv * RG;
     const int64_t span_max = W > 0 ? W : s->cap;
-    int64_t target, cmax;
+    const int64_t rows_eff = R < rows_per_group ? R : rows_per_group;
+    int64_t target, cmax, cmin = TT;
     if (num_splits == 0) {
         target = ((int64_t)num_cus * kWgPerCu + units - 1) / units;
         cmax = 2 * units >= num_cus ? chunk_max_tokens(s->D) : 0;
+        cmin = (kTokensPerRow * rows_eff + TT - 1) / TT * TT;
     } else {
         target = num_splits;
         cmax = 0;
@@ -789,7 +805,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
         const int64_t need = (span_max + cmax - 1) / cmax;
         if (need > splits) splits = need;
     }
-    const int64_t most = (span_max + TT - 1) / TT;
+    const int64_t most = (span_max + cmin - 1) / cmin;
     if (splits > most) splits = most;
     if (splits > CK_MAX_SPLITS) splits = CK_MAX_SPLITS;
     if (splits < 1) splits = 1;
@@ -798,6 +814,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     pl->units = (int32_t)units;
     pl->splits = (int32_t)splits;
     pl->split_target = (int32_t)target;
+    pl->chunk_min = (int32_t)cmin;
     pl->chunk_max = (int32_t)cmax;
     pl->granule = TT;
     pl->rows = (int32_t)R;
@@ -805,10 +822,9 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     pl->rows_per_group = rows_per_group;
     // Column slices of the merge: about 16 KiB of partials each, at most one
     // per 4 columns.
-    const int64_t rows_eff = R < rows_per_group ? R : rows_per_group;
     const int64_t merge_bytes = splits * rows_eff * s->D * 4;
     int64_t slices = 1;
-    while (slices * 16384 < merge_bytes && slices < s->D / 4 && slices < 64) slices *= 2;
+    while (slices * 16384 < merge_bytes && slices < s->D / 4 && slices < kMaxSlices) slices *= 2;
     pl->slices = (int32_t)slices;
     if (splits == 1) {
         pl->workspace_bytes = 0;
@@ -912,6 +928,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.units = pl.units;
     kp.splits = pl.splits;
     kp.S_target = pl.split_target;
+    kp.c_min = pl.chunk_min;
     kp.c_max = pl.chunk_max;
     kp.gran = pl.granule;
     kp.slices = pl.slices;

@@ -104,6 +104,7 @@ typedef struct ck_decode_plan {
     int32_t units;
     int32_t splits;          /* grid splits per unit                         */
     int32_t split_target;    /* splits aimed for when the range is long      */
+    int32_t chunk_min;       /* shortest range one split takes               */
     int32_t chunk_max;       /* longest range one split takes (0: no limit)  */
     int32_t granule;         /* split ranges are multiples of this           */
     int32_t rows;            /* query rows per unit                          */

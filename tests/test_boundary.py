@@ -64,6 +64,16 @@ def test_plan_batched_uses_chunk_limit():
     assert p["chunk_max"] == 4096 and p["splits"] == 8
 
 
+def test_plan_minimum_range_grows_with_rows():
+    # at least 5 tokens per packed row, in whole tiles
+    assert ck.plan(shape(), num_cus=256)["chunk_min"] == 32
+    assert ck.plan(shape(n_q=3), num_cus=256)["chunk_min"] == 64
+    assert ck.plan(shape(n_q=6), num_cus=256)["chunk_min"] == 128
+    assert ck.plan(shape(B=32, Hq=32, Hkv=8, D=128, cap=32768), num_cus=256)["chunk_min"] == 64
+    # a forced split count is used as given
+    assert ck.plan(shape(n_q=6), num_splits=64, num_cus=256)["chunk_min"] == 32
+
+
 def test_plan_causal_window_row_groups():
     p = ck.plan(shape(n_q=6), num_cus=256)
     assert p["rows"] == 24 and p["rows_per_group"] == 32 and p["row_groups"] == 1
