@@ -52,6 +52,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // arrived and finished counters on separate cache lines, then one claim flag
 // per merge slice.
 constexpr int kCntStride = 256, kStarted = 0, kArrived = 32, kFinished = 64, kSliceFlag = 96;
+constexpr int kSpinLimit = 1 << 22;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 
@@ -98,6 +99,7 @@ struct KParams {
     int64_t idx_head_stride;  // 0: one list per query shared by its heads
     float scale_log2;         // softmax scale times log2(e)
     int32_t causal, out_bf16;
+    int32_t mask_dw;     // keep_mask rows start 4-byte aligned: read 4 cells per load
     uint32_t row_bytes;  // bytes between consecutive positions of one head
 };
 
@@ -228,22 +230,37 @@ struct MergeScratch {
     uint64_t owned;  // slices the unit's last split claimed (bit c = slice c)
 };
 
+// All-reduce over aligned groups of `span` neighbouring lanes (a power of two
+// up to 64, the same in the whole wave; every lane must be active).  Steps
+// inside a 16-lane row are DPP lane moves: swap neighbours, swap pairs, then
+// the half-row and row mirrors, each of which pairs a lane with one of the
+// other half of its group.  Wider steps go through the cross-lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <bool MAX>
+__device__ __forceinline__ float group_reduce(float v, int span) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if (span >= 2) v = op(v, dpp<kDppXor1>(v));
+    if (span >= 4) v = op(v, dpp<kDppXor2>(v));
+    if (span >= 8) v = op(v, dpp<kDppHalfMirror>(v));
+    if (span >= 16) v = op(v, dpp<kDppMirror>(v));
+    if (span >= 32) v = op(v, __shfl_xor(v, 16));
+    if (span >= 64) v = op(v, __shfl_xor(v, 32));
+    return v;
+}
+
 // Merge column slice `c` of `ns` for one unit from the n_active published
 // partials (acc_s, m_s, l_s):  O = sum_s w_s acc_s / sum_s w_s l_s with
 // w_s = 2^(m_s - max m).  Each output group (row, 4 columns) is taken by TPP
-// neighbouring lanes; a lane folds its strided subset of the splits into a
-// running (max, denominator, accumulator) with the online-softmax rule, and
-// the TPP lane states are then folded together by shuffles.  TPP is large
-// enough that a lane has at most PRE splits, whose loads are all issued
-// before the first use, so each pass over the outputs costs one round trip.
-__device__ __forceinline__ void fold(float& M, float& den, f32x4& acc, float m2, float l2, f32x4 a2) {
-    float w1, w2, m;
-    merge_scale(M, m2, w1, w2, m);
-    M = m;
-    den = w1 * den + w2 * l2;
-    acc = w1 * acc + w2 * a2;
-}
-
+// neighbouring lanes, each lane by a strided subset of at most PRE splits
+// whose loads are all issued before the first use, so a pass over the
+// outputs costs one round trip.  A lane takes the max of its m_s, then sums
+// its weighted terms (independent exponentials, no serial chain); the TPP
+// lanes then agree on the max, rescale once and sum.  The order is fixed, so
+// the result does not depend on which workgroup merges or when.
 template <int D>
 __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows, int c, int ns, int b, int g,
                             int iq, bool gather, int row0) {
@@ -255,6 +272,7 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
     const int P = nrows * ncol;
     int TPP = 1;
     while (TPP < 64 && 2 * TPP * P <= kThreads) TPP *= 2;
+    static_assert(CK_MAX_SPLITS <= 64 * PRE, "a lane holds at most PRE splits");
     while (TPP < 64 && TPP * PRE < n_active) TPP *= 2;
     const int per_pass = kThreads / TPP;
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
@@ -269,35 +287,40 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
         const int col = act ? col_lo + pos % ncol : 0;
         const uint32_t xoff = (uint32_t)(rr * D + 4 * col) * 4u;
         const uint32_t moff = (uint32_t)(rr * p.splits) * 8u;
-        float M = -INFINITY, den = 0.f;
+        f32x4 x[PRE];
+        f32x2 ml[PRE];
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const int s2 = j + u * TPP;
+            const bool ok = act && s2 < n_active;
+            x[u] = ok ? load_dev4(ro, xoff + (uint32_t)s2 * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+            ml[u] = ok ? load_dev2(rml, moff + (uint32_t)s2 * 8u) : f32x2{-INFINITY, 0.f};
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) M = fmaxf(M, ml[u][0]);
+        float den = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = j; s0 < n_active; s0 += PRE * TPP) {
-            f32x4 x[PRE];
-            f32x2 ml[PRE];
+        {
+            const float mu = (M == -INFINITY) ? 0.f : M;
 #pragma unroll
             for (int u = 0; u < PRE; ++u) {
-                const int s2 = s0 + u * TPP;
-                const bool ok = act && s2 < n_active;
-                x[u] = ok ? load_dev4(ro, xoff + (uint32_t)s2 * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-                ml[u] = ok ? load_dev2(rml, moff + (uint32_t)s2 * 8u) : f32x2{-INFINITY, 0.f};
+                const float w = fast_exp2(ml[u][0] - mu);
+                den += w * ml[u][1];
+                acc += w * x[u];
             }
+        }
+        const float Mg = group_reduce<true>(M, TPP);
+        const float mu = (Mg == -INFINITY) ? 0.f : Mg;
+        const float r = fast_exp2(M - mu);
+        den = group_reduce<false>(den * r, TPP);
 #pragma unroll
-            for (int u = 0; u < PRE; ++u) fold(M, den, acc, ml[u][0], ml[u][1], x[u]);
-        }
-        for (int off = TPP / 2; off >= 1; off /= 2) {
-            const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(den, off);
-            f32x4 a2;
-            a2[0] = __shfl_xor(acc[0], off);
-            a2[1] = __shfl_xor(acc[1], off);
-            a2[2] = __shfl_xor(acc[2], off);
-            a2[3] = __shfl_xor(acc[3], off);
-            fold(M, den, acc, m2, l2, a2);
-        }
+        for (int k = 0; k < 4; ++k) acc[k] = group_reduce<false>(acc[k] * r, TPP);
         if (act && j == 0) {
             const float inv = den > 0.f ? 1.f / den : 0.f;
             const size_t orow = out_row(p, b, g, row0 + rr, iq, gather);
             store4<D>(p, orow, 4 * col, acc * inv);
-            if (col == 0 && p.lse != nullptr) p.lse[orow] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+            if (col == 0 && p.lse != nullptr) p.lse[orow] = den > 0.f ? (Mg + __log2f(den)) * kLn2 : -INFINITY;
         }
     }
 }
@@ -471,9 +494,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                                                    (uint32_t)(tb + 16 * mb + 4 * q4)
                                              : kOOB;
                     uint32_t bits = 0;
+                    if (p.mask_dw) {  // the four bytes form one aligned dword
+                        const uint32_t w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, off, 0, 0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        bits |= (uint32_t)(__builtin_amdgcn_raw_buffer_load_b8(rm, off + e, 0, 0) != 0) << e;
+                        for (int e = 0; e < 4; ++e) bits |= (uint32_t)(((w >> (8 * e)) & 0xFFu) != 0u) << e;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bits |= (uint32_t)(__builtin_amdgcn_raw_buffer_load_b8(rm, off + e, 0, 0) != 0) << e;
+                    }
                     mbits[rt][mb] = bits;
                 }
         }
@@ -728,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 int spins = 0;
                 while (atomic_ld(cnt + kArrived) < n_active) {
                     __builtin_amdgcn_s_sleep(2);
-                    if (++spins > (1 << 22)) {  // cannot happen while every split runs
+                    if (++spins > kSpinLimit) {  // cannot happen while every split runs
                         ok = 0;
                         break;
                     }
@@ -820,11 +849,11 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     pl->rows = (int32_t)R;
     pl->row_groups = (int32_t)RG;
     pl->rows_per_group = rows_per_group;
-    // Column slices of the merge: about 16 KiB of partials each, at most one
+    // Column slices of the merge: about 32 KiB of partials each, at most one
     // per 4 columns.
     const int64_t merge_bytes = splits * rows_eff * s->D * 4;
     int64_t slices = 1;
-    while (slices * 16384 < merge_bytes && slices < s->D / 4 && slices < kMaxSlices) slices *= 2;
+    while (slices * 32768 < merge_bytes && slices < s->D / 4 && slices < kMaxSlices) slices *= 2;
     pl->slices = (int32_t)slices;
     if (splits == 1) {
         pl->workspace_bytes = 0;
@@ -937,6 +966,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     kp.causal = causal ? 1 : 0;
     kp.out_bf16 = out_dtype == CK_DT_BF16 ? 1 : 0;
+    kp.mask_dw = keep_mask != nullptr && aligned(keep_mask, 4) && s->cap % 4 == 0 ? 1 : 0;
     kp.row_bytes = (uint32_t)(s->Hkv * s->D * 2);
 
     const int RT = pl.rows_per_group / 16;

@@ -173,6 +173,30 @@ def test_masked_scan_matches_oracle_and_gather(sparse_case):
     assert np.max(np.abs(gathered[1] - masked[1])) <= 4e-3
 
 
+@pytest.mark.parametrize("cap,offset", [(1024, 0), (1023, 0), (1024, 1)])
+def test_masked_scan_mask_layouts(cap, offset):
+    """keep_mask read four cells per load (rows 4-byte aligned) and one per
+    load (odd capacity, or a mask pointer off by one byte); any nonzero byte
+    keeps its cell.  Causal window, two sequences of different length."""
+    B, n_q, Hq, Hkv, D = 2, 3, 8, 2, 128
+    lens = [cap - 5, 517]
+    note(f"masked scan layout cap={cap} offset={offset}")
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 1021 + cap)
+    q = synth.queries(B, n_q, Hq, D, 1022)
+    rng = np.random.default_rng(1023 + cap + offset)
+    mask = (rng.random((B, n_q, Hkv, cap)) < 0.3) * rng.integers(1, 256, (B, n_q, Hkv, cap))
+    mask = mask.astype(np.uint8)
+    buf = torch.zeros(mask.size + offset, dtype=torch.uint8, device=DEV)
+    mask_d = buf[offset:].view(B, n_q, Hkv, cap)
+    mask_d.copy_(torch.from_numpy(mask).to(DEV))
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out, lse = ck.decode_attn(q.to(DEV), k.to(DEV), v.to(DEV), lens_d, causal=True, keep_mask=mask_d,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    gpu = (out.cpu().numpy(), lse.cpu().numpy())
+    assert_close(gpu, oracle_ref(q, k, v, lens, causal=True, keep_mask=mask), what=f"mask cap={cap}")
+
+
 def test_gather_lists_edge_entries():
     """Invalid entries (< 0, >= limit, >= capacity), duplicates, shared
     lists, per-query lists under a causal window, ragged list length."""
