@@ -202,6 +202,14 @@ __device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float
     w2 = fast_exp2(m2 - mu);
 }
 
+// Bit e set where byte e of w is nonzero (4 keep_mask cells).
+__device__ __forceinline__ uint32_t mask_bits(uint32_t w) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bits |= (uint32_t)(((w >> (8 * e)) & 0xFFu) != 0u) << e;
+    return bits;
+}
+
 // Flat (b, i, h) index of packed row r of a unit.
 __device__ __forceinline__ size_t out_row(const KParams& p, int b, int g, int r, int iq, bool gather) {
     int i = gather ? iq : r / p.G;
@@ -464,7 +472,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     // reads 16 bytes of cache row n*RPI + lane/CPR, so one instruction covers
     // RPI whole rows.
     u32x4 kraw[VI], vraw[VI];
-    uint32_t mbits[RT][MB];
+    uint32_t mraw[RT][MB];
+    constexpr bool kDeferMask = !(D == 256 && RT == 2);
     uint64_t gvalid = 0;
     auto issue = [&](int tile, int jv) {
         const int tb = pos_begin + tile * TT;
@@ -479,11 +488,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 #pragma unroll
             for (int n = 0; n < VI; ++n) roff[n] = (uint32_t)(tb + n * RPI + lane / CPR) * p.row_bytes;
         }
-        const uint32_t coff = (uint32_t)(lane % CPR) * 16u;
-#pragma unroll
-        for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rk, roff[n] + coff);
-#pragma unroll
-        for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rv, roff[n] + coff);
+        // Mask cells of the lane's 4 tokens per 16-token block.  An aligned
+        // dword stays raw until the tile is consumed, so the issue does not
+        // wait for it (except with two row tiles at D = 256, where the
+        // registers are short); single bytes (unaligned rows) are reduced to
+        // bits here.
         if constexpr (MODE == 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -493,19 +502,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                                              ? (uint32_t)(i_r[rt] * p.Hkv + g) * (uint32_t)p.cap +
                                                    (uint32_t)(tb + 16 * mb + 4 * q4)
                                              : kOOB;
-                    uint32_t bits = 0;
                     if (p.mask_dw) {  // the four bytes form one aligned dword
                         const uint32_t w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, off, 0, 0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) bits |= (uint32_t)(((w >> (8 * e)) & 0xFFu) != 0u) << e;
+                        mraw[rt][mb] = kDeferMask ? w : mask_bits(w);
                     } else {
+                        uint32_t bits = 0;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             bits |= (uint32_t)(__builtin_amdgcn_raw_buffer_load_b8(rm, off + e, 0, 0) != 0) << e;
+                        mraw[rt][mb] = bits;
                     }
-                    mbits[rt][mb] = bits;
                 }
         }
+        const uint32_t coff = (uint32_t)(lane % CPR) * 16u;
+#pragma unroll
+        for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rk, roff[n] + coff);
+#pragma unroll
+        for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rv, roff[n] + coff);
     };
 
     // Query fragments to LDS before the first tile's loads are issued (they
@@ -525,12 +538,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     for (int tile = wave; tile < ntiles; tile += kWaves) {
         const int tb = pos_begin + tile * TT;
         const uint64_t tvalid = gvalid;
-        uint32_t tmbits[RT][MB];
+        uint32_t tmbits[RT][MB];  // keep bit e: token 16mb + 4q4 + e
         if constexpr (MODE == 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) tmbits[rt][mb] = mbits[rt][mb];
+                for (int mb = 0; mb < MB; ++mb) {
+                    tmbits[rt][mb] = (kDeferMask && p.mask_dw) ? mask_bits(mraw[rt][mb]) : mraw[rt][mb];
+                }
         }
 
         // -- stage K and V rows in LDS, then send the next tile's loads -----
