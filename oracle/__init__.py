@@ -49,6 +49,12 @@ def load(path: str | None = None):
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
     ]
+    lib.ck_oracle_attn_steps.restype = ctypes.c_int
+    lib.ck_oracle_attn_steps.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
     lib.ck_oracle_nthreads_default.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -128,6 +134,35 @@ def attn(q, k_cache, v_cache, kv_lens, scale: float, causal: bool = False, keep_
     st = lib.ck_oracle_attn(B, n_q, Hq, Hkv, D, cap, ptr(qb), ptr(kb), ptr(vb), ptr(lens),
                             ctypes.c_float(scale), 1 if causal else 0, ptr(mask_arr),
                             ptr(idx_arr), W, hs, num_splits, ptr(out), ptr(lse), nthreads)
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return out, lse
+
+
+def attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, scale: float, num_splits: int = 0,
+               nthreads: int = 0, lib=None):
+    """Attention of n_q verification queries over the cache prefix [0, L)
+    plus their own step rows: query i sees step rows 0..i of
+    k_step / v_step [B, n_q, Hkv, D] (not written into the cache).
+    Returns (out [B, n_q, Hq, D] float64, lse [B, n_q, Hq] float64)."""
+    lib = lib or load()
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    ksb, vsb = _bits(k_step), _bits(v_step)
+    B, n_q, Hq, D = qb.shape
+    Bk, cap, Hkv, Dk = kb.shape
+    if vb.shape != kb.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k_cache and v_cache")
+    if ksb.shape != (B, n_q, Hkv, D) or vsb.shape != ksb.shape:
+        raise ValueError("k_step / v_step must be [B, n_q, Hkv, D]")
+    lens = _np(kv_lens, np.int32).reshape(-1)
+    if lens.shape[0] != B:
+        raise ValueError("kv_lens must have B entries")
+    out = np.empty((B, n_q, Hq, D), dtype=np.float64)
+    lse = np.empty((B, n_q, Hq), dtype=np.float64)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.ck_oracle_attn_steps(B, n_q, Hq, Hkv, D, cap, ptr(qb), ptr(kb), ptr(vb), ptr(lens),
+                                  ptr(ksb), ptr(vsb), ctypes.c_float(scale), num_splits, ptr(out),
+                                  ptr(lse), nthreads)
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
     return out, lse

@@ -32,6 +32,15 @@
  *             are gathered into a window of their own and the mask is taken
  *             at those cells; llama.cpp PR "qwen4exp : gather-based sparse
  *             attention for QSA decode", Overview)
+ *     steps : (k_step/v_step given, dense, non-causal, no mask) the cache
+ *             cells j in [0, L), then the query's own step rows t = 0..i of
+ *             k_step/v_step [B, n_q, Hkv, D]: the verification drafts are
+ *             not written into the cache; each query sees the whole prefix
+ *             plus the drafts up to itself, and the two parts are merged
+ *             (comfy-kitchen PR "Performance improvements for qwen 3.x LLM
+ *             (Part 1)", commit list: causal step rows merged into prefix
+ *             attention).  It equals the causal window over a cache that
+ *             holds the step rows at [L, L + n_q).
  *   V empty -> o = 0, lse = -inf
  *   else      s_j = scale * sum_d q[b,i,h,d] * K[b,j,g,d]
  *             m   = max_j s_j,  e_j = exp(s_j - m),  l = sum_j e_j
@@ -71,6 +80,7 @@ static double bf16_to_f64(uint16_t bits) {
 typedef struct {
     int B, n_q, Hq, Hkv, D, cap;
     const uint16_t *q, *k, *v;
+    const uint16_t *k_step, *v_step; /* NULL unless step rows are merged */
     const int32_t *kv_lens;
     double scale;
     int causal;
@@ -87,6 +97,14 @@ typedef struct {
     long long unit_begin, unit_end;
     int status;
 } worker_t;
+
+/* Row of K or V behind visible entry e of (b, g): a cache row, or step row
+   e - cap. */
+static const uint16_t *kv_row(const job_t *J, const uint16_t *cache, const uint16_t *step, int b,
+                              int g, int32_t e) {
+    if (e < J->cap) return cache + (((size_t)b * J->cap + (size_t)e) * J->Hkv + g) * (size_t)J->D;
+    return step + (((size_t)b * J->n_q + (size_t)(e - J->cap)) * J->Hkv + g) * (size_t)J->D;
+}
 
 /* Visible cell list for (b, i, g), written to vis[]; returns its length. */
 static int visible_cells(const job_t *J, int b, int i, int g, int32_t *vis) {
@@ -108,6 +126,9 @@ static int visible_cells(const job_t *J, int b, int i, int g, int32_t *vis) {
             }
             vis[n++] = (int32_t)j;
         }
+        /* Step rows are listed after the cache cells as cap + t. */
+        if (J->k_step != NULL)
+            for (int t = 0; t <= i; ++t) vis[n++] = (int32_t)(J->cap + t);
     } else {
         const int32_t *list;
         if (J->idx_head_stride == 0)
@@ -146,9 +167,9 @@ static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, do
 
     /* scores over the visible list */
     for (int t = 0; t < n; ++t) {
-        size_t ko = (((size_t)b * J->cap + (size_t)vis[t]) * J->Hkv + g) * (size_t)D;
+        const uint16_t *krow = kv_row(J, J->k, J->k_step, b, g, vis[t]);
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += qrow[d] * bf16_to_f64(J->k[ko + d]);
+        for (int d = 0; d < D; ++d) dot += qrow[d] * bf16_to_f64(krow[d]);
         s[t] = J->scale * dot;
     }
 
@@ -175,8 +196,8 @@ static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, do
         for (int t = t0; t < t1; ++t) {
             double e = exp(s[t] - m_c[c]);
             l_c += e;
-            size_t vo = (((size_t)b * J->cap + (size_t)vis[t]) * J->Hkv + g) * (size_t)D;
-            for (int d = 0; d < D; ++d) acc[d] += e * bf16_to_f64(J->v[vo + d]);
+            const uint16_t *vrow = kv_row(J, J->v, J->v_step, b, g, vis[t]);
+            for (int d = 0; d < D; ++d) acc[d] += e * bf16_to_f64(vrow[d]);
         }
         double w = exp(m_c[c] - M);
         den += w * l_c;
@@ -190,7 +211,7 @@ static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, do
 static void *worker_main(void *arg) {
     worker_t *w = (worker_t *)arg;
     const job_t *J = w->job;
-    size_t vis_cap = J->idx ? (size_t)J->W : (size_t)J->cap;
+    size_t vis_cap = J->idx ? (size_t)J->W : (size_t)J->cap + (J->k_step ? (size_t)J->n_q : 0);
     if (vis_cap == 0) vis_cap = 1;
     int32_t *vis = (int32_t *)malloc(sizeof(int32_t) * vis_cap);
     double *s = (double *)malloc(sizeof(double) * vis_cap);
@@ -223,6 +244,8 @@ int ck_oracle_nthreads_default(void) {
  * [B, n_q, W].  out [B, n_q, Hq, D] fp64; lse [B, n_q, Hq] fp64 or NULL.
  * nthreads <= 0 uses every online host core.  Returns 0 or a negative code.
  */
+static int run_job(const job_t *J, int nthreads);
+
 int ck_oracle_attn(int B, int n_q, int Hq, int Hkv, int D, int cap, const uint16_t *q,
                    const uint16_t *k, const uint16_t *v, const int32_t *kv_lens, float scale,
                    int causal, const uint8_t *keep_mask, const int32_t *idx, int W,
@@ -235,8 +258,33 @@ int ck_oracle_attn(int B, int n_q, int Hq, int Hkv, int D, int cap, const uint16
     if (idx && keep_mask) return ORACLE_ERR_ARG;
     if (num_splits < 0) return ORACLE_ERR_ARG;
 
-    job_t J = {B, n_q, Hq, Hkv, D, cap, q, k, v, kv_lens, (double)scale, causal ? 1 : 0,
+    job_t J = {B, n_q, Hq, Hkv, D, cap, q, k, v, NULL, NULL, kv_lens, (double)scale, causal ? 1 : 0,
                keep_mask, idx, W, idx_head_stride, num_splits, out, lse};
+    return run_job(&J, nthreads);
+}
+
+/*
+ * The step-row definition: q [B, n_q, Hq, D], cache k/v [B, cap, Hkv, D],
+ * k_step/v_step [B, n_q, Hkv, D] (bf16 bit patterns), kv_lens [B] (host).
+ * Query i sees the cache prefix and step rows 0..i.  Arguments otherwise as
+ * ck_oracle_attn.
+ */
+int ck_oracle_attn_steps(int B, int n_q, int Hq, int Hkv, int D, int cap, const uint16_t *q,
+                         const uint16_t *k, const uint16_t *v, const int32_t *kv_lens,
+                         const uint16_t *k_step, const uint16_t *v_step, float scale,
+                         int num_splits, double *out, double *lse, int nthreads) {
+    if (B < 1 || n_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || cap < 1) return ORACLE_ERR_ARG;
+    if (Hq % Hkv != 0) return ORACLE_ERR_ARG;
+    if (!q || !k || !v || !kv_lens || !k_step || !v_step || !out) return ORACLE_ERR_ARG;
+    if (num_splits < 0) return ORACLE_ERR_ARG;
+    job_t J = {B, n_q, Hq, Hkv, D, cap, q, k, v, k_step, v_step, kv_lens, (double)scale, 0,
+               NULL, NULL, 0, 0, num_splits, out, lse};
+    return run_job(&J, nthreads);
+}
+
+static int run_job(const job_t *JP, int nthreads) {
+    const job_t J = *JP;
+    const int B = J.B, n_q = J.n_q, Hq = J.Hq;
     long long units = (long long)B * n_q * Hq;
     if (nthreads <= 0) nthreads = ck_oracle_nthreads_default();
     if (nthreads > units) nthreads = (int)units;

@@ -7,7 +7,9 @@ something fixed from outside it:
     routine) with an explicit boolean mask, K/V expanded over the GQA group;
   * closed forms (uniform V, one visible key, K = 0, two keys);
   * invariants (split count, gather vs mask, causal row vs a shorter plain
-    decode, head permutation within a group, duplicate cells).
+    decode, head permutation within a group, duplicate cells);
+  * for the step-row merge: SDPA over a cache that holds the step rows after
+    the prefix, with the bottom-right causal mask, and its closed forms.
 Every check returns the largest deviation it saw, so a caller can assert a
 bound or, for a planted mistake, that some bound is broken.
 """
@@ -246,6 +248,49 @@ def check_head_permutation(lib) -> float:
     return max_dev(op, o[:, :, perm.numpy()])
 
 
+def steps_case(B=2, n_q=3, Hq=4, Hkv=2, D=16, cap=48, lens=(37, 0), seed=61):
+    """A cache with garbage past the prefix, and separate step rows."""
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, seed)
+    q = synth.queries(B, n_q, Hq, D, seed)
+    gen = synth.generator(seed + 1)
+    ks = synth.bf16_normal((B, n_q, Hkv, D), gen)
+    vs = synth.bf16_normal((B, n_q, Hkv, D), gen)
+    return q, k, v, np.asarray(lens, dtype=np.int32), ks, vs
+
+
+def check_sdpa_steps(lib) -> float:
+    """Step rows merged into the prefix equal SDPA over a cache holding the
+    step rows at [L, L + n_q) under the bottom-right causal mask."""
+    worst = 0.0
+    for n_q, lens in ((3, (37, 0)), (1, (12, 1)), (5, (20, 43))):
+        q, k, v, L, ks, vs = steps_case(n_q=n_q, lens=lens, seed=60 + n_q)
+        o, l = oracle.attn_steps(q, k, v, L, ks, vs, 0.3, lib=lib)
+        kc, vc = k.clone(), v.clone()
+        for b in range(q.shape[0]):
+            kc[b, L[b]:L[b] + n_q] = ks[b]
+            vc[b, L[b]:L[b] + n_q] = vs[b]
+        ro, rl = sdpa_reference(q, kc, vc, L + n_q, np.float32(0.3), True)
+        worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    return worst
+
+
+def check_steps_closed_forms(lib) -> float:
+    """Empty prefix: the first query sees only its own step row (output = that
+    V row, lse = its score); with K = 0 query i averages step rows 0..i."""
+    worst = 0.0
+    q, k, v, L, ks, vs = steps_case(B=1, n_q=3, lens=(0,), seed=71)
+    o, l = oracle.attn_steps(q, k, v, L, ks, vs, 0.3, lib=lib)
+    for h in range(4):
+        worst = max(worst, max_dev(o[0, 0, h], f64(vs[0, 0, h // 2]).numpy()))
+        sc = float(np.float32(0.3)) * float(np.dot(f64(q[0, 0, h]).numpy(), f64(ks[0, 0, h // 2]).numpy()))
+        worst = max(worst, abs(l[0, 0, h] - sc))
+    o, _ = oracle.attn_steps(q, k, v, L, torch.zeros_like(ks), vs, 0.3, lib=lib)
+    for i in range(3):
+        mean = f64(vs[0, :i + 1]).mean(dim=0).repeat_interleave(2, dim=0).numpy()
+        worst = max(worst, max_dev(o[0, i], mean))
+    return worst
+
+
 ALL_CHECKS = {
     "sdpa_dense": check_sdpa_dense,
     "sdpa_mask": check_sdpa_mask,
@@ -255,4 +300,6 @@ ALL_CHECKS = {
     "split_invariance": check_split_invariance,
     "causal_rows": check_causal_rows,
     "head_permutation": check_head_permutation,
+    "sdpa_steps": check_sdpa_steps,
+    "steps_closed_forms": check_steps_closed_forms,
 }

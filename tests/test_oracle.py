@@ -101,8 +101,12 @@ MUTANTS = {
     "wrong_exp_sign": ("double e = exp(s[t] - m_c[c]);", "double e = exp(m_c[c] - s[t]);"),
     "causal_off_by_one": ("lim = L - J->n_q + i + 1;", "lim = L - J->n_q + i;"),
     "wrong_head_map": ("int g = h / G;", "int g = h % J->Hkv;"),
-    "k_v_swapped": ("dot += qrow[d] * bf16_to_f64(J->k[ko + d]);",
-                    "dot += qrow[d] * bf16_to_f64(J->v[ko + d]);"),
+    "k_v_swapped": ("const uint16_t *krow = kv_row(J, J->k, J->k_step, b, g, vis[t]);",
+                    "const uint16_t *krow = kv_row(J, J->v, J->v_step, b, g, vis[t]);"),
+    "step_rows_off_by_one": ("for (int t = 0; t <= i; ++t) vis[n++]", "for (int t = 0; t < i; ++t) vis[n++]"),
+    "step_rows_read_from_cache": (
+        "return step + (((size_t)b * J->n_q + (size_t)(e - J->cap)) * J->Hkv + g) * (size_t)J->D;",
+        "return cache + (((size_t)b * J->cap + (size_t)(e - J->cap)) * J->Hkv + g) * (size_t)J->D;"),
     "mask_ignored": ("if (J->keep_mask[mo] == 0) continue;", "(void)mo;"),
     "gather_limit_inclusive": ("if (j >= 0 && j < lim) vis[n++]", "if (j >= 0 && j <= lim) vis[n++]"),
     "lse_missing_max": ("if (lse) *lse = M + log(den);", "if (lse) *lse = log(den);"),
