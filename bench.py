@@ -114,6 +114,30 @@ def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_l
                 frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
 
 
+def steps_case(stack, n_q, Hq, Hkv, D, L, steps, warmup, n_layers=None):
+    """Verification window with the drafts beside the cache (decode_attn_steps)."""
+    import torch
+    import decode_attention_flash_amd as ck
+    from decode_attention_flash_amd import synth
+    kv_bytes = 4 * Hkv * D * (L + n_q)
+    n = min(n_layers or layers_for(kv_bytes), len(stack.k))
+    qs = [synth.queries(1, n_q, Hq, D, 9 + l, device="cuda") for l in range(n)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    kss = [torch.randn((1, n_q, Hkv, D), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(n)]
+    vss = [torch.randn((1, n_q, Hkv, D), generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(n)]
+    outs = [torch.empty((1, n_q, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+    lens_d = torch.tensor([L], dtype=torch.int32, device="cuda")
+    ws = ck.new_workspace(ck.shape_of(qs[0], stack.k[0]))
+
+    def launch(l):
+        ck.decode_attn_steps(qs[l], stack.k[l], stack.v[l], lens_d, kss[l], vss[l], out=outs[l], workspace=ws)
+
+    ms, us = time_graph(launch, n, steps, warmup)
+    return dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, kv_gbs=kv_bytes / us / 1e3,
+                frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
+
+
 def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None):
     import numpy as np
     import torch
@@ -249,6 +273,12 @@ def main():
                 r = dense_case(stack, 1, n_q, Hq, Hkv, D, [L], args.steps, args.warmup, causal=True)
                 log(f"window n_q={n_q} L={L}: {r['us']:.2f} us")
                 sweep["causal_window"].append(dict(kv_len=L, n_q=n_q, **r))
+        sweep["step_rows"] = []
+        for L in (2000, 4000):
+            for n_q in (3, 4, 5, 6):
+                r = steps_case(stack, n_q, Hq, Hkv, D, L - n_q, args.steps, args.warmup)
+                log(f"step rows n_q={n_q} prefix={L - n_q}: {r['us']:.2f} us")
+                sweep["step_rows"].append(dict(prefix=L - n_q, n_q=n_q, **r))
         del stack
         torch.cuda.empty_cache()
         sweep["capacity"] = []

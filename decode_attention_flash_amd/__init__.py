@@ -22,7 +22,7 @@ CK_MAX_NQ = 6
 CK_MAX_SPLITS = 256
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misaligned pointer",
           -4: "workspace missing or too small", -5: "HIP runtime error"}
-EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_workspace_size",
+EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_workspace_size",
            "ck_decode_attn_plan", "ck_status_string")
 
 
@@ -72,6 +72,9 @@ def lib():
                                             ctypes.c_int, vp, ctypes.c_int, vp, vp, sz,
                                             ctypes.c_int, vp]
         L.ck_decode_attn_gather.restype = ctypes.c_int
+        L.ck_decode_attn_steps.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int,
+                                           vp, vp, sz, ctypes.c_int, vp]
+        L.ck_decode_attn_steps.restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
         L.ck_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -226,4 +229,33 @@ def decode_attn_gather(q, k_cache, v_cache, kv_lens, idx, *, scale: float | None
                                      ctypes.c_void_p(st_handle))
     if st != 0:
         raise CkError(st, "ck_decode_attn_gather")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, *, scale: float | None = None,
+                      out_dtype=torch.float32, out=None, lse=None, return_lse=False, workspace=None,
+                      num_splits: int = 0, stream=None):
+    """Verification queries over the cache prefix plus their own step rows
+    (``ck_decode_attn_steps``): query i sees cache cells j < kv_lens[b] and
+    step rows 0..i of k_step / v_step [B, n_q, Hkv, D] bf16, which are not in
+    the cache.  Same result as ``decode_attn(..., causal=True)`` over a cache
+    holding the step rows at [L, L + n_q)."""
+    shape, out, lse, odt = _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse)
+    _check(k_step, "k_step", torch.bfloat16)
+    _check(v_step, "v_step", torch.bfloat16)
+    want = (shape.B, shape.n_q, shape.Hkv, shape.D)
+    if tuple(k_step.shape) != want or tuple(v_step.shape) != want:
+        raise ValueError(f"k_step and v_step must be [B, n_q, Hkv, D] = {want}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if workspace is None:
+        workspace = _cached_workspace(shape, 0, num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().ck_decode_attn_steps(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(kv_lens), _ptr(k_step), _ptr(v_step), ctypes.c_float(scale),
+                                    _ptr(out), odt, _ptr(lse), _ptr(workspace), ws_bytes, num_splits,
+                                    ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn_steps")
     return (out, lse) if (return_lse or lse is not None) else out

@@ -81,6 +81,8 @@ struct KParams {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
+    const uint16_t* k_step;  // step rows [B, n_q, Hkv, D] merged into the prefix, or null
+    const uint16_t* v_step;
     const int32_t* kv_lens;
     const uint8_t* keep_mask;
     const int32_t* idx;
@@ -440,6 +442,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     const uint32_t kv_bytes = rows_lim > 0 ? (uint32_t)(rows_lim - 1) * p.row_bytes + 2u * D : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, kv_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, kv_bytes);
+    // Step rows (verification drafts that are not in the cache): the unit's
+    // last split streams them as one extra tile, whose row t is visible to
+    // query i when t <= i.
+    const bool steps = MODE == 0 && p.k_step != nullptr;
+    const size_t step_off = ((size_t)b * p.n_q * p.Hkv + g) * D;
+    const uint32_t step_bytes = (uint32_t)(p.n_q - 1) * p.row_bytes + 2u * D;
+    const __amdgpu_buffer_rsrc_t rks = make_rsrc(steps ? p.k_step + step_off : p.k, steps ? step_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rvs = make_rsrc(steps ? p.v_step + step_off : p.v, steps ? step_bytes : 0u);
     const size_t mask_per_b = (size_t)p.n_q * p.Hkv * p.cap;
     const __amdgpu_buffer_rsrc_t rm = MODE == 1 ? make_rsrc(p.keep_mask + (size_t)b * mask_per_b, (uint32_t)mask_per_b)
                                                 : make_rsrc(p.k, 0u);
@@ -455,7 +465,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 
     unsigned char* klds = smem + wave * Gm::STAGE;
     unsigned char* vlds = klds + Gm::KBYTES;
-    const int ntiles = (pos_end - pos_begin + TT - 1) / TT;
+    const int ntiles_c = (pos_end - pos_begin + TT - 1) / TT;  // cache tiles
+    const int ntiles = ntiles_c + ((steps && s == n_active - 1) ? 1 : 0);
     // Whether every split of the unit has started: thread 0 reads the count
     // after its first tile's data has arrived, so the round trip hides under
     // the tile loop.  The count only grows until the unit's last arrival,
@@ -476,7 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     constexpr bool kDeferMask = !(D == 256 && RT == 2);
     uint64_t gvalid = 0;
     auto issue = [&](int tile, int jv) {
-        const int tb = pos_begin + tile * TT;
+        const bool st_tile = steps && tile == ntiles_c;
+        const int tb = st_tile ? 0 : pos_begin + tile * TT;
         uint32_t roff[VI];
         if constexpr (GATHER) {
             const bool ok = jv >= 0 && jv < lim_g;
@@ -515,10 +527,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 }
         }
         const uint32_t coff = (uint32_t)(lane % CPR) * 16u;
+        const __amdgpu_buffer_rsrc_t rkt = st_tile ? rks : rk;
+        const __amdgpu_buffer_rsrc_t rvt = st_tile ? rvs : rv;
 #pragma unroll
-        for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rk, roff[n] + coff);
+        for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rkt, roff[n] + coff);
 #pragma unroll
-        for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rv, roff[n] + coff);
+        for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rvt, roff[n] + coff);
     };
 
     // Query fragments to LDS before the first tile's loads are issued (they
@@ -537,6 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 
     for (int tile = wave; tile < ntiles; tile += kWaves) {
         const int tb = pos_begin + tile * TT;
+        const bool st_tile = steps && tile == ntiles_c;
         const uint64_t tvalid = gvalid;
         uint32_t tmbits[RT][MB];  // keep bit e: token 16mb + 4q4 + e
         if constexpr (MODE == 1) {
@@ -602,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                     if constexpr (GATHER) {
                         ok = row_ok && ((tvalid >> off) & 1ull);
                     } else {
-                        ok = tb + off < lim;
+                        ok = st_tile ? (row_ok && off <= i_r[rt]) : tb + off < lim;
                         if constexpr (MODE == 1) ok = ok && ((tmbits[rt][mb] >> e) & 1u);
                     }
                     const float x = ok ? sc[rt][mb][e] * p.scale_log2 : -INFINITY;
@@ -918,12 +933,15 @@ static hipError_t launch_mode(int D, int RT, const KParams& kp, int grid, hipStr
 static int run(const ck_decode_shape* s, const void* q, const void* k, const void* v, const int32_t* kv_lens,
                const uint8_t* keep_mask, const int32_t* idx, int32_t W, int64_t idx_head_stride, float scale,
                int causal, void* out, int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
-               int num_splits, void* stream) {
+               int num_splits, void* stream, const void* k_step = nullptr, const void* v_step = nullptr) {
     if (!s) return CK_ERR_ARG;
     ck_decode_plan pl;
     int st = plan_impl(s, W, num_splits, 1, &pl);  // shape checks only
     if (st != CK_OK) return st;
     if (!q || !k || !v || !kv_lens || !out) return CK_ERR_ARG;
+    if ((k_step == nullptr) != (v_step == nullptr)) return CK_ERR_ARG;
+    if (k_step && (W > 0 || keep_mask || causal)) return CK_ERR_ARG;
+    if (k_step && (!aligned(k_step, 16) || !aligned(v_step, 16))) return CK_ERR_ALIGN;
     if (W > 0 && !idx) return CK_ERR_ARG;
     if (W > 0 && idx_head_stride != 0 && idx_head_stride < W) return CK_ERR_ARG;
     if (out_dtype != CK_DT_F32 && out_dtype != CK_DT_BF16) return CK_ERR_ARG;
@@ -944,6 +962,8 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
 
     KParams kp{};
     kp.q = static_cast<const uint16_t*>(q);
+    kp.k_step = static_cast<const uint16_t*>(k_step);
+    kp.v_step = static_cast<const uint16_t*>(v_step);
     kp.k = static_cast<const uint16_t*>(k);
     kp.v = static_cast<const uint16_t*>(v);
     kp.kv_lens = kv_lens;
@@ -1035,6 +1055,15 @@ int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const voi
     if (W < 1) return CK_ERR_ARG;
     return ckda::run(shape, q, k_cache, v_cache, kv_lens, nullptr, idx, W, idx_head_stride, scale, causal, out,
                      out_dtype, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+int ck_decode_attn_steps(const ck_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* kv_lens, const void* k_step, const void* v_step, float scale, void* out,
+                         int out_dtype, float* lse, void* workspace, size_t workspace_bytes, int num_splits,
+                         void* stream) {
+    if (!k_step || !v_step) return CK_ERR_ARG;
+    return ckda::run(shape, q, k_cache, v_cache, kv_lens, nullptr, nullptr, 0, 0, scale, 0, out, out_dtype, lse,
+                     workspace, workspace_bytes, num_splits, stream, k_step, v_step);
 }
 
 const char* ck_status_string(int status) {

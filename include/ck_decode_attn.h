@@ -161,6 +161,23 @@ int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const voi
                           int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
                           int num_splits, void* stream);
 
+/* Step rows merged into prefix attention: the n_q verification queries of
+ * an MTP step attend the cache prefix [0, L) plus their own draft rows,
+ * whose K/V are passed separately instead of being written into the cache
+ * first (comfy-kitchen PR "Performance improvements for qwen 3.x LLM
+ * (Part 1)", commit list: causal step rows merged into prefix attention).
+ * Query i sees every cache cell j < L and step rows 0..i, so the result
+ * equals ck_decode_attn with causal = 1 over a cache holding the step rows
+ * at [L, L + n_q).  The unit's last split streams the step rows as one more
+ * tile and the in-launch combine merges it with the prefix.
+ *   k_step, v_step : bf16 [B, n_q, Hkv, D], 16-byte aligned, non-null.
+ * Other arguments as ck_decode_attn (no keep_mask; the window is implied);
+ * the workspace is the dense one (ck_decode_attn_workspace_size, W = 0). */
+int ck_decode_attn_steps(const ck_decode_shape* shape, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* kv_lens, const void* k_step,
+                         const void* v_step, float scale, void* out, int out_dtype, float* lse,
+                         void* workspace, size_t workspace_bytes, int num_splits, void* stream);
+
 /* Static text for a status code. */
 const char* ck_status_string(int status);
 

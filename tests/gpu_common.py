@@ -63,6 +63,27 @@ def oracle_ref(q, k, v, lens, *, causal=False, keep_mask=None, idx=None, scale=N
                        keep_mask=keep_mask, idx=idx)
 
 
+def steps_gpu(q, k, v, lens, ks, vs, *, out_dtype=torch.float32, num_splits=0, scale=None,
+              device_inputs=None):
+    D = q.shape[-1]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    if device_inputs is None:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    else:
+        qd, kd, vd = device_inputs
+    lens_d = torch.as_tensor(np.asarray(lens), dtype=torch.int32).to(DEV)
+    out, lse = ck.decode_attn_steps(qd, kd, vd, lens_d, ks.to(DEV), vs.to(DEV), scale=scale,
+                                    out_dtype=out_dtype, return_lse=True, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def steps_ref(q, k, v, lens, ks, vs, *, scale=None):
+    D = q.shape[-1]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    return oracle.attn_steps(q, k, v, np.asarray(lens, dtype=np.int32), ks, vs, scale)
+
+
 def assert_close(gpu, ref, out_dtype=torch.float32, what=""):
     go, gl = gpu
     ro, rl = ref

@@ -9,7 +9,8 @@ import torch
 
 import decode_attention_flash_amd as ck
 from decode_attention_flash_amd import synth
-from gpu_common import (DEV, TOL_F32, assert_close, dense_gpu, gather_gpu, note, oracle_ref)
+from gpu_common import (DEV, TOL_F32, assert_close, dense_gpu, gather_gpu, note, oracle_ref, steps_gpu,
+                        steps_ref)
 
 pytestmark = pytest.mark.gpu
 
@@ -141,6 +142,84 @@ def test_batched_ragged_graph_replay():
     pl = ck.plan(shape)
     cnt = ws[:pl["units"] * 1024].view(torch.int32)
     assert int(cnt.abs().sum().item()) == 0
+
+
+# ----------------------------------------------------- step-row merge ----
+
+def _steps(B, n_q, Hkv, D, seed):
+    gen = synth.generator(seed)
+    return synth.bf16_normal((B, n_q, Hkv, D), gen), synth.bf16_normal((B, n_q, Hkv, D), gen)
+
+
+@pytest.mark.parametrize("n_q", [1, 3, 6])
+@pytest.mark.parametrize("L", [0, 1, 37, 2000, 4000])
+def test_d256_step_rows_match_oracle(layer_d256, n_q, L):
+    """MTP verification with the drafts passed beside the cache: prefix
+    [0, L) plus step rows 0..i for query i."""
+    note(f"step rows D=256 n_q={n_q} L={L}")
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, n_q, 16, 256, 1030 + n_q)
+    ks, vs = _steps(1, n_q, 4, 256, 1040 + n_q + L)
+    gpu = steps_gpu(q, k, v, [L], ks, vs, device_inputs=(q.to(DEV), kd, vd))
+    assert_close(gpu, steps_ref(q, k, v, [L], ks, vs), what=f"steps n_q={n_q} L={L}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_d128_step_rows_batch(out_dtype):
+    """Two sequences of different length (one empty), D=128, ragged tail."""
+    B, n_q, Hq, Hkv, D, cap = 2, 4, 8, 2, 128, 1024
+    lens = [301, 0]
+    note(f"step rows D=128 batch {out_dtype}")
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 1050)
+    q = synth.queries(B, n_q, Hq, D, 1051)
+    ks, vs = _steps(B, n_q, Hkv, D, 1052)
+    gpu = steps_gpu(q, k, v, lens, ks, vs, out_dtype=out_dtype)
+    assert_close(gpu, steps_ref(q, k, v, lens, ks, vs), out_dtype, "steps D=128")
+
+
+def test_step_rows_equal_causal_window_in_cache(layer_d256):
+    """The same window computed both ways on the GPU: drafts beside the cache,
+    and drafts written into the cache at [L, L + n_q) with the causal mask."""
+    n_q, L = 5, 3000
+    note("step rows vs causal window")
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, n_q, 16, 256, 1060)
+    ks, vs = _steps(1, n_q, 4, 256, 1061)
+    a = steps_gpu(q, k, v, [L], ks, vs, device_inputs=(q.to(DEV), kd, vd))
+    kc, vc = kd.clone(), vd.clone()
+    kc[0, L:L + n_q] = ks[0].to(DEV)
+    vc[0, L:L + n_q] = vs[0].to(DEV)
+    bw = dense_gpu(q, k, v, [L + n_q], causal=True, device_inputs=(q.to(DEV), kc, vc))
+    assert np.max(np.abs(a[0] - bw[0])) <= TOL_F32
+    assert np.max(np.abs(a[1] - bw[1])) <= 4e-3
+
+
+def test_step_rows_split_counts(layer_d256):
+    """Forced split counts (1, 7, 64) give the same window within tolerance."""
+    n_q, L = 3, 2000
+    note("step rows split counts")
+    k, v, (kd, vd) = layer_d256
+    q = synth.queries(1, n_q, 16, 256, 1070)
+    ks, vs = _steps(1, n_q, 4, 256, 1071)
+    ref = steps_ref(q, k, v, [L], ks, vs)
+    for S in (1, 7, 64):
+        gpu = steps_gpu(q, k, v, [L], ks, vs, num_splits=S, device_inputs=(q.to(DEV), kd, vd))
+        assert_close(gpu, ref, what=f"steps S={S}")
+
+
+def test_step_rows_argument_errors():
+    B, n_q, Hq, Hkv, D, cap = 1, 2, 8, 2, 128, 64
+    q = torch.zeros((B, n_q, Hq, D), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((B, cap, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    lens = torch.tensor([10], dtype=torch.int32, device=DEV)
+    ks = torch.zeros((B, n_q, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        ck.decode_attn_steps(q, k, k, lens, ks[:, :1].contiguous(), ks)
+    buf = torch.zeros(ks.numel() + 8, dtype=torch.bfloat16, device=DEV)
+    odd = buf[1:1 + ks.numel()].view(ks.shape)   # 2-byte aligned only
+    with pytest.raises(ck.CkError) as e:
+        ck.decode_attn_steps(q, k, k, lens, odd, ks)
+    assert e.value.status == -3
 
 
 # -------------------------------------------------------------- gather ----
