@@ -55,6 +55,14 @@ def load(path: str | None = None):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
     ]
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.ck_oracle_attn_q8.restype = ci
+    lib.ck_oracle_attn_q8.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_float, ci, ci, vp, vp, ci]
+    lib.ck_oracle_q8_quantize_rows.restype = None
+    lib.ck_oracle_q8_quantize_rows.argtypes = [ctypes.c_longlong, ci, vp, vp, vp]
+    lib.ck_oracle_q8_append.restype = ci
+    lib.ck_oracle_q8_append.argtypes = [ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ck_oracle_nthreads_default.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -163,6 +171,69 @@ def attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, scale: float, num_s
     st = lib.ck_oracle_attn_steps(B, n_q, Hq, Hkv, D, cap, ptr(qb), ptr(kb), ptr(vb), ptr(lens),
                                   ptr(ksb), ptr(vsb), ctypes.c_float(scale), num_splits, ptr(out),
                                   ptr(lse), nthreads)
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return out, lse
+
+
+def q8_quantize(x, lib=None):
+    """Rows of bf16 x [..., D] to (codes int8 [..., D], scales float32 [...])."""
+    lib = lib or load()
+    xb = _bits(x)
+    D = xb.shape[-1]
+    codes = np.empty(xb.shape, dtype=np.int8)
+    scales = np.empty(xb.shape[:-1], dtype=np.float32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    lib.ck_oracle_q8_quantize_rows(xb.size // D, D, ptr(xb), ptr(codes), ptr(scales))
+    return codes, scales
+
+
+def q8_append(k_new, v_new, start, block_table, kq, vq, ksc, vsc, lib=None):
+    """Quantize k_new / v_new [B, n_new, Hkv, D] (bf16) into the paged cache
+    (kq, vq int8 [num_pages, page, Hkv, D]; ksc, vsc float32 [num_pages,
+    page, Hkv]; numpy arrays updated in place) at positions start[b] + t."""
+    lib = lib or load()
+    kb, vb = _bits(k_new), _bits(v_new)
+    B, n_new, Hkv, D = kb.shape
+    num_pages, page = kq.shape[0], kq.shape[1]
+    bt = _np(block_table, np.int32)
+    st = _np(start, np.int32).reshape(-1)
+    for a, dt in ((kq, np.int8), (vq, np.int8), (ksc, np.float32), (vsc, np.float32)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError("paged cache arrays must be contiguous int8 / float32")
+    if kq.shape != (num_pages, page, Hkv, D) or vq.shape != kq.shape or ksc.shape != kq.shape[:3] \
+            or vsc.shape != ksc.shape or bt.shape[0] != B or st.shape[0] != B:
+        raise ValueError("paged cache shape mismatch")
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    r = lib.ck_oracle_q8_append(B, n_new, Hkv, D, page, bt.shape[1], num_pages, ptr(kb), ptr(vb), ptr(st),
+                                ptr(bt), ptr(kq), ptr(vq), ptr(ksc), ptr(vsc))
+    if r != 0:
+        raise RuntimeError(f"oracle failed with status {r}")
+
+
+def attn_q8(q, kq, vq, ksc, vsc, block_table, kv_lens, scale: float, causal: bool = False,
+            num_splits: int = 0, nthreads: int = 0, lib=None):
+    """Attention over the paged INT8 cache (cell j of sequence b in page
+    block_table[b, j // page], value code * scale).  q [B, n_q, Hq, D] bf16.
+    Returns (out [B, n_q, Hq, D] float64, lse [B, n_q, Hq] float64)."""
+    lib = lib or load()
+    qb = _bits(q)
+    B, n_q, Hq, D = qb.shape
+    kq, vq = _np(kq, np.int8), _np(vq, np.int8)
+    ksc, vsc = _np(ksc, np.float32), _np(vsc, np.float32)
+    num_pages, page, Hkv, Dk = kq.shape
+    bt = _np(block_table, np.int32)
+    if Dk != D or vq.shape != kq.shape or ksc.shape != kq.shape[:3] or vsc.shape != ksc.shape:
+        raise ValueError("paged cache shape mismatch")
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    lens = _np(kv_lens, np.int32).reshape(-1)
+    out = np.empty((B, n_q, Hq, D), dtype=np.float64)
+    lse = np.empty((B, n_q, Hq), dtype=np.float64)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.ck_oracle_attn_q8(B, n_q, Hq, Hkv, D, page, bt.shape[1], num_pages, ptr(qb), ptr(kq), ptr(vq),
+                               ptr(ksc), ptr(vsc), ptr(bt), ptr(lens), ctypes.c_float(scale),
+                               1 if causal else 0, num_splits, ptr(out), ptr(lse), nthreads)
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
     return out, lse

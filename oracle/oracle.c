@@ -54,6 +54,21 @@
  * is split and the splits' results are combined).  It exists to pin that
  * algebra; it must agree with the unsplit result to rounding.
  *
+ * Paged INT8 cache (ck_oracle_attn_q8): K and V are stored per (token, KV
+ * head) row as int8 codes with one fp32 scale, in pages of `page` tokens
+ * reached through a block table (comfy-kitchen PR "Performance improvements
+ * for qwen 3.x LLM (Part 1)", commit list: bounded paged INT8 decode cache
+ * with rollback; the pages run 8-bit KV caches throughout, llama.cpp PR
+ * "qwen4exp: attend the selected cells instead of masking the window",
+ * Additional information).  Cell j of sequence b lives in page
+ * block_table[b][j / page], row j % page; its value is code * scale, taken
+ * exactly in fp64, and the definition above applies unchanged.  A cell whose
+ * page id is outside [0, num_pages) reads as zeros.  Rows are quantized in
+ * fp32 (ck_oracle_q8_quantize_row): scale = amax / 127, code = x * (127 /
+ * amax) rounded half to even and clamped to [-127, 127]; an all-zero row has
+ * scale 0.  Rolling a sequence back is lowering its length: cells at or past
+ * it are never read and are overwritten by the next append.
+ *
  * Inputs are bf16 bit patterns (uint16); each is widened to fp64 exactly.
  * scale arrives as the fp32 value the GPU receives and is widened.  Cells
  * outside V are never read, so garbage (NaN/Inf bit patterns) there cannot
@@ -90,6 +105,11 @@ typedef struct {
     long long idx_head_stride;
     int num_splits;
     double *out, *lse;
+    /* paged INT8 cache; kq == NULL for the bf16 cache */
+    const int8_t *kq, *vq;
+    const float *ksc, *vsc;
+    const int32_t *block_table;
+    int page, max_pages, num_pages;
 } job_t;
 
 typedef struct {
@@ -97,6 +117,20 @@ typedef struct {
     long long unit_begin, unit_end;
     int status;
 } worker_t;
+
+/* Dequantized row of cell j of (b, g) in the paged INT8 cache, exactly in
+   fp64; zeros when the page id is outside [0, num_pages). */
+static void q8_row(const job_t *J, const int8_t *codes, const float *scales, int b, int g, int32_t j,
+                   double *dst) {
+    int32_t pg = J->block_table[(size_t)b * J->max_pages + (size_t)(j / J->page)];
+    if (pg < 0 || pg >= J->num_pages) {
+        for (int d = 0; d < J->D; ++d) dst[d] = 0.0;
+        return;
+    }
+    size_t row = ((size_t)pg * J->page + (size_t)(j % J->page)) * J->Hkv + g;
+    double sc = (double)scales[row];
+    for (int d = 0; d < J->D; ++d) dst[d] = (double)codes[row * J->D + d] * sc;
+}
 
 /* Row of K or V behind visible entry e of (b, g): a cache row, or step row
    e - cap. */
@@ -145,7 +179,7 @@ static int visible_cells(const job_t *J, int b, int i, int g, int32_t *vis) {
 }
 
 static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, double *acc,
-                     double *qrow) {
+                     double *qrow, double *rowbuf) {
     const int D = J->D;
     const int G = J->Hq / J->Hkv;
     int h = (int)(unit % J->Hq);
@@ -167,9 +201,14 @@ static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, do
 
     /* scores over the visible list */
     for (int t = 0; t < n; ++t) {
-        const uint16_t *krow = kv_row(J, J->k, J->k_step, b, g, vis[t]);
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += qrow[d] * bf16_to_f64(krow[d]);
+        if (J->kq != NULL) {
+            q8_row(J, J->kq, J->ksc, b, g, vis[t], rowbuf);
+            for (int d = 0; d < D; ++d) dot += qrow[d] * rowbuf[d];
+        } else {
+            const uint16_t *krow = kv_row(J, J->k, J->k_step, b, g, vis[t]);
+            for (int d = 0; d < D; ++d) dot += qrow[d] * bf16_to_f64(krow[d]);
+        }
         s[t] = J->scale * dot;
     }
 
@@ -196,8 +235,13 @@ static void one_unit(const job_t *J, long long unit, int32_t *vis, double *s, do
         for (int t = t0; t < t1; ++t) {
             double e = exp(s[t] - m_c[c]);
             l_c += e;
-            const uint16_t *vrow = kv_row(J, J->v, J->v_step, b, g, vis[t]);
-            for (int d = 0; d < D; ++d) acc[d] += e * bf16_to_f64(vrow[d]);
+            if (J->vq != NULL) {
+                q8_row(J, J->vq, J->vsc, b, g, vis[t], rowbuf);
+                for (int d = 0; d < D; ++d) acc[d] += e * rowbuf[d];
+            } else {
+                const uint16_t *vrow = kv_row(J, J->v, J->v_step, b, g, vis[t]);
+                for (int d = 0; d < D; ++d) acc[d] += e * bf16_to_f64(vrow[d]);
+            }
         }
         double w = exp(m_c[c] - M);
         den += w * l_c;
@@ -217,16 +261,18 @@ static void *worker_main(void *arg) {
     double *s = (double *)malloc(sizeof(double) * vis_cap);
     double *acc = (double *)malloc(sizeof(double) * (size_t)J->D);
     double *qrow = (double *)malloc(sizeof(double) * (size_t)J->D);
-    if (!vis || !s || !acc || !qrow) {
+    double *rowbuf = (double *)malloc(sizeof(double) * (size_t)J->D);
+    if (!vis || !s || !acc || !qrow || !rowbuf) {
         w->status = ORACLE_ERR_NOMEM;
     } else {
-        for (long long u = w->unit_begin; u < w->unit_end; ++u) one_unit(J, u, vis, s, acc, qrow);
+        for (long long u = w->unit_begin; u < w->unit_end; ++u) one_unit(J, u, vis, s, acc, qrow, rowbuf);
         w->status = ORACLE_OK;
     }
     free(vis);
     free(s);
     free(acc);
     free(qrow);
+    free(rowbuf);
     return NULL;
 }
 
@@ -259,7 +305,8 @@ int ck_oracle_attn(int B, int n_q, int Hq, int Hkv, int D, int cap, const uint16
     if (num_splits < 0) return ORACLE_ERR_ARG;
 
     job_t J = {B, n_q, Hq, Hkv, D, cap, q, k, v, NULL, NULL, kv_lens, (double)scale, causal ? 1 : 0,
-               keep_mask, idx, W, idx_head_stride, num_splits, out, lse};
+               keep_mask, idx, W, idx_head_stride, num_splits, out, lse,
+               NULL, NULL, NULL, NULL, NULL, 0, 0, 0};
     return run_job(&J, nthreads);
 }
 
@@ -278,8 +325,93 @@ int ck_oracle_attn_steps(int B, int n_q, int Hq, int Hkv, int D, int cap, const 
     if (!q || !k || !v || !kv_lens || !k_step || !v_step || !out) return ORACLE_ERR_ARG;
     if (num_splits < 0) return ORACLE_ERR_ARG;
     job_t J = {B, n_q, Hq, Hkv, D, cap, q, k, v, k_step, v_step, kv_lens, (double)scale, 0,
-               NULL, NULL, 0, 0, num_splits, out, lse};
+               NULL, NULL, 0, 0, num_splits, out, lse,
+               NULL, NULL, NULL, NULL, NULL, 0, 0, 0};
     return run_job(&J, nthreads);
+}
+
+/*
+ * Attention over the paged INT8 cache: q [B, n_q, Hq, D] bf16; kq/vq int8
+ * [num_pages, page, Hkv, D]; ksc/vsc fp32 [num_pages, page, Hkv];
+ * block_table int32 [B, max_pages]; kv_lens [B] clamped to
+ * [0, max_pages * page].  Dense and causal windows as ck_oracle_attn.
+ */
+int ck_oracle_attn_q8(int B, int n_q, int Hq, int Hkv, int D, int page, int max_pages, int num_pages,
+                      const uint16_t *q, const int8_t *kq, const int8_t *vq, const float *ksc,
+                      const float *vsc, const int32_t *block_table, const int32_t *kv_lens,
+                      float scale, int causal, int num_splits, double *out, double *lse,
+                      int nthreads) {
+    if (B < 1 || n_q < 1 || Hq < 1 || Hkv < 1 || D < 1 || page < 1 || max_pages < 1 || num_pages < 1)
+        return ORACLE_ERR_ARG;
+    if (Hq % Hkv != 0) return ORACLE_ERR_ARG;
+    if ((long long)page * max_pages > 0x7fffffffLL) return ORACLE_ERR_ARG;
+    if (!q || !kq || !vq || !ksc || !vsc || !block_table || !kv_lens || !out) return ORACLE_ERR_ARG;
+    if (num_splits < 0) return ORACLE_ERR_ARG;
+    job_t J = {B, n_q, Hq, Hkv, D, page * max_pages, q, NULL, NULL, NULL, NULL, kv_lens, (double)scale,
+               causal ? 1 : 0, NULL, NULL, 0, 0, num_splits, out, lse,
+               kq, vq, ksc, vsc, block_table, page, max_pages, num_pages};
+    return run_job(&J, nthreads);
+}
+
+/* One row of D bf16 values to int8 codes and an fp32 scale (see the header
+   comment); all arithmetic in fp32, rounding half to even. */
+void ck_oracle_q8_quantize_row(int D, const uint16_t *x, int8_t *codes, float *scale) {
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float a = fabsf((float)bf16_to_f64(x[d]));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int d = 0; d < D; ++d) codes[d] = 0;
+        *scale = 0.0f;
+        return;
+    }
+    float inv = 127.0f / amax;
+    *scale = amax / 127.0f;
+    for (int d = 0; d < D; ++d) {
+        float c = nearbyintf((float)bf16_to_f64(x[d]) * inv);
+        if (c > 127.0f) c = 127.0f;
+        if (c < -127.0f) c = -127.0f;
+        codes[d] = (int8_t)c;
+    }
+}
+
+/* n_rows independent rows (x [n_rows, D]), as ck_oracle_q8_quantize_row. */
+void ck_oracle_q8_quantize_rows(long long n_rows, int D, const uint16_t *x, int8_t *codes, float *scales) {
+    for (long long r = 0; r < n_rows; ++r)
+        ck_oracle_q8_quantize_row(D, x + r * D, codes + r * D, scales + r);
+}
+
+/*
+ * Append n_new rows per sequence: k_new/v_new [B, n_new, Hkv, D] bf16 go to
+ * positions start[b] + t (start clamped to [0, max_pages * page]); rows past
+ * the capacity, or whose page id is outside [0, num_pages), are dropped.
+ */
+int ck_oracle_q8_append(int B, int n_new, int Hkv, int D, int page, int max_pages, int num_pages,
+                        const uint16_t *k_new, const uint16_t *v_new, const int32_t *start,
+                        const int32_t *block_table, int8_t *kq, int8_t *vq, float *ksc, float *vsc) {
+    if (B < 1 || n_new < 1 || Hkv < 1 || D < 1 || page < 1 || max_pages < 1 || num_pages < 1)
+        return ORACLE_ERR_ARG;
+    if (!k_new || !v_new || !start || !block_table || !kq || !vq || !ksc || !vsc) return ORACLE_ERR_ARG;
+    long long cap = (long long)page * max_pages;
+    for (int b = 0; b < B; ++b) {
+        long long s0 = start[b];
+        if (s0 < 0) s0 = 0;
+        if (s0 > cap) s0 = cap;
+        for (int t = 0; t < n_new; ++t) {
+            long long pos = s0 + t;
+            if (pos >= cap) break;
+            int32_t pg = block_table[(size_t)b * max_pages + (size_t)(pos / page)];
+            if (pg < 0 || pg >= num_pages) continue;
+            for (int g = 0; g < Hkv; ++g) {
+                size_t row = ((size_t)pg * page + (size_t)(pos % page)) * Hkv + g;
+                size_t src = (((size_t)b * n_new + t) * Hkv + g) * (size_t)D;
+                ck_oracle_q8_quantize_row(D, k_new + src, kq + row * D, ksc + row);
+                ck_oracle_q8_quantize_row(D, v_new + src, vq + row * D, vsc + row);
+            }
+        }
+    }
+    return ORACLE_OK;
 }
 
 static int run_job(const job_t *JP, int nthreads) {

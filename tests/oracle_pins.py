@@ -9,7 +9,10 @@ something fixed from outside it:
   * invariants (split count, gather vs mask, causal row vs a shorter plain
     decode, head permutation within a group, duplicate cells);
   * for the step-row merge: SDPA over a cache that holds the step rows after
-    the prefix, with the bottom-right causal mask, and its closed forms.
+    the prefix, with the bottom-right causal mask, and its closed forms;
+  * for the paged INT8 cache: the quantizer's error bound, extremes and an
+    exact round trip; SDPA over the pages gathered through the block table;
+    page-pool permutation; append placement and rollback.
 Every check returns the largest deviation it saw, so a caller can assert a
 bound or, for a planted mistake, that some bound is broken.
 """
@@ -291,6 +294,128 @@ def check_steps_closed_forms(lib) -> float:
     return worst
 
 
+# ------------------------------------------------------- paged INT8 cache ----
+
+def check_q8_quantize(lib) -> float:
+    """Codes in [-127, 127]; the largest |x| maps to +-127; |x - code*scale| is
+    at most half a step; negation is symmetric; zero rows give scale 0; rows
+    k * 2^e (integers |k| <= 127, one of them 127) round-trip exactly."""
+    worst = 0.0
+    x = synth.bf16_normal((48, 64), synth.generator(81)) * 3
+    x[5] = 0
+    codes, sc = oracle.q8_quantize(x, lib=lib)
+    xd = f64(x).numpy()
+    worst = max(worst, float(np.max(np.abs(codes.astype(np.int64))) > 127))
+    for r in range(x.shape[0]):
+        if sc[r] == 0:
+            worst = max(worst, float(np.any(codes[r] != 0)), float(np.any(xd[r] != 0)))
+            continue
+        err = np.abs(xd[r] - codes[r].astype(np.float64) * float(sc[r]))
+        worst = max(worst, float(np.max(np.maximum(err - 0.5 * float(sc[r]) * (1 + 1e-5), 0))))
+        worst = max(worst, float(abs(int(codes[r][np.argmax(np.abs(xd[r]))])) != 127))
+    cn, sn = oracle.q8_quantize(-x, lib=lib)
+    worst = max(worst, float(np.any(cn != -codes)), float(np.any(sn != sc)))
+    gen = np.random.default_rng(82)
+    k = gen.integers(-127, 128, size=(8, 32))
+    k[:, 3] = 127 * np.where(gen.random(8) < 0.5, 1, -1)
+    e = gen.integers(-20, 20, size=(8, 1))
+    xr = torch.from_numpy(k * np.exp2(e.astype(np.float64))).to(torch.bfloat16)
+    cr, sr = oracle.q8_quantize(xr, lib=lib)
+    worst = max(worst, float(np.any(cr != k)), float(np.max(np.abs(sr - np.exp2(e[:, 0])))))
+    return worst
+
+
+def q8_case(B=2, n_q=3, Hq=4, Hkv=2, D=16, page=8, max_pages=4, num_pages=9, seed=91):
+    gen = np.random.default_rng(seed)
+    kq = gen.integers(-127, 128, size=(num_pages, page, Hkv, D)).astype(np.int8)
+    vq = gen.integers(-127, 128, size=(num_pages, page, Hkv, D)).astype(np.int8)
+    ksc = (gen.random((num_pages, page, Hkv)) * 0.05 + 0.001).astype(np.float32)
+    vsc = (gen.random((num_pages, page, Hkv)) * 0.05 + 0.001).astype(np.float32)
+    bt = np.stack([gen.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
+    q = synth.queries(B, n_q, Hq, D, seed)
+    return q, kq, vq, ksc, vsc, bt
+
+
+def q8_dense(codes, scales, bt, num_pages):
+    """[B, max_pages * page, Hkv, D] float64 view of the pages through the
+    block table (invalid page ids give zeros)."""
+    B, max_pages = bt.shape
+    page = codes.shape[1]
+    vals = codes.astype(np.float64) * scales.astype(np.float64)[..., None]
+    out = np.zeros((B, max_pages * page) + codes.shape[2:], dtype=np.float64)
+    for b in range(B):
+        for lp in range(max_pages):
+            pg = bt[b, lp]
+            if 0 <= pg < num_pages:
+                out[b, lp * page:(lp + 1) * page] = vals[pg]
+    return torch.from_numpy(out)
+
+
+def check_q8_sdpa(lib) -> float:
+    """Attention over the paged INT8 cache equals SDPA over the dequantized
+    pages gathered through the block table (dense and causal, a page id
+    outside the pool reading as zeros)."""
+    worst = 0.0
+    q, kq, vq, ksc, vsc, bt = q8_case()
+    bt[1, 1] = 40   # outside the pool of 9 pages: its cells read as zeros
+    for causal in (False, True):
+        lens = np.array([29, 17], dtype=np.int32)
+        o, l = oracle.attn_q8(q, kq, vq, ksc, vsc, bt, lens, 0.3, causal, lib=lib)
+        kd, vd = q8_dense(kq, ksc, bt, 9), q8_dense(vq, vsc, bt, 9)
+        ro, rl = sdpa_reference(q, kd, vd, lens, np.float32(0.3), causal)
+        worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    return worst
+
+
+def check_q8_page_permutation(lib) -> float:
+    """Moving pages around the pool (and the block table with them) leaves the
+    result bit-identical."""
+    q, kq, vq, ksc, vsc, bt = q8_case(seed=92)
+    lens = np.array([31, 9], dtype=np.int32)
+    o, l = oracle.attn_q8(q, kq, vq, ksc, vsc, bt, lens, 0.25, True, lib=lib)
+    perm = np.random.default_rng(93).permutation(9)      # new slot of old page p: perm[p]
+    inv = np.argsort(perm)
+    o2, l2 = oracle.attn_q8(q, kq[inv], vq[inv], ksc[inv], vsc[inv], perm[bt].astype(np.int32), lens,
+                            0.25, True, lib=lib)
+    return float(not (np.array_equal(o, o2) and np.array_equal(l, l2)))
+
+
+def check_q8_append(lib) -> float:
+    """Appended rows land at block_table[b][pos // page], row pos % page, as
+    the quantizer's codes; a rollback (lower start) overwrites from there and
+    leaves the rows past the new end as they were."""
+    B, Hkv, D, page, max_pages, num_pages = 2, 2, 16, 8, 4, 9
+    gen = np.random.default_rng(94)
+    bt = np.stack([gen.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
+    kq = np.zeros((num_pages, page, Hkv, D), np.int8)
+    vq = np.zeros_like(kq)
+    ksc = np.zeros((num_pages, page, Hkv), np.float32)
+    vsc = np.zeros_like(ksc)
+    g0 = synth.generator(95)
+    a_k, a_v = synth.bf16_normal((B, 6, Hkv, D), g0), synth.bf16_normal((B, 6, Hkv, D), g0)
+    b_k, b_v = synth.bf16_normal((B, 2, Hkv, D), g0), synth.bf16_normal((B, 2, Hkv, D), g0)
+    start = np.array([5, 27], dtype=np.int32)           # the second runs past capacity 32
+    oracle.q8_append(a_k, a_v, start, bt, kq, vq, ksc, vsc, lib=lib)
+    oracle.q8_append(b_k, b_v, start + 2, bt, kq, vq, ksc, vsc, lib=lib)   # rolled back to +2
+    worst = 0.0
+    for b in range(B):
+        for t, (src_k, src_v) in enumerate([(a_k[b, 0], a_v[b, 0]), (a_k[b, 1], a_v[b, 1]),
+                                            (b_k[b, 0], b_v[b, 0]), (b_k[b, 1], b_v[b, 1]),
+                                            (a_k[b, 4], a_v[b, 4]), (a_k[b, 5], a_v[b, 5])]):
+            pos = int(start[b]) + t
+            if pos >= page * max_pages:
+                continue
+            pg, r = bt[b, pos // page], pos % page
+            ck, sk = oracle.q8_quantize(src_k, lib=lib)
+            cv, sv = oracle.q8_quantize(src_v, lib=lib)
+            worst = max(worst, float(np.any(kq[pg, r] != ck)), float(np.any(ksc[pg, r] != sk)),
+                        float(np.any(vq[pg, r] != cv)), float(np.any(vsc[pg, r] != sv)))
+    untouched = np.ones(num_pages, bool)
+    untouched[bt.reshape(-1)] = False
+    worst = max(worst, float(np.any(kq[untouched] != 0)))
+    return worst
+
+
 ALL_CHECKS = {
     "sdpa_dense": check_sdpa_dense,
     "sdpa_mask": check_sdpa_mask,
@@ -302,4 +427,8 @@ ALL_CHECKS = {
     "head_permutation": check_head_permutation,
     "sdpa_steps": check_sdpa_steps,
     "steps_closed_forms": check_steps_closed_forms,
+    "q8_quantize": check_q8_quantize,
+    "q8_sdpa": check_q8_sdpa,
+    "q8_page_permutation": check_q8_page_permutation,
+    "q8_append": check_q8_append,
 }

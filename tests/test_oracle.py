@@ -103,6 +103,11 @@ MUTANTS = {
     "wrong_head_map": ("int g = h / G;", "int g = h % J->Hkv;"),
     "k_v_swapped": ("const uint16_t *krow = kv_row(J, J->k, J->k_step, b, g, vis[t]);",
                     "const uint16_t *krow = kv_row(J, J->v, J->v_step, b, g, vis[t]);"),
+    "q8_scale_step": ("*scale = amax / 127.0f;", "*scale = amax / 128.0f;"),
+    "q8_truncating_round": ("float c = nearbyintf(", "float c = truncf("),
+    "q8_page_row_swapped": ("size_t row = ((size_t)pg * J->page + (size_t)(j % J->page)) * J->Hkv + g;",
+                            "size_t row = ((size_t)pg * J->page + (size_t)(j / J->page)) * J->Hkv + g;"),
+    "q8_append_position": ("long long pos = s0 + t;", "long long pos = s0 + t + 1;"),
     "step_rows_off_by_one": ("for (int t = 0; t <= i; ++t) vis[n++]", "for (int t = 0; t < i; ++t) vis[n++]"),
     "step_rows_read_from_cache": (
         "return step + (((size_t)b * J->n_q + (size_t)(e - J->cap)) * J->Hkv + g) * (size_t)J->D;",
