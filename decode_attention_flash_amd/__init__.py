@@ -22,7 +22,8 @@ CK_MAX_NQ = 6
 CK_MAX_SPLITS = 256
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misaligned pointer",
           -4: "workspace missing or too small", -5: "HIP runtime error"}
-EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_workspace_size",
+EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
+           "ck_kv_append_q8", "ck_decode_attn_workspace_size",
            "ck_decode_attn_plan", "ck_status_string")
 
 
@@ -35,6 +36,12 @@ class CkError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("n_q", ctypes.c_int32), ("Hq", ctypes.c_int32),
                 ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("cap", ctypes.c_int32)]
+
+
+class Q8CacheC(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -75,6 +82,12 @@ def lib():
         L.ck_decode_attn_steps.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int,
                                            vp, vp, sz, ctypes.c_int, vp]
         L.ck_decode_attn_steps.restype = ctypes.c_int
+        qp = ctypes.POINTER(Q8CacheC)
+        L.ck_decode_attn_q8.argtypes = [sp, vp, qp, vp, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp,
+                                        vp, sz, ctypes.c_int, vp]
+        L.ck_decode_attn_q8.restype = ctypes.c_int
+        L.ck_kv_append_q8.argtypes = [sp, vp, vp, vp, qp, vp]
+        L.ck_kv_append_q8.restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
         L.ck_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -258,4 +271,97 @@ def decode_attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, *, scale: fl
                                     ctypes.c_void_p(st_handle))
     if st != 0:
         raise CkError(st, "ck_decode_attn_steps")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+class PagedQ8Cache:
+    """A paged INT8 KV cache in device memory: k/v codes int8 [num_pages,
+    page_tokens, Hkv, D], k/v scales fp32 [num_pages, page_tokens, Hkv], and a
+    block table int32 [B, max_pages] mapping each sequence's logical pages to
+    pool pages (see ck_q8_cache).  Pages are the caller's to assign; lowering
+    a sequence's kv_lens entry rolls it back."""
+
+    def __init__(self, num_pages: int, page_tokens: int, Hkv: int, D: int, block_table: torch.Tensor,
+                 device=None):
+        device = device or block_table.device
+        _check(block_table, "block_table", torch.int32)
+        if block_table.dim() != 2:
+            raise ValueError("block_table must be [B, max_pages]")
+        self.k_codes = torch.zeros((num_pages, page_tokens, Hkv, D), dtype=torch.int8, device=device)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_scales = torch.zeros((num_pages, page_tokens, Hkv), dtype=torch.float32, device=device)
+        self.v_scales = torch.zeros_like(self.k_scales)
+        self.block_table = block_table
+        self.page_tokens, self.num_pages, self.Hkv, self.D = page_tokens, num_pages, Hkv, D
+
+    @property
+    def B(self) -> int:
+        return self.block_table.shape[0]
+
+    @property
+    def max_pages(self) -> int:
+        return self.block_table.shape[1]
+
+    @property
+    def capacity(self) -> int:
+        return self.page_tokens * self.max_pages
+
+    def c_struct(self) -> Q8CacheC:
+        return Q8CacheC(self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_scales.data_ptr(),
+                        self.v_scales.data_ptr(), self.block_table.data_ptr(), self.page_tokens,
+                        self.max_pages, self.num_pages)
+
+
+def kv_append_q8(cache: PagedQ8Cache, k_new, v_new, start, stream=None):
+    """Quantize k_new / v_new [B, n_new, Hkv, D] bf16 into the cache at
+    positions start[b] + t (``ck_kv_append_q8``); start is int32 [B] on the
+    device (usually kv_lens, which the caller then advances)."""
+    _check(k_new, "k_new", torch.bfloat16)
+    _check(v_new, "v_new", torch.bfloat16)
+    _check(start, "start", torch.int32)
+    B, n_new, Hkv, D = k_new.shape
+    if tuple(v_new.shape) != tuple(k_new.shape) or (B, Hkv, D) != (cache.B, cache.Hkv, cache.D):
+        raise ValueError("k_new / v_new must be [B, n_new, Hkv, D] matching the cache")
+    shape = Shape(B, n_new, Hkv, Hkv, D, cache.capacity)
+    cs = cache.c_struct()
+    st_handle = stream if stream is not None else torch.cuda.current_stream(k_new.device).cuda_stream
+    st = lib().ck_kv_append_q8(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(start), ctypes.byref(cs),
+                               ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_kv_append_q8")
+
+
+def decode_attn_q8(q, cache: PagedQ8Cache, kv_lens, *, scale: float | None = None, causal: bool = False,
+                   out_dtype=torch.float32, out=None, lse=None, return_lse=False, workspace=None,
+                   num_splits: int = 0, stream=None):
+    """Decode attention over the paged INT8 cache (``ck_decode_attn_q8``)."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    _check(q, "q", torch.bfloat16)
+    _check(kv_lens, "kv_lens", torch.int32)
+    B, n_q, Hq, D = q.shape
+    if B != cache.B or D != cache.D:
+        raise ValueError("q and the cache disagree on B or D")
+    shape = Shape(B, n_q, Hq, cache.Hkv, D, cache.capacity)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _check(out, "out", out_dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check(lse, "lse", torch.float32)
+    odt = CK_DT_BF16 if out_dtype == torch.bfloat16 else CK_DT_F32
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = _cached_workspace(shape, 0, num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cs = cache.c_struct()
+    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().ck_decode_attn_q8(ctypes.byref(shape), _ptr(q), ctypes.byref(cs), _ptr(kv_lens),
+                                 ctypes.c_float(scale), 1 if causal else 0, _ptr(out), odt, _ptr(lse),
+                                 _ptr(workspace), ws_bytes, num_splits, ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn_q8")
     return (out, lse) if (return_lse or lse is not None) else out

@@ -75,6 +75,11 @@ struct Geo {
     static constexpr int RSK = 2 * D + 16;
     static constexpr int KBYTES = TT * RSK;
     static constexpr int STAGE = KBYTES + VBYTES;  // LDS bytes per wave
+    // Paged INT8 cache: 16-byte chunks of an int8 row, rows per load
+    // instruction, load instructions per tile.
+    static constexpr int CPR8 = D / 16;
+    static constexpr int RPI8 = 64 / CPR8;
+    static constexpr int VI8 = TT / RPI8;
 };
 
 struct KParams {
@@ -91,6 +96,13 @@ struct KParams {
     float* ws_o;
     float* ws_ml;
     int32_t* ws_cnt;  // per unit kCntStride ints: counters and slice claim flags
+    // paged INT8 cache (MODE 3)
+    const int8_t* kq;
+    const int8_t* vq;
+    const float* ksc;
+    const float* vsc;
+    const int32_t* block_table;  // [B, max_pages]
+    int32_t page, max_pages, num_pages;
     int32_t B, n_q, Hq, Hkv, G, cap;
     int32_t R, RG, rows_alloc;
     int32_t units;   // work units (grid = splits x units)
@@ -202,6 +214,19 @@ __device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float
     float mu = (m == -INFINITY) ? 0.f : m;
     w1 = fast_exp2(m1 - mu);
     w2 = fast_exp2(m2 - mu);
+}
+
+// 16 int8 codes to 16 bf16 values (exact: |code| <= 128 needs 8 significant
+// bits), as two 16-byte halves.
+__device__ __forceinline__ void i8x16_to_bf16(u32x4 w, u32x4& lo, u32x4& hi) {
+    bf16x8 a, c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(float)(int8_t)(w[e >> 2] >> (8 * (e & 3)));
+        c[e] = (__bf16)(float)(int8_t)(w[2 + (e >> 2)] >> (8 * (e & 3)));
+    }
+    lo = __builtin_bit_cast(u32x4, a);
+    hi = __builtin_bit_cast(u32x4, c);
 }
 
 // Bit e set where byte e of w is nonzero (4 keep_mask cells).
@@ -335,7 +360,8 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
     }
 }
 
-// MODE 0: dense, 1: dense with keep_mask, 2: gather.
+// MODE 0: dense, 1: dense with keep_mask, 2: gather, 3: dense over the paged
+// INT8 cache.
 template <int D, int RT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     using Gm = Geo<D>;
@@ -347,6 +373,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     __shared__ float s_ml[kWaves][RT][64][2];
     __shared__ bf16x8 q_lds[RT * KS * 64];
     __shared__ MergeScratch ms;
+    constexpr bool Q8 = (MODE == 3);
+    // per wave: the tile's K scales, V scales and reciprocal V scales
+    __shared__ float sc_lds[Q8 ? kWaves * 3 * TT : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -478,17 +507,51 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         const int pe = pos_begin + tile * TT + lane;
         return (tile < ntiles && lane < TT && pe < pos_end) ? list[pe] : -1;
     };
+    // Paged INT8 cache: page id of a tile, read one tile ahead of its loads.
+    auto page_of = [&](int tile) -> int {
+        return tile < ntiles ? p.block_table[(size_t)b * p.max_pages + (size_t)((pos_begin + tile * TT) / p.page)]
+                             : -1;
+    };
 
     // Issue the K and V loads (and mask loads) of one tile.  Load n of a lane
     // reads 16 bytes of cache row n*RPI + lane/CPR, so one instruction covers
     // RPI whole rows.
     u32x4 kraw[VI], vraw[VI];
+    u32x4 k8[Gm::VI8], v8[Gm::VI8];  // paged INT8 tile (MODE 3)
+    float ksv = 0.f, vsv = 0.f;       // scales of token `lane` of that tile
     uint32_t mraw[RT][MB];
     constexpr bool kDeferMask = !(D == 256 && RT == 2);
     uint64_t gvalid = 0;
     auto issue = [&](int tile, int jv) {
         const bool st_tile = steps && tile == ntiles_c;
         const int tb = st_tile ? 0 : pos_begin + tile * TT;
+        if constexpr (Q8) {
+            // jv is the tile's page id.  The tile lies in one page (pages hold a
+            // multiple of 64 tokens, tiles start at multiples of TT); the
+            // descriptors cover only its readable rows, and none of an id
+            // outside the pool, so such rows read as zero.
+            const int pg = __builtin_amdgcn_readfirstlane(jv);
+            const int nvalid = (pg >= 0 && pg < p.num_pages) ? min(TT, pos_end - tb) : 0;
+            const size_t prow = (size_t)(nvalid > 0 ? pg : 0) * p.page + (size_t)(tb % p.page);
+            const uint32_t rstride = (uint32_t)(p.Hkv * D);
+            const uint32_t cbytes = nvalid > 0 ? (uint32_t)(nvalid - 1) * rstride + D : 0u;
+            const uint32_t sbytes = nvalid > 0 ? (uint32_t)((nvalid - 1) * p.Hkv + 1) * 4u : 0u;
+            const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(p.kq + (prow * p.Hkv + g) * D, cbytes);
+            const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(p.vq + (prow * p.Hkv + g) * D, cbytes);
+            const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ksc + prow * p.Hkv + g, sbytes);
+            const __amdgpu_buffer_rsrc_t rvs8 = make_rsrc(p.vsc + prow * p.Hkv + g, sbytes);
+            constexpr int CPR8 = Gm::CPR8, RPI8 = Gm::RPI8;
+#pragma unroll
+            for (int n = 0; n < Gm::VI8; ++n)
+                k8[n] = bload128<2>(rk8, (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u);
+#pragma unroll
+            for (int n = 0; n < Gm::VI8; ++n)
+                v8[n] = bload128<2>(rv8, (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u);
+            const uint32_t soff = (uint32_t)(lane * p.Hkv) * 4u;
+            ksv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, soff, 0, 0));
+            vsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs8, soff, 0, 0));
+            return;
+        }
         uint32_t roff[VI];
         if constexpr (GATHER) {
             const bool ok = jv >= 0 && jv < lim_g;
@@ -542,8 +605,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     int jv_next = 0;
     if (wave < ntiles) {
         if constexpr (GATHER) jv_next = list_entry(wave);
+        if constexpr (Q8) jv_next = page_of(wave);
         issue(wave, jv_next);
         if constexpr (GATHER) jv_next = list_entry(wave + kWaves);
+        if constexpr (Q8) jv_next = page_of(wave + kWaves);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -564,12 +629,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         }
 
         // -- stage K and V rows in LDS, then send the next tile's loads -----
+        float* scw = sc_lds + (Q8 ? wave * 3 * TT : 0);
+        if constexpr (Q8) {
+            // int8 codes become bf16 in the same layout; the scales go beside.
+            constexpr int CPR8 = Gm::CPR8, RPI8 = Gm::RPI8;
 #pragma unroll
-        for (int n = 0; n < VI; ++n)
-            *reinterpret_cast<u32x4*>(klds + (n * RPI + lane / CPR) * RSK + (lane % CPR) * 16) = kraw[n];
+            for (int n = 0; n < Gm::VI8; ++n) {
+                const int row = n * RPI8 + lane / CPR8, c8 = lane % CPR8;
+                u32x4 lo, hi;
+                i8x16_to_bf16(k8[n], lo, hi);
+                *reinterpret_cast<u32x4*>(klds + row * RSK + c8 * 32) = lo;
+                *reinterpret_cast<u32x4*>(klds + row * RSK + c8 * 32 + 16) = hi;
+                i8x16_to_bf16(v8[n], lo, hi);
+                *reinterpret_cast<u32x4*>(vlds + row * RS + c8 * 32) = lo;
+                *reinterpret_cast<u32x4*>(vlds + row * RS + c8 * 32 + 16) = hi;
+            }
+            if (lane < TT) {
+                scw[lane] = ksv;
+                scw[TT + lane] = vsv;
+                scw[2 * TT + lane] = vsv > 0.f ? 1.f / vsv : 0.f;
+            }
+        } else {
 #pragma unroll
-        for (int n = 0; n < VI; ++n)
-            *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vraw[n];
+            for (int n = 0; n < VI; ++n)
+                *reinterpret_cast<u32x4*>(klds + (n * RPI + lane / CPR) * RSK + (lane % CPR) * 16) = kraw[n];
+#pragma unroll
+            for (int n = 0; n < VI; ++n)
+                *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vraw[n];
+        }
         wave_lds_sync();
         // The next tile's loads go out now, or after QK^T where the registers
         // of two row tiles at D = 256 would not hold them during it.
@@ -578,6 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         if (kEarly && next < ntiles) {
             issue(next, jv_next);
             if constexpr (GATHER) jv_next = list_entry(next + kWaves);
+            if constexpr (Q8) jv_next = page_of(next + kWaves);
         }
 
         // -- S^T = K Q^T ---------------------------------------------------
@@ -598,11 +686,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         if (!kEarly && next < ntiles) {
             issue(next, jv_next);
             if constexpr (GATHER) jv_next = list_entry(next + kWaves);
+            if constexpr (Q8) jv_next = page_of(next + kWaves);
         }
         if (tid == 0 && tile == 0 && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
 
         // -- online softmax (log2 domain) -----------------------------------
         bf16x8 pb[RT][KB];
+        // Paged INT8 cache: the K scale multiplies the score of its token, the
+        // V scale the probability that weights its codes.
+        // Each probability is rounded to bf16 after the V scale is applied;
+        // the denominator takes that rounded weight back over the scale, so
+        // the output stays a convex combination of the dequantized rows (one
+        // visible cell returns its row exactly).  A zero scale (zero row)
+        // keeps the plain rounded probability.
+        f32x4 kss[MB], vss[MB], ivs[MB];
+        if constexpr (Q8) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                kss[mb] = *reinterpret_cast<const f32x4*>(scw + 16 * mb + 4 * q4) * p.scale_log2;
+                vss[mb] = *reinterpret_cast<const f32x4*>(scw + TT + 16 * mb + 4 * q4);
+                ivs[mb] = *reinterpret_cast<const f32x4*>(scw + 2 * TT + 16 * mb + 4 * q4);
+            }
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int lim = GATHER ? 0 : min(lim_r[rt], pos_end);
@@ -620,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                         ok = st_tile ? (row_ok && off <= i_r[rt]) : tb + off < lim;
                         if constexpr (MODE == 1) ok = ok && ((tmbits[rt][mb] >> e) & 1u);
                     }
-                    const float x = ok ? sc[rt][mb][e] * p.scale_log2 : -INFINITY;
+                    const float x = ok ? sc[rt][mb][e] * (Q8 ? kss[mb][e] : p.scale_log2) : -INFINITY;
                     sc[rt][mb][e] = x;
                     mx = fmaxf(mx, x);
                 }
@@ -635,9 +740,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const __bf16 h = (__bf16)fast_exp2(sc[rt][mb][e] - mu);
-                    ph[mb][e] = h;
-                    lsum += (float)h;
+                    const float pe = fast_exp2(sc[rt][mb][e] - mu);
+                    if constexpr (Q8) {
+                        const __bf16 h = (__bf16)(pe * vss[mb][e]);
+                        ph[mb][e] = h;
+                        lsum += vss[mb][e] > 0.f ? (float)h * ivs[mb][e] : (float)(__bf16)pe;
+                    } else {
+                        const __bf16 h = (__bf16)pe;
+                        ph[mb][e] = h;
+                        lsum += (float)h;
+                    }
                 }
             st.l[rt] = st.l[rt] * alpha + lsum;
             st.m[rt] = m_new;
@@ -810,6 +922,67 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     }
 }
 
+// ---------------------------------------------------- paged INT8 append ----
+// One wave per (sequence, new token, KV head, K or V) row: the row's D bf16
+// values become int8 codes and one fp32 scale, in fp32 with the rounding the
+// format fixes (scale = amax / 127, code = x * (127 / amax) rounded half to
+// even, clamped to +-127; an all-zero row gets scale 0), and land in page
+// block_table[b][pos / page], row pos % page, with pos = clamp(start[b]) + t.
+// Rows past the capacity, or whose page id is outside the pool, are dropped.
+struct AppendParams {
+    const uint16_t* k_new;  // [B, n_new, Hkv, D] bf16
+    const uint16_t* v_new;
+    const int32_t* start;   // [B]
+    const int32_t* block_table;
+    int8_t* kq;
+    int8_t* vq;
+    float* ksc;
+    float* vsc;
+    int32_t B, n_new, Hkv, page, max_pages, num_pages;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void q8_append_kernel(const AppendParams p) {
+    constexpr int PER = D / 64;  // values per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t rows = (int64_t)p.B * p.n_new * p.Hkv * 2;
+    if (row_id >= rows) return;
+    const int which = (int)(row_id & 1);  // 0: K, 1: V
+    int64_t r = row_id >> 1;
+    const int g = (int)(r % p.Hkv);
+    r /= p.Hkv;
+    const int t = (int)(r % p.n_new);
+    const int b = (int)(r / p.n_new);
+    const int64_t cap = (int64_t)p.page * p.max_pages;
+    int64_t s0 = p.start[b];
+    s0 = s0 < 0 ? 0 : (s0 > cap ? cap : s0);
+    const int64_t pos = s0 + t;
+    if (pos >= cap) return;
+    const int32_t pg = p.block_table[(size_t)b * p.max_pages + (size_t)(pos / p.page)];
+    if (pg < 0 || pg >= p.num_pages) return;
+    const uint16_t* src = (which ? p.v_new : p.k_new) + (((size_t)b * p.n_new + t) * p.Hkv + g) * D;
+    float x[PER];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        x[e] = __uint_as_float((uint32_t)src[lane * PER + e] << 16);
+        amax = fmaxf(amax, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const size_t row = ((size_t)pg * p.page + (size_t)(pos % p.page)) * p.Hkv + g;
+    int8_t* dst = (which ? p.vq : p.kq) + row * D + lane * PER;
+    const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        float c = __builtin_rintf(x[e] * inv);
+        c = fminf(fmaxf(c, -127.f), 127.f);
+        dst[e] = (int8_t)(int)c;
+    }
+    if (lane == 0) (which ? p.vsc : p.ksc)[row] = amax > 0.f ? __fdiv_rn(amax, 127.f) : 0.f;
+}
+
 // ------------------------------------------------------------------ host ----
 
 constexpr int kWgPerCu = 1;
@@ -933,11 +1106,26 @@ static hipError_t launch_mode(int D, int RT, const KParams& kp, int grid, hipStr
 static int run(const ck_decode_shape* s, const void* q, const void* k, const void* v, const int32_t* kv_lens,
                const uint8_t* keep_mask, const int32_t* idx, int32_t W, int64_t idx_head_stride, float scale,
                int causal, void* out, int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
-               int num_splits, void* stream, const void* k_step = nullptr, const void* v_step = nullptr) {
+               int num_splits, void* stream, const void* k_step = nullptr, const void* v_step = nullptr,
+               const ck_q8_cache* q8 = nullptr) {
     if (!s) return CK_ERR_ARG;
     ck_decode_plan pl;
     int st = plan_impl(s, W, num_splits, 1, &pl);  // shape checks only
     if (st != CK_OK) return st;
+    if (q8) {
+        // The paged INT8 cache replaces k and v: check it and its pointers.
+        if (!q8->k_codes || !q8->v_codes || !q8->k_scales || !q8->v_scales || !q8->block_table)
+            return CK_ERR_ARG;
+        if (q8->page_tokens < 64 || q8->page_tokens % 64 != 0 || q8->max_pages < 1 || q8->num_pages < 1)
+            return CK_ERR_ARG;
+        if ((int64_t)q8->page_tokens * q8->max_pages != s->cap) return CK_ERR_ARG;
+        if ((int64_t)q8->page_tokens * s->Hkv * s->D >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+        if (!aligned(q8->k_codes, 16) || !aligned(q8->v_codes, 16) || !aligned(q8->k_scales, 4) ||
+            !aligned(q8->v_scales, 4) || !aligned(q8->block_table, 4))
+            return CK_ERR_ALIGN;
+        if (W > 0 || keep_mask || k_step) return CK_ERR_ARG;
+        k = v = q;  // not read in this mode
+    }
     if (!q || !k || !v || !kv_lens || !out) return CK_ERR_ARG;
     if ((k_step == nullptr) != (v_step == nullptr)) return CK_ERR_ARG;
     if (k_step && (W > 0 || keep_mask || causal)) return CK_ERR_ARG;
@@ -963,6 +1151,16 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     KParams kp{};
     kp.q = static_cast<const uint16_t*>(q);
     kp.k_step = static_cast<const uint16_t*>(k_step);
+    if (q8) {
+        kp.kq = static_cast<const int8_t*>(q8->k_codes);
+        kp.vq = static_cast<const int8_t*>(q8->v_codes);
+        kp.ksc = q8->k_scales;
+        kp.vsc = q8->v_scales;
+        kp.block_table = q8->block_table;
+        kp.page = q8->page_tokens;
+        kp.max_pages = q8->max_pages;
+        kp.num_pages = q8->num_pages;
+    }
     kp.v_step = static_cast<const uint16_t*>(v_step);
     kp.k = static_cast<const uint16_t*>(k);
     kp.v = static_cast<const uint16_t*>(v);
@@ -1008,7 +1206,9 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     const int grid = pl.units * pl.splits;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (W > 0)
+    if (q8)
+        e = launch_mode<3>(s->D, RT, kp, grid, hs);
+    else if (W > 0)
         e = launch_mode<2>(s->D, RT, kp, grid, hs);
     else if (keep_mask)
         e = launch_mode<1>(s->D, RT, kp, grid, hs);
@@ -1064,6 +1264,55 @@ int ck_decode_attn_steps(const ck_decode_shape* shape, const void* q, const void
     if (!k_step || !v_step) return CK_ERR_ARG;
     return ckda::run(shape, q, k_cache, v_cache, kv_lens, nullptr, nullptr, 0, 0, scale, 0, out, out_dtype, lse,
                      workspace, workspace_bytes, num_splits, stream, k_step, v_step);
+}
+
+int ck_decode_attn_q8(const ck_decode_shape* shape, const void* q, const ck_q8_cache* cache,
+                      const int32_t* kv_lens, float scale, int causal, void* out, int out_dtype, float* lse,
+                      void* workspace, size_t workspace_bytes, int num_splits, void* stream) {
+    if (!cache) return CK_ERR_ARG;
+    return ckda::run(shape, q, nullptr, nullptr, kv_lens, nullptr, nullptr, 0, 0, scale, causal, out, out_dtype, lse,
+                     workspace, workspace_bytes, num_splits, stream, nullptr, nullptr, cache);
+}
+
+int ck_kv_append_q8(const ck_decode_shape* shape, const void* k_new, const void* v_new, const int32_t* start,
+                    const ck_q8_cache* cache, void* stream) {
+    if (!shape || !cache || !k_new || !v_new || !start) return CK_ERR_ARG;
+    const ck_decode_shape& s = *shape;
+    if (s.B < 1 || s.n_q < 1 || s.Hkv < 1) return CK_ERR_ARG;
+    if (s.D != 128 && s.D != 256) return CK_ERR_UNSUPPORTED;
+    if (!cache->k_codes || !cache->v_codes || !cache->k_scales || !cache->v_scales || !cache->block_table)
+        return CK_ERR_ARG;
+    if (cache->page_tokens < 64 || cache->page_tokens % 64 != 0 || cache->max_pages < 1 || cache->num_pages < 1)
+        return CK_ERR_ARG;
+    if ((int64_t)cache->page_tokens * cache->max_pages != s.cap) return CK_ERR_ARG;
+    if (!ckda::aligned(k_new, 2) || !ckda::aligned(v_new, 2) || !ckda::aligned(start, 4) ||
+        !ckda::aligned(cache->k_scales, 4) || !ckda::aligned(cache->v_scales, 4) ||
+        !ckda::aligned(cache->block_table, 4))
+        return CK_ERR_ALIGN;
+    const int64_t rows = (int64_t)s.B * s.n_q * s.Hkv * 2;
+    const int64_t blocks = (rows + ckda::kWaves - 1) / ckda::kWaves;
+    if (blocks >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+    ckda::AppendParams ap{};
+    ap.k_new = static_cast<const uint16_t*>(k_new);
+    ap.v_new = static_cast<const uint16_t*>(v_new);
+    ap.start = start;
+    ap.block_table = cache->block_table;
+    ap.kq = static_cast<int8_t*>(cache->k_codes);
+    ap.vq = static_cast<int8_t*>(cache->v_codes);
+    ap.ksc = cache->k_scales;
+    ap.vsc = cache->v_scales;
+    ap.B = s.B;
+    ap.n_new = s.n_q;
+    ap.Hkv = s.Hkv;
+    ap.page = cache->page_tokens;
+    ap.max_pages = cache->max_pages;
+    ap.num_pages = cache->num_pages;
+    void* args[] = {&ap};
+    const void* fn = s.D == 128 ? reinterpret_cast<const void*>(&ckda::q8_append_kernel<128>)
+                                : reinterpret_cast<const void*>(&ckda::q8_append_kernel<256>);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(ckda::kThreads), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CK_OK : CK_ERR_HIP;
 }
 
 const char* ck_status_string(int status) {

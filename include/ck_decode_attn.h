@@ -178,6 +178,54 @@ int ck_decode_attn_steps(const ck_decode_shape* shape, const void* q, const void
                          const void* v_step, float scale, void* out, int out_dtype, float* lse,
                          void* workspace, size_t workspace_bytes, int num_splits, void* stream);
 
+/* Paged INT8 KV cache (comfy-kitchen PR "Performance improvements for qwen
+ * 3.x LLM (Part 1)", commit list: bounded paged INT8 decode cache with
+ * rollback; 8-bit KV caches are what the pages run, llama.cpp PR "qwen4exp:
+ * attend the selected cells instead of masking the window", Additional
+ * information).  Each (token, KV head) row of K and of V is D int8 codes with
+ * one fp32 scale: scale = amax / 127 and code = x * (127 / amax) rounded half
+ * to even and clamped to [-127, 127], in fp32 (an all-zero row has scale 0);
+ * the row's value is code * scale.  Token j of sequence b lives in page
+ * block_table[b * max_pages + j / page_tokens], row j % page_tokens.  Pages
+ * are owned by the caller: several sequences may share a page pool, and
+ * rolling a sequence back (rejected MTP drafts) is lowering its kv_lens
+ * entry, after which the next append overwrites from there.
+ *   k_codes, v_codes   : int8 [num_pages, page_tokens, Hkv, D], 16-byte aligned
+ *   k_scales, v_scales : fp32 [num_pages, page_tokens, Hkv], 4-byte aligned
+ *   block_table        : int32 [B, max_pages], device memory; an id outside
+ *                        [0, num_pages) is never dereferenced: the tokens it
+ *                        would hold read as zeros, appends to it are dropped
+ *   page_tokens        : a multiple of 64; shape->cap must equal
+ *                        page_tokens * max_pages (the logical capacity). */
+typedef struct ck_q8_cache {
+    void* k_codes;
+    void* v_codes;
+    float* k_scales;
+    float* v_scales;
+    const int32_t* block_table;
+    int32_t page_tokens;
+    int32_t max_pages;
+    int32_t num_pages;
+} ck_q8_cache;
+
+/* Dense decode (optionally the causal window) over the paged INT8 cache.
+ * Arguments as ck_decode_attn, with the cache in place of k_cache/v_cache
+ * (and no keep_mask); the workspace is the dense one (W = 0).  The tiles are
+ * dequantized exactly to bf16 codes, the K scale multiplies each score and
+ * the V scale each probability. */
+int ck_decode_attn_q8(const ck_decode_shape* shape, const void* q, const ck_q8_cache* cache,
+                      const int32_t* kv_lens, float scale, int causal, void* out, int out_dtype,
+                      float* lse, void* workspace, size_t workspace_bytes, int num_splits,
+                      void* stream);
+
+/* Quantize and append shape->n_q new tokens per sequence: k_new, v_new bf16
+ * [B, n_q, Hkv, D] (2-byte aligned) go to positions start[b] + t, with start
+ * (int32 [B], device memory, usually kv_lens) clamped to [0, cap]; rows past
+ * the capacity or in a page outside the pool are dropped.  shape->Hq is not
+ * used.  The caller advances kv_lens afterwards.  No workspace. */
+int ck_kv_append_q8(const ck_decode_shape* shape, const void* k_new, const void* v_new,
+                    const int32_t* start, const ck_q8_cache* cache, void* stream);
+
 /* Static text for a status code. */
 const char* ck_status_string(int status);
 

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "ck_decode_attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ck_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ck_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_exports():
@@ -151,3 +151,42 @@ def test_workspace_size_rejects_bad_shape():
     assert ck.lib().ck_decode_attn_workspace_size(ctypes.byref(shape(D=64)), 0, 0,
                                                    ctypes.byref(n)) == -2
     assert ck.lib().ck_decode_attn_workspace_size(ctypes.byref(shape()), 0, 0, None) == -1
+
+
+def _q8(page=64, max_pages=4, num_pages=8, codes=0x10000, scales=0x20000, table=0x30000):
+    return ck.Q8CacheC(codes, codes + 0x1000000, scales, scales + 0x1000000, table, page, max_pages, num_pages)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=48), -1), (dict(page=0), -1), (dict(max_pages=0), -1), (dict(num_pages=0), -1),
+    (dict(codes=0), -1), (dict(table=0), -1), (dict(codes=0x10008), -3), (dict(scales=0x20002), -3),
+])
+def test_q8_attention_rejects_bad_cache(kw, status):
+    """Checked on the host before any HIP call (pointers are never read)."""
+    c = _q8(**kw)
+    sh = shape(cap=c.page_tokens * c.max_pages)
+    st = ck.lib().ck_decode_attn_q8(ctypes.byref(sh), ctypes.c_void_p(0x40000), ctypes.byref(c),
+                                    ctypes.c_void_p(0x50000), ctypes.c_float(0.1), 0, ctypes.c_void_p(0x60000),
+                                    0, None, None, 0, 0, None)
+    assert st == status
+
+
+def test_q8_attention_capacity_must_match_pages():
+    c = _q8()
+    sh = shape(cap=c.page_tokens * c.max_pages + 1)
+    st = ck.lib().ck_decode_attn_q8(ctypes.byref(sh), ctypes.c_void_p(0x40000), ctypes.byref(c),
+                                    ctypes.c_void_p(0x50000), ctypes.c_float(0.1), 0, ctypes.c_void_p(0x60000),
+                                    0, None, None, 0, 0, None)
+    assert st == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), -2), (dict(n_q=0), -1), (dict(cap=100), -1), (dict(start=0), -1), (dict(start=0x50002), -3),
+])
+def test_q8_append_rejects(kw, status):
+    c = _q8()
+    start = kw.pop("start", 0x50000)
+    sh = shape(**{"cap": c.page_tokens * c.max_pages, **kw})
+    st = ck.lib().ck_kv_append_q8(ctypes.byref(sh), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x48000),
+                                  ctypes.c_void_p(start) if start else None, ctypes.byref(c), None)
+    assert st == status
