@@ -377,7 +377,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     // per wave: the tile's K scales, V scales and reciprocal V scales
     __shared__ float sc_lds[Q8 ? kWaves * 3 * TT : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform in its wave; saying so keeps everything
+    // derived from it (tile indices, descriptors chosen per tile) in scalar
+    // registers, so buffer loads never need a per-lane descriptor.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
     // Split-major numbering: every unit's first split comes first and the
     // (often inactive) high splits last.  Workgroups are dealt round-robin to
@@ -710,8 +713,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const int lim = GATHER ? 0 : min(lim_r[rt], pos_end);
             const bool row_ok = (rt * 16 + l16) < nrows;
+            // Tokens of this tile below lim_off are visible to the lane's row:
+            // the cache limit, or for the step tile the query's own index + 1.
+            const int lim_off = GATHER ? 0
+                                       : (st_tile ? (row_ok ? i_r[rt] + 1 : 0) : min(lim_r[rt], pos_end) - tb);
             float mx = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -722,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                     if constexpr (GATHER) {
                         ok = row_ok && ((tvalid >> off) & 1ull);
                     } else {
-                        ok = st_tile ? (row_ok && off <= i_r[rt]) : tb + off < lim;
+                        ok = off < lim_off;
                         if constexpr (MODE == 1) ok = ok && ((tmbits[rt][mb] >> e) & 1u);
                     }
                     const float x = ok ? sc[rt][mb][e] * (Q8 ? kss[mb][e] : p.scale_log2) : -INFINITY;
