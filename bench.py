@@ -138,6 +138,51 @@ def steps_case(stack, n_q, Hq, Hkv, D, L, steps, warmup, n_layers=None):
                 frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
 
 
+class Q8Stack:
+    """`n` layers of paged INT8 caches (random codes and scales, the block
+    tables a random permutation of each layer's pool), on the device."""
+
+    def __init__(self, n, B, cap, Hkv, D, page, seed):
+        import torch
+        import decode_attention_flash_amd as ck
+        self.caches = []
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        max_pages = (cap + page - 1) // page
+        for _ in range(n):
+            perm = torch.randperm(B * max_pages, generator=g, device="cuda").to(torch.int32)
+            c = ck.PagedQ8Cache(B * max_pages, page, Hkv, D, perm.view(B, max_pages))
+            c.k_codes.copy_(torch.randint(-127, 128, c.k_codes.shape, generator=g, device="cuda",
+                                          dtype=torch.int8))
+            c.v_codes.copy_(torch.randint(-127, 128, c.v_codes.shape, generator=g, device="cuda",
+                                          dtype=torch.int8))
+            c.k_scales.uniform_(0.005, 0.03, generator=g)
+            c.v_scales.uniform_(0.005, 0.03, generator=g)
+            self.caches.append(c)
+
+
+def q8_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_layers=None):
+    """Decode over the paged INT8 cache (decode_attn_q8); bytes read are the
+    int8 codes plus one fp32 scale per token row, for K and V."""
+    import torch
+    import decode_attention_flash_amd as ck
+    from decode_attention_flash_amd import synth
+    kv_bytes = int(sum(2 * Hkv * (D + 4) * int(L) for L in lens))
+    n = min(n_layers or layers_for(kv_bytes), len(stack.caches))
+    qs = [synth.queries(B, n_q, Hq, D, 13 + l, device="cuda") for l in range(n)]
+    outs = [torch.empty((B, n_q, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
+    c0 = stack.caches[0]
+    ws = ck.new_workspace(ck.Shape(B, n_q, Hq, Hkv, D, c0.capacity))
+
+    def launch(l):
+        ck.decode_attn_q8(qs[l], stack.caches[l], lens_d, causal=causal, out=outs[l], workspace=ws)
+
+    ms, us = time_graph(launch, n, steps, warmup)
+    return dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, kv_gbs=kv_bytes / us / 1e3,
+                frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
+
+
 def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None):
     import numpy as np
     import torch
@@ -315,6 +360,26 @@ def main():
             sweep["sparse"].append(dict(n_kv=n_kv, gather=rg, masked=rm))
             del st, masks
             torch.cuda.empty_cache()
+
+    if not args.headline_only:
+        # paged INT8 cache: the same head_dim-256 layer and the ragged batch
+        sweep["q8_kv_len"] = []
+        n_q8 = max(layers_for(2 * Hkv * (D + 4) * L) for L in lens_sweep)
+        qst = Q8Stack(n_q8, 1, cap, Hkv, D, 128, 3001)
+        for L in lens_sweep:
+            r = q8_case(qst, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup)
+            log(f"int8 pages kv_len {L}: {r['us']:.2f} us, {r['kv_gbs']:.0f} GB/s")
+            sweep["q8_kv_len"].append(dict(kv_len=L, page=128, **r))
+        del qst
+        torch.cuda.empty_cache()
+        from decode_attention_flash_amd import synth
+        lens = synth.ragged_lens(32, 512, 32768, 4000)
+        qst = Q8Stack(4, 32, 32768, 8, 128, 128, 3004)
+        r = q8_case(qst, 32, 1, 32, 8, 128, lens.tolist(), max(3, args.steps // 4), 2, n_layers=4)
+        log(f"int8 pages ragged B=32: {r['us']:.1f} us, {r['kv_gbs']:.0f} GB/s")
+        sweep["q8_ragged_batch"] = dict(B=32, sum_kv_len=int(lens.sum()), page=128, **r)
+        del qst
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu and not args.headline_only:

@@ -275,8 +275,8 @@ def decode_attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, *, scale: fl
 
 
 class PagedQ8Cache:
-    """A paged INT8 KV cache in device memory: k/v codes int8 [num_pages,
-    page_tokens, Hkv, D], k/v scales fp32 [num_pages, page_tokens, Hkv], and a
+    """A paged INT8 KV cache in device memory: k/v codes int8 [num_pages, Hkv,
+    page_tokens, D], k/v scales fp32 [num_pages, Hkv, page_tokens], and a
     block table int32 [B, max_pages] mapping each sequence's logical pages to
     pool pages (see ck_q8_cache).  Pages are the caller's to assign; lowering
     a sequence's kv_lens entry rolls it back."""
@@ -287,9 +287,9 @@ class PagedQ8Cache:
         _check(block_table, "block_table", torch.int32)
         if block_table.dim() != 2:
             raise ValueError("block_table must be [B, max_pages]")
-        self.k_codes = torch.zeros((num_pages, page_tokens, Hkv, D), dtype=torch.int8, device=device)
+        self.k_codes = torch.zeros((num_pages, Hkv, page_tokens, D), dtype=torch.int8, device=device)
         self.v_codes = torch.zeros_like(self.k_codes)
-        self.k_scales = torch.zeros((num_pages, page_tokens, Hkv), dtype=torch.float32, device=device)
+        self.k_scales = torch.zeros((num_pages, Hkv, page_tokens), dtype=torch.float32, device=device)
         self.v_scales = torch.zeros_like(self.k_scales)
         self.block_table = block_table
         self.page_tokens, self.num_pages, self.Hkv, self.D = page_tokens, num_pages, Hkv, D

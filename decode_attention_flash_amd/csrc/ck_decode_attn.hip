@@ -510,10 +510,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         const int pe = pos_begin + tile * TT + lane;
         return (tile < ntiles && lane < TT && pe < pos_end) ? list[pe] : -1;
     };
-    // Paged INT8 cache: page id of a tile, read one tile ahead of its loads.
+    // Paged INT8 cache: page id of a tile, read one tile ahead of its loads
+    // with a vector-memory load (a scalar load would be counted with the LDS
+    // accesses, and every LDS wait would then also wait for it).  Past the
+    // table the load reads 0; such tiles are past the split and read nothing.
+    const __amdgpu_buffer_rsrc_t rbt =
+        make_rsrc(Q8 ? p.block_table + (size_t)b * p.max_pages : p.kv_lens, Q8 ? (uint32_t)p.max_pages * 4u : 0u);
     auto page_of = [&](int tile) -> int {
-        return tile < ntiles ? p.block_table[(size_t)b * p.max_pages + (size_t)((pos_begin + tile * TT) / p.page)]
-                             : -1;
+        const uint32_t idx = (uint32_t)((pos_begin + tile * TT) / (Q8 ? p.page : 1));
+        return __builtin_amdgcn_raw_buffer_load_b32(rbt, idx * 4u, 0, 0);
     };
 
     // Issue the K and V loads (and mask loads) of one tile.  Load n of a lane
@@ -533,16 +538,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
             // multiple of 64 tokens, tiles start at multiples of TT); the
             // descriptors cover only its readable rows, and none of an id
             // outside the pool, so such rows read as zero.
+            // (Every value that shapes a descriptor goes through readfirstlane:
+            // left to itself the compiler may compute one of them with vector
+            // instructions, and a descriptor in vector registers makes it wrap
+            // each load in a loop over the lanes.)
             const int pg = __builtin_amdgcn_readfirstlane(jv);
-            const int nvalid = (pg >= 0 && pg < p.num_pages) ? min(TT, pos_end - tb) : 0;
-            const size_t prow = (size_t)(nvalid > 0 ? pg : 0) * p.page + (size_t)(tb % p.page);
-            const uint32_t rstride = (uint32_t)(p.Hkv * D);
-            const uint32_t cbytes = nvalid > 0 ? (uint32_t)(nvalid - 1) * rstride + D : 0u;
-            const uint32_t sbytes = nvalid > 0 ? (uint32_t)((nvalid - 1) * p.Hkv + 1) * 4u : 0u;
-            const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(p.kq + (prow * p.Hkv + g) * D, cbytes);
-            const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(p.vq + (prow * p.Hkv + g) * D, cbytes);
-            const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ksc + prow * p.Hkv + g, sbytes);
-            const __amdgpu_buffer_rsrc_t rvs8 = make_rsrc(p.vsc + prow * p.Hkv + g, sbytes);
+            const int nvalid = __builtin_amdgcn_readfirstlane(
+                (pg >= 0 && pg < p.num_pages) ? max(0, min(TT, pos_end - tb)) : 0);
+            const int prow_page = __builtin_amdgcn_readfirstlane(nvalid > 0 ? pg : 0);
+            // pages are [Hkv][page][D]: the tile's rows of head g are contiguous
+            const size_t prow = ((size_t)prow_page * p.Hkv + g) * p.page + (size_t)(tb % p.page);
+            const uint32_t rstride = (uint32_t)D;
+            const uint32_t cbytes =
+                (uint32_t)__builtin_amdgcn_readfirstlane(nvalid > 0 ? (int)((uint32_t)(nvalid - 1) * rstride + D) : 0);
+            const uint32_t sbytes = (uint32_t)__builtin_amdgcn_readfirstlane(nvalid * 4);
+            const __amdgpu_buffer_rsrc_t rk8 = make_rsrc(p.kq + prow * D, cbytes);
+            const __amdgpu_buffer_rsrc_t rv8 = make_rsrc(p.vq + prow * D, cbytes);
+            const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ksc + prow, sbytes);
+            const __amdgpu_buffer_rsrc_t rvs8 = make_rsrc(p.vsc + prow, sbytes);
             constexpr int CPR8 = Gm::CPR8, RPI8 = Gm::RPI8;
 #pragma unroll
             for (int n = 0; n < Gm::VI8; ++n)
@@ -550,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
 #pragma unroll
             for (int n = 0; n < Gm::VI8; ++n)
                 v8[n] = bload128<2>(rv8, (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u);
-            const uint32_t soff = (uint32_t)(lane * p.Hkv) * 4u;
+            const uint32_t soff = (uint32_t)lane * 4u;
             ksv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, soff, 0, 0));
             vsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs8, soff, 0, 0));
             return;
@@ -977,7 +990,7 @@ __global__ __launch_bounds__(kThreads) void q8_append_kernel(const AppendParams 
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const size_t row = ((size_t)pg * p.page + (size_t)(pos % p.page)) * p.Hkv + g;
+    const size_t row = ((size_t)pg * p.Hkv + g) * p.page + (size_t)(pos % p.page);
     int8_t* dst = (which ? p.vq : p.kq) + row * D + lane * PER;
     const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
 #pragma unroll

@@ -186,12 +186,14 @@ int ck_decode_attn_steps(const ck_decode_shape* shape, const void* q, const void
  * one fp32 scale: scale = amax / 127 and code = x * (127 / amax) rounded half
  * to even and clamped to [-127, 127], in fp32 (an all-zero row has scale 0);
  * the row's value is code * scale.  Token j of sequence b lives in page
- * block_table[b * max_pages + j / page_tokens], row j % page_tokens.  Pages
+ * block_table[b * max_pages + j / page_tokens], row j % page_tokens of its
+ * KV head's block: a page is [Hkv][page_tokens][D], so a head's rows in a
+ * page are one contiguous run (the pages leave the layout open).  Pages
  * are owned by the caller: several sequences may share a page pool, and
  * rolling a sequence back (rejected MTP drafts) is lowering its kv_lens
  * entry, after which the next append overwrites from there.
- *   k_codes, v_codes   : int8 [num_pages, page_tokens, Hkv, D], 16-byte aligned
- *   k_scales, v_scales : fp32 [num_pages, page_tokens, Hkv], 4-byte aligned
+ *   k_codes, v_codes   : int8 [num_pages, Hkv, page_tokens, D], 16-byte aligned
+ *   k_scales, v_scales : fp32 [num_pages, Hkv, page_tokens], 4-byte aligned
  *   block_table        : int32 [B, max_pages], device memory; an id outside
  *                        [0, num_pages) is never dereferenced: the tokens it
  *                        would hold read as zeros, appends to it are dropped

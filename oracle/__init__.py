@@ -190,18 +190,18 @@ def q8_quantize(x, lib=None):
 
 def q8_append(k_new, v_new, start, block_table, kq, vq, ksc, vsc, lib=None):
     """Quantize k_new / v_new [B, n_new, Hkv, D] (bf16) into the paged cache
-    (kq, vq int8 [num_pages, page, Hkv, D]; ksc, vsc float32 [num_pages,
-    page, Hkv]; numpy arrays updated in place) at positions start[b] + t."""
+    (kq, vq int8 [num_pages, Hkv, page, D]; ksc, vsc float32 [num_pages,
+    Hkv, page]; numpy arrays updated in place) at positions start[b] + t."""
     lib = lib or load()
     kb, vb = _bits(k_new), _bits(v_new)
     B, n_new, Hkv, D = kb.shape
-    num_pages, page = kq.shape[0], kq.shape[1]
+    num_pages, page = kq.shape[0], kq.shape[2]
     bt = _np(block_table, np.int32)
     st = _np(start, np.int32).reshape(-1)
     for a, dt in ((kq, np.int8), (vq, np.int8), (ksc, np.float32), (vsc, np.float32)):
         if a.dtype != dt or not a.flags.c_contiguous:
             raise ValueError("paged cache arrays must be contiguous int8 / float32")
-    if kq.shape != (num_pages, page, Hkv, D) or vq.shape != kq.shape or ksc.shape != kq.shape[:3] \
+    if kq.shape != (num_pages, Hkv, page, D) or vq.shape != kq.shape or ksc.shape != kq.shape[:3] \
             or vsc.shape != ksc.shape or bt.shape[0] != B or st.shape[0] != B:
         raise ValueError("paged cache shape mismatch")
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
@@ -213,7 +213,8 @@ def q8_append(k_new, v_new, start, block_table, kq, vq, ksc, vsc, lib=None):
 
 def attn_q8(q, kq, vq, ksc, vsc, block_table, kv_lens, scale: float, causal: bool = False,
             num_splits: int = 0, nthreads: int = 0, lib=None):
-    """Attention over the paged INT8 cache (cell j of sequence b in page
+    """Attention over the paged INT8 cache (kq/vq [num_pages, Hkv, page, D],
+    ksc/vsc [num_pages, Hkv, page]; cell j of sequence b in page
     block_table[b, j // page], value code * scale).  q [B, n_q, Hq, D] bf16.
     Returns (out [B, n_q, Hq, D] float64, lse [B, n_q, Hq] float64)."""
     lib = lib or load()
@@ -221,7 +222,7 @@ def attn_q8(q, kq, vq, ksc, vsc, block_table, kv_lens, scale: float, causal: boo
     B, n_q, Hq, D = qb.shape
     kq, vq = _np(kq, np.int8), _np(vq, np.int8)
     ksc, vsc = _np(ksc, np.float32), _np(vsc, np.float32)
-    num_pages, page, Hkv, Dk = kq.shape
+    num_pages, Hkv, page, Dk = kq.shape
     bt = _np(block_table, np.int32)
     if Dk != D or vq.shape != kq.shape or ksc.shape != kq.shape[:3] or vsc.shape != ksc.shape:
         raise ValueError("paged cache shape mismatch")

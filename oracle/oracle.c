@@ -61,7 +61,9 @@
  * with rollback; the pages run 8-bit KV caches throughout, llama.cpp PR
  * "qwen4exp: attend the selected cells instead of masking the window",
  * Additional information).  Cell j of sequence b lives in page
- * block_table[b][j / page], row j % page; its value is code * scale, taken
+ * block_table[b][j / page], row j % page of its KV head's block (a page is
+ * [Hkv][page][D], so a head's rows in a page are contiguous; the pages leave
+ * the layout open); its value is code * scale, taken
  * exactly in fp64, and the definition above applies unchanged.  A cell whose
  * page id is outside [0, num_pages) reads as zeros.  Rows are quantized in
  * fp32 (ck_oracle_q8_quantize_row): scale = amax / 127, code = x * (127 /
@@ -127,7 +129,7 @@ static void q8_row(const job_t *J, const int8_t *codes, const float *scales, int
         for (int d = 0; d < J->D; ++d) dst[d] = 0.0;
         return;
     }
-    size_t row = ((size_t)pg * J->page + (size_t)(j % J->page)) * J->Hkv + g;
+    size_t row = ((size_t)pg * J->Hkv + g) * J->page + (size_t)(j % J->page);
     double sc = (double)scales[row];
     for (int d = 0; d < J->D; ++d) dst[d] = (double)codes[row * J->D + d] * sc;
 }
@@ -332,7 +334,7 @@ int ck_oracle_attn_steps(int B, int n_q, int Hq, int Hkv, int D, int cap, const 
 
 /*
  * Attention over the paged INT8 cache: q [B, n_q, Hq, D] bf16; kq/vq int8
- * [num_pages, page, Hkv, D]; ksc/vsc fp32 [num_pages, page, Hkv];
+ * [num_pages, Hkv, page, D]; ksc/vsc fp32 [num_pages, Hkv, page];
  * block_table int32 [B, max_pages]; kv_lens [B] clamped to
  * [0, max_pages * page].  Dense and causal windows as ck_oracle_attn.
  */
@@ -404,7 +406,7 @@ int ck_oracle_q8_append(int B, int n_new, int Hkv, int D, int page, int max_page
             int32_t pg = block_table[(size_t)b * max_pages + (size_t)(pos / page)];
             if (pg < 0 || pg >= num_pages) continue;
             for (int g = 0; g < Hkv; ++g) {
-                size_t row = ((size_t)pg * page + (size_t)(pos % page)) * Hkv + g;
+                size_t row = ((size_t)pg * Hkv + g) * page + (size_t)(pos % page);
                 size_t src = (((size_t)b * n_new + t) * Hkv + g) * (size_t)D;
                 ck_oracle_q8_quantize_row(D, k_new + src, kq + row * D, ksc + row);
                 ck_oracle_q8_quantize_row(D, v_new + src, vq + row * D, vsc + row);

@@ -327,22 +327,22 @@ def check_q8_quantize(lib) -> float:
 
 def q8_case(B=2, n_q=3, Hq=4, Hkv=2, D=16, page=8, max_pages=4, num_pages=9, seed=91):
     gen = np.random.default_rng(seed)
-    kq = gen.integers(-127, 128, size=(num_pages, page, Hkv, D)).astype(np.int8)
-    vq = gen.integers(-127, 128, size=(num_pages, page, Hkv, D)).astype(np.int8)
-    ksc = (gen.random((num_pages, page, Hkv)) * 0.05 + 0.001).astype(np.float32)
-    vsc = (gen.random((num_pages, page, Hkv)) * 0.05 + 0.001).astype(np.float32)
+    kq = gen.integers(-127, 128, size=(num_pages, Hkv, page, D)).astype(np.int8)
+    vq = gen.integers(-127, 128, size=(num_pages, Hkv, page, D)).astype(np.int8)
+    ksc = (gen.random((num_pages, Hkv, page)) * 0.05 + 0.001).astype(np.float32)
+    vsc = (gen.random((num_pages, Hkv, page)) * 0.05 + 0.001).astype(np.float32)
     bt = np.stack([gen.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
     q = synth.queries(B, n_q, Hq, D, seed)
     return q, kq, vq, ksc, vsc, bt
 
 
 def q8_dense(codes, scales, bt, num_pages):
-    """[B, max_pages * page, Hkv, D] float64 view of the pages through the
-    block table (invalid page ids give zeros)."""
+    """[B, max_pages * page, Hkv, D] float64 view of the pages ([num_pages,
+    Hkv, page, D]) through the block table (invalid page ids give zeros)."""
     B, max_pages = bt.shape
-    page = codes.shape[1]
-    vals = codes.astype(np.float64) * scales.astype(np.float64)[..., None]
-    out = np.zeros((B, max_pages * page) + codes.shape[2:], dtype=np.float64)
+    page = codes.shape[2]
+    vals = (codes.astype(np.float64) * scales.astype(np.float64)[..., None]).transpose(0, 2, 1, 3)
+    out = np.zeros((B, max_pages * page, codes.shape[1], codes.shape[3]), dtype=np.float64)
     for b in range(B):
         for lp in range(max_pages):
             pg = bt[b, lp]
@@ -387,9 +387,9 @@ def check_q8_append(lib) -> float:
     B, Hkv, D, page, max_pages, num_pages = 2, 2, 16, 8, 4, 9
     gen = np.random.default_rng(94)
     bt = np.stack([gen.permutation(num_pages)[:max_pages] for _ in range(B)]).astype(np.int32)
-    kq = np.zeros((num_pages, page, Hkv, D), np.int8)
+    kq = np.zeros((num_pages, Hkv, page, D), np.int8)
     vq = np.zeros_like(kq)
-    ksc = np.zeros((num_pages, page, Hkv), np.float32)
+    ksc = np.zeros((num_pages, Hkv, page), np.float32)
     vsc = np.zeros_like(ksc)
     g0 = synth.generator(95)
     a_k, a_v = synth.bf16_normal((B, 6, Hkv, D), g0), synth.bf16_normal((B, 6, Hkv, D), g0)
@@ -408,8 +408,8 @@ def check_q8_append(lib) -> float:
             pg, r = bt[b, pos // page], pos % page
             ck, sk = oracle.q8_quantize(src_k, lib=lib)
             cv, sv = oracle.q8_quantize(src_v, lib=lib)
-            worst = max(worst, float(np.any(kq[pg, r] != ck)), float(np.any(ksc[pg, r] != sk)),
-                        float(np.any(vq[pg, r] != cv)), float(np.any(vsc[pg, r] != sv)))
+            worst = max(worst, float(np.any(kq[pg, :, r] != ck)), float(np.any(ksc[pg, :, r] != sk)),
+                        float(np.any(vq[pg, :, r] != cv)), float(np.any(vsc[pg, :, r] != sv)))
     untouched = np.ones(num_pages, bool)
     untouched[bt.reshape(-1)] = False
     worst = max(worst, float(np.any(kq[untouched] != 0)))

@@ -17,8 +17,8 @@ pytestmark = pytest.mark.gpu
 
 
 def host_pages(num_pages, page, Hkv, D):
-    kq = np.zeros((num_pages, page, Hkv, D), np.int8)
-    ksc = np.zeros((num_pages, page, Hkv), np.float32)
+    kq = np.zeros((num_pages, Hkv, page, D), np.int8)
+    ksc = np.zeros((num_pages, Hkv, page), np.float32)
     return kq, kq.copy(), ksc, ksc.copy()
 
 

@@ -105,8 +105,10 @@ MUTANTS = {
                     "const uint16_t *krow = kv_row(J, J->v, J->v_step, b, g, vis[t]);"),
     "q8_scale_step": ("*scale = amax / 127.0f;", "*scale = amax / 128.0f;"),
     "q8_truncating_round": ("float c = nearbyintf(", "float c = truncf("),
-    "q8_page_row_swapped": ("size_t row = ((size_t)pg * J->page + (size_t)(j % J->page)) * J->Hkv + g;",
-                            "size_t row = ((size_t)pg * J->page + (size_t)(j / J->page)) * J->Hkv + g;"),
+    "q8_page_row_swapped": ("size_t row = ((size_t)pg * J->Hkv + g) * J->page + (size_t)(j % J->page);",
+                            "size_t row = ((size_t)pg * J->Hkv + g) * J->page + (size_t)(j / J->page);"),
+    "q8_token_major_page": ("size_t row = ((size_t)pg * J->Hkv + g) * J->page + (size_t)(j % J->page);",
+                            "size_t row = ((size_t)pg * J->page + (size_t)(j % J->page)) * J->Hkv + g;"),
     "q8_append_position": ("long long pos = s0 + t;", "long long pos = s0 + t + 1;"),
     "step_rows_off_by_one": ("for (int t = 0; t <= i; ++t) vis[n++]", "for (int t = 0; t < i; ++t) vis[n++]"),
     "step_rows_read_from_cache": (
