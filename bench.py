@@ -183,7 +183,9 @@ def q8_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_laye
                 frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
 
 
-def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None):
+def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None, block=0):
+    """Gather over per-layer top-k lists of W_sel cells plus the tail: cells
+    drawn one by one, or (block > 0) as W_sel / block aligned runs."""
     import numpy as np
     import torch
     import decode_attention_flash_amd as ck
@@ -194,8 +196,12 @@ def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None):
     n = min(n_layers or layers_for(kv_bytes), len(stack.k))
     qs = [synth.queries(B, n_q, Hq, D, 11 + l, device="cuda") for l in range(n)]
     outs = [torch.empty((B, n_q, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n)]
-    idxs = [torch.from_numpy(synth.topk_lists(B, n_q, Hkv, n_kv, W_sel, tail, seed=5000 + n_kv + l))
-            .to("cuda") for l in range(n)]
+    def lists(l):
+        if block:
+            return synth.block_lists(B, n_q, Hkv, n_kv, W_sel // block, block, tail, seed=5100 + n_kv + l)
+        return synth.topk_lists(B, n_q, Hkv, n_kv, W_sel, tail, seed=5000 + n_kv + l)
+
+    idxs = [torch.from_numpy(lists(l)).to("cuda") for l in range(n)]
     lens_d = torch.full((B,), n_kv, dtype=torch.int32, device="cuda")
     shape = ck.shape_of(qs[0], stack.k[0])
     ws = ck.new_workspace(shape, W=W)

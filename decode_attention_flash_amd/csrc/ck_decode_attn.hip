@@ -45,6 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer descriptor, dword data format
 constexpr uint32_t kOOB = 0x80000000u;        // an offset beyond every range we build
+constexpr int kMaxQueries = CK_MAX_NQ;         // query rows per sequence (n_q)
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -114,6 +115,7 @@ struct KParams {
     float scale_log2;         // softmax scale times log2(e)
     int32_t causal, out_bf16;
     int32_t mask_dw;     // keep_mask rows start 4-byte aligned: read 4 cells per load
+    int32_t mask_skip;   // keep_mask rows start 16-byte aligned: tiles without a kept cell are skipped
     uint32_t row_bytes;  // bytes between consecutive positions of one head
 };
 
@@ -614,15 +616,66 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rvt, roff[n] + coff);
     };
 
+    // keep_mask: tiles that hold no kept cell of the workgroup's mask rows
+    // are skipped, with neither K/V traffic nor arithmetic (they would add
+    // exact zeros).  The split's tiles are taken in windows of 64: lane l
+    // reads the mask cells of tile l of the window for every mask row and one
+    // ballot gives the window's tile bitmap.  Every wave computes the same
+    // bitmap and takes every kWaves-th set bit, so the waves share the kept
+    // tiles evenly however they cluster.  When rows are not 16-byte aligned
+    // every tile counts as kept.
+    const int i_lo = row0 / p.G, i_hi = (row0 + nrows - 1) / p.G;
+    auto window_bits = [&](int w) -> uint64_t {
+        const int tile = 64 * w + lane;
+        const bool in = tile < ntiles_c;
+        if (!p.mask_skip) return __ballot(in);
+        // All rows' loads go out before the first is used (one round trip).
+        u32x4 x[kMaxQueries][TT / 16];
+#pragma unroll
+        for (int k = 0; k < kMaxQueries; ++k) {
+            const uint32_t base =
+                (uint32_t)((i_lo + k) * p.Hkv + g) * (uint32_t)p.cap + (uint32_t)(pos_begin + tile * TT);
+#pragma unroll
+            for (int c = 0; c < TT / 16; ++c)
+                x[k][c] = k <= i_hi - i_lo ? bload128(rm, in ? base + 16u * c : kOOB) : u32x4{0u, 0u, 0u, 0u};
+        }
+        uint32_t any = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxQueries; ++k)
+#pragma unroll
+            for (int c = 0; c < TT / 16; ++c) any |= x[k][c][0] | x[k][c][1] | x[k][c][2] | x[k][c][3];
+        return __ballot(in && any != 0);
+    };
+    uint64_t tbits = 0;  // set bits: kept tiles of window `twin` not yet passed
+    int twin = 0;
+    // Drops the k lowest kept tiles still ahead, then returns the lowest one
+    // left (ntiles when none): k = wave gives the wave's first tile, k =
+    // kWaves its next.  Wave-uniform scalar work, except one mask round trip
+    // per window crossed.
+    auto pick = [&](int k) -> int {
+        for (;;) {
+            for (; k > 0 && tbits != 0; --k) tbits &= tbits - 1;
+            if (tbits != 0) return 64 * twin + __builtin_ctzll(tbits);
+            if (64 * (twin + 1) >= ntiles_c) return ntiles;
+            ++twin;
+            tbits = window_bits(twin);
+        }
+    };
+
     // Query fragments to LDS before the first tile's loads are issued (they
     // arrived with the length), then an LDS-only barrier after the issue.
 #pragma unroll
     for (int u = 0; u < QF; ++u) q_lds[tid + u * kThreads] = qfrag[u];
     int jv_next = 0;
-    if (wave < ntiles) {
+    int first = wave;
+    if constexpr (MODE == 1) {
+        tbits = window_bits(0);
+        first = pick(wave);
+    }
+    if (first < ntiles) {
         if constexpr (GATHER) jv_next = list_entry(wave);
         if constexpr (Q8) jv_next = page_of(wave);
-        issue(wave, jv_next);
+        issue(first, jv_next);
         if constexpr (GATHER) jv_next = list_entry(wave + kWaves);
         if constexpr (Q8) jv_next = page_of(wave + kWaves);
     }
@@ -630,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-    for (int tile = wave; tile < ntiles; tile += kWaves) {
+    for (int tile = first, next; tile < ntiles; tile = next) {
         const int tb = pos_begin + tile * TT;
         const bool st_tile = steps && tile == ntiles_c;
         const uint64_t tvalid = gvalid;
@@ -677,7 +730,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         // The next tile's loads go out now, or after QK^T where the registers
         // of two row tiles at D = 256 would not hold them during it.
         constexpr bool kEarly = !(D == 256 && RT == 2);
-        const int next = tile + kWaves;
+        auto next_tile = [&]() -> int {
+            if constexpr (MODE == 1)
+                return pick(kWaves);
+            else
+                return tile + kWaves;
+        };
+        if (kEarly) next = next_tile();
         if (kEarly && next < ntiles) {
             issue(next, jv_next);
             if constexpr (GATHER) jv_next = list_entry(next + kWaves);
@@ -699,12 +758,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
                 for (int rt = 0; rt < RT; ++rt) sc[rt][mb] = mfma(ka, q_lds[(rt * KS + ks) * 64 + lane], sc[rt][mb]);
             }
 
+        if (!kEarly) next = next_tile();
         if (!kEarly && next < ntiles) {
             issue(next, jv_next);
             if constexpr (GATHER) jv_next = list_entry(next + kWaves);
             if constexpr (Q8) jv_next = page_of(next + kWaves);
         }
-        if (tid == 0 && tile == 0 && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
+        if (tid == 0 && tile == first && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
 
         // -- online softmax (log2 domain) -----------------------------------
         bf16x8 pb[RT][KB];
@@ -1219,6 +1279,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.causal = causal ? 1 : 0;
     kp.out_bf16 = out_dtype == CK_DT_BF16 ? 1 : 0;
     kp.mask_dw = keep_mask != nullptr && aligned(keep_mask, 4) && s->cap % 4 == 0 ? 1 : 0;
+    kp.mask_skip = keep_mask != nullptr && aligned(keep_mask, 16) && s->cap % 16 == 0 ? 1 : 0;
     kp.row_bytes = (uint32_t)(s->Hkv * s->D * 2);
 
     const int RT = pl.rows_per_group / 16;

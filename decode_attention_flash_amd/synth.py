@@ -99,6 +99,30 @@ def topk_lists(B: int, n_q: int, Hkv: int, n_kv: int, n_sel: int, tail: int, see
     return out
 
 
+def block_lists(B: int, n_q: int, Hkv: int, n_kv: int, n_blocks: int, block: int, tail: int,
+                seed: int) -> np.ndarray:
+    """Index lists [B, n_q, Hkv, n_blocks * block + tail] int32 whose cells
+    come in runs: ``n_blocks`` distinct random aligned blocks of ``block``
+    cells from [0, n_kv - tail), in increasing order, followed by the last
+    ``tail`` cells.  A selection made over pooled block keys looks like this:
+    the same number of cells as a scattered selection, in few places."""
+    n_avail = (n_kv - tail) // block
+    if n_blocks > n_avail:
+        raise ValueError("not enough blocks to select from")
+    rng = np.random.default_rng(seed)
+    out = np.empty((B, n_q, Hkv, n_blocks * block + tail), dtype=np.int32)
+    tail_cells = np.arange(n_kv - tail, n_kv, dtype=np.int32)
+    offs = np.arange(block, dtype=np.int64)
+    for b in range(B):
+        for i in range(n_q):
+            for g in range(Hkv):
+                blocks = np.sort(rng.choice(n_avail, size=n_blocks, replace=False))
+                cells = (blocks.reshape(-1, 1) * block + offs.reshape(1, -1)).reshape(-1)
+                out[b, i, g, : n_blocks * block] = cells.astype(np.int32)
+                out[b, i, g, n_blocks * block:] = tail_cells
+    return out
+
+
 def mask_from_lists(idx: np.ndarray, cap: int) -> np.ndarray:
     """keep_mask [B, n_q, Hkv, cap] uint8 with 1 exactly at the listed cells
     that fall in [0, cap)."""

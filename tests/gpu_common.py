@@ -10,6 +10,7 @@ import torch
 
 import decode_attention_flash_amd as ck
 import oracle
+from decode_attention_flash_amd import synth
 
 # Tolerances for N(0, 1) inputs: max |delta| against the fp64 oracle.
 TOL_F32 = 4e-3     # fp32 output
@@ -97,3 +98,35 @@ def assert_close(gpu, ref, out_dtype=torch.float32, what=""):
         dl = float(np.max(np.abs(gl[~empty] - rl[~empty])))
         assert dl <= TOL_LSE, f"{what}: lse max|delta| {dl:.3e}"
     return d
+
+
+def counting_case(n_q, Hq, Hkv, D, cap, lens, seed, nbits=17):
+    B = len(lens)
+    k, _ = synth.kv_cache(B, cap, Hkv, D, lens, seed)
+    v1 = synth.counting_values(cap, Hkv, D, nbits)
+    v = v1.expand(B, cap, Hkv, D).contiguous()
+    for b, L in enumerate(lens):
+        k[b, :L] = 0
+        v[b, L:] = float("nan")
+        k[b, L:] = float("nan")
+    q = synth.queries(B, n_q, Hq, D, seed)
+    return q, k, v
+
+
+def check_counts(out, visible_sets, G, nbits=17):
+    """out [B, n_q, Hq, D] fp32; visible_sets[b][i][g] = array of cells."""
+    B, n_q, Hq, _ = out.shape
+    for b in range(B):
+        for i in range(n_q):
+            for h in range(Hq):
+                cells = np.asarray(visible_sets[b][i][h // G], dtype=np.int64)
+                n = len(cells)
+                if n == 0:
+                    assert np.all(out[b, i, h] == 0.0)
+                    continue
+                o = out[b, i, h].astype(np.float64)
+                assert abs(o[nbits] - 1.0) < 1e-6
+                counts = np.array([np.sum((cells >> d) & 1) for d in range(nbits)])
+                got = n * o[:nbits]
+                assert np.max(np.abs(got - counts)) < 0.01, (b, i, h)
+                assert np.array_equal(np.rint(got).astype(np.int64), counts), (b, i, h)

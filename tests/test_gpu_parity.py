@@ -9,8 +9,8 @@ import torch
 
 import decode_attention_flash_amd as ck
 from decode_attention_flash_amd import synth
-from gpu_common import (DEV, TOL_F32, assert_close, dense_gpu, gather_gpu, note, oracle_ref, steps_gpu,
-                        steps_ref)
+from gpu_common import (DEV, TOL_F32, assert_close, check_counts, counting_case, dense_gpu, gather_gpu, note,
+                        oracle_ref, steps_gpu, steps_ref)
 
 pytestmark = pytest.mark.gpu
 
@@ -299,38 +299,6 @@ def test_gather_lists_edge_entries():
 
 
 # ------------------------------------------------------- exactness checks ----
-
-def counting_case(n_q, Hq, Hkv, D, cap, lens, seed, nbits=17):
-    B = len(lens)
-    k, _ = synth.kv_cache(B, cap, Hkv, D, lens, seed)
-    v1 = synth.counting_values(cap, Hkv, D, nbits)
-    v = v1.expand(B, cap, Hkv, D).contiguous()
-    for b, L in enumerate(lens):
-        k[b, :L] = 0
-        v[b, L:] = float("nan")
-        k[b, L:] = float("nan")
-    q = synth.queries(B, n_q, Hq, D, seed)
-    return q, k, v
-
-
-def check_counts(out, visible_sets, G, nbits=17):
-    """out [B, n_q, Hq, D] fp32; visible_sets[b][i][g] = array of cells."""
-    B, n_q, Hq, _ = out.shape
-    for b in range(B):
-        for i in range(n_q):
-            for h in range(Hq):
-                cells = np.asarray(visible_sets[b][i][h // G], dtype=np.int64)
-                n = len(cells)
-                if n == 0:
-                    assert np.all(out[b, i, h] == 0.0)
-                    continue
-                o = out[b, i, h].astype(np.float64)
-                assert abs(o[nbits] - 1.0) < 1e-6
-                counts = np.array([np.sum((cells >> d) & 1) for d in range(nbits)])
-                got = n * o[:nbits]
-                assert np.max(np.abs(got - counts)) < 0.01, (b, i, h)
-                assert np.array_equal(np.rint(got).astype(np.int64), counts), (b, i, h)
-
 
 @pytest.mark.parametrize("cfg", [
     dict(n_q=1, Hq=8, Hkv=2, D=128, cap=1024, lens=[300], causal=False),
