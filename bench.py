@@ -350,21 +350,27 @@ def main():
         sweep["ragged_batch"] = dict(B=32, sum_kv_len=int(lens.sum()), **r)
         del st
         torch.cuda.empty_cache()
-        # sparse: gathered top-k lists vs the masked full-window scan
+        # sparse: gathered top-k lists vs the masked full-window scan, with the
+        # 2048 cells drawn one by one or as 32 aligned runs of 64 (tiles skip)
         sweep["sparse"] = []
         for n_kv in (32768, 65536, 131072):
             W_sel, tail = 2048, 64
             n_g = layers_for(2 * (W_sel + tail) * 4 * 128)
             n_m = layers_for(4 * 2 * 128 * n_kv)
             st = Stack(max(n_g, n_m), 1, n_kv, 2, 128, 1005)
-            rg, idxs = gather_case(st, n_kv, W_sel, tail, args.steps, args.warmup)
-            masks = [torch.from_numpy(synth.mask_from_lists(idxs[l].cpu().numpy(), n_kv)).to("cuda")
-                     for l in range(n_m)]
-            rm = dense_case(st, 1, 1, 16, 2, 128, [n_kv], args.steps, args.warmup, n_layers=n_m,
-                            masks=masks)
-            log(f"sparse n_kv={n_kv}: gather {rg['us']:.2f} us, masked {rm['us']:.2f} us")
-            sweep["sparse"].append(dict(n_kv=n_kv, gather=rg, masked=rm))
-            del st, masks
+            path = ck.sparse_path(ck.Shape(1, 1, 16, 2, 128, n_kv), W_sel + tail, n_kv)
+            for block in (0, 64):
+                sel = "blocks" if block else "scattered"
+                rg, idxs = gather_case(st, n_kv, W_sel, tail, args.steps, args.warmup, block=block)
+                masks = [torch.from_numpy(synth.mask_from_lists(idxs[l].cpu().numpy(), n_kv)).to("cuda")
+                         for l in range(n_m)]
+                rm = dense_case(st, 1, 1, 16, 2, 128, [n_kv], args.steps, args.warmup, n_layers=n_m,
+                                masks=masks)
+                log(f"sparse n_kv={n_kv} {sel}: gather {rg['us']:.2f} us, masked {rm['us']:.2f} us "
+                    f"(chosen: {path})")
+                sweep["sparse"].append(dict(n_kv=n_kv, selection=sel, chosen=path, gather=rg, masked=rm))
+                del masks
+            del st
             torch.cuda.empty_cache()
 
     if not args.headline_only:

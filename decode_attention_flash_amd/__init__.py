@@ -20,11 +20,13 @@ CK_DT_F32 = 0
 CK_DT_BF16 = 1
 CK_MAX_NQ = 6
 CK_MAX_SPLITS = 256
+CK_PATH_GATHER = 0
+CK_PATH_SCAN = 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misaligned pointer",
           -4: "workspace missing or too small", -5: "HIP runtime error"}
 EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
            "ck_kv_append_q8", "ck_decode_attn_workspace_size",
-           "ck_decode_attn_plan", "ck_status_string")
+           "ck_decode_attn_plan", "ck_decode_sparse_path", "ck_status_string")
 
 
 class CkError(RuntimeError):
@@ -88,6 +90,8 @@ def lib():
         L.ck_decode_attn_q8.restype = ctypes.c_int
         L.ck_kv_append_q8.argtypes = [sp, vp, vp, vp, qp, vp]
         L.ck_kv_append_q8.restype = ctypes.c_int
+        L.ck_decode_sparse_path.argtypes = [sp, i32, i64, ctypes.POINTER(i32)]
+        L.ck_decode_sparse_path.restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
         L.ck_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -243,6 +247,34 @@ def decode_attn_gather(q, k_cache, v_cache, kv_lens, idx, *, scale: float | None
     if st != 0:
         raise CkError(st, "ck_decode_attn_gather")
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def sparse_path(shape: Shape, W: int, n_kv: int) -> str:
+    """"gather" or "scan": the faster entry point for a top-k selection of W
+    cells per query over lengths up to n_kv (``ck_decode_sparse_path``)."""
+    path = ctypes.c_int32(-1)
+    st = lib().ck_decode_sparse_path(ctypes.byref(shape), int(W), int(n_kv), ctypes.byref(path))
+    if st != 0:
+        raise CkError(st, "ck_decode_sparse_path")
+    return "scan" if path.value == CK_PATH_SCAN else "gather"
+
+
+def decode_attn_sparse(q, k_cache, v_cache, kv_lens, idx, *, keep_mask=None, n_kv: int | None = None,
+                       scale: float | None = None, causal: bool = False, out_dtype=torch.float32, out=None,
+                       lse=None, return_lse=False, num_splits: int = 0, stream=None):
+    """Attention over a top-k selection given as index lists ``idx`` (and,
+    optionally, the same cells as ``keep_mask``): runs the gather or the
+    masked scan, whichever ``sparse_path`` names for the shape, W and n_kv
+    (default: the cache capacity).  The scan needs the mask; without one the
+    gather runs.  Workspaces come from the per-plan cache."""
+    shape = shape_of(q, k_cache)
+    W = idx.shape[-1]
+    path = sparse_path(shape, W, shape.cap if n_kv is None else n_kv)
+    kw = dict(scale=scale, causal=causal, out_dtype=out_dtype, out=out, lse=lse, return_lse=return_lse,
+              num_splits=num_splits, stream=stream)
+    if path == "scan" and keep_mask is not None:
+        return decode_attn(q, k_cache, v_cache, kv_lens, keep_mask=keep_mask, **kw)
+    return decode_attn_gather(q, k_cache, v_cache, kv_lens, idx, **kw)
 
 
 def decode_attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, *, scale: float | None = None,

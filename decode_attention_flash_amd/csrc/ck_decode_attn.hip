@@ -1102,7 +1102,10 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     const int64_t rows_eff = R < rows_per_group ? R : rows_per_group;
     int64_t target, cmax, cmin = TT;
     if (num_splits == 0) {
-        target = ((int64_t)num_cus * kWgPerCu + units - 1) / units;
+        // As many splits as keep every unit's workgroups in one round (one
+        // workgroup per CU): one more would leave a few workgroups for a
+        // second round and double the time.
+        target = (int64_t)num_cus * kWgPerCu / units;
         cmax = 2 * units >= num_cus ? chunk_max_tokens(s->D) : 0;
         cmin = (kTokensPerRow * rows_eff + TT - 1) / TT * TT;
     } else {
@@ -1304,6 +1307,28 @@ extern "C" {
 int ck_decode_attn_plan(const ck_decode_shape* shape, int32_t W, int num_splits, int num_cus,
                         ck_decode_plan* plan) {
     return ckda::plan_impl(shape, W, num_splits, num_cus, plan);
+}
+
+int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv, int32_t* path) {
+    if (!path || W < 1 || n_kv < 0) return CK_ERR_ARG;
+    ck_decode_plan pl;
+    const int st = ckda::plan_impl(shape, W, 0, 1, &pl);  // validates the shape
+    if (st != CK_OK) return st;
+    // Time model fitted to MI355X timings of both paths (cold caches, B = 1,
+    // D 128 and 256, 2 and 4 KV heads, n_q 1/3/6, n_kv 1k-64k, W 128-32k,
+    // scattered cells), in us, with a cell = B * Hkv * 4 * D bytes (the K
+    // and V rows of every KV head at one position):
+    //   gather = 9.6 + 0.150 * MB of listed cells            (n_q * W cells)
+    //   scan   = 12.3 + 0.85 * (n_q - 1) + (0.137 + 0.027 * (n_q - 1)) * MB of window   (n_kv cells)
+    // It names the faster path at each of the 158 measured points.  The scan
+    // term is its cost with every tile holding a kept cell; clustered
+    // selections make the scan cheaper (skipped tiles), never the gather.
+    const double cell_mb = (double)shape->B * shape->Hkv * 4.0 * shape->D / 1e6;
+    const double extra_q = (double)(shape->n_q - 1);
+    const double t_gather = 9.6 + 0.150 * (double)shape->n_q * (double)W * cell_mb;
+    const double t_scan = 12.3 + 0.85 * extra_q + (0.137 + 0.027 * extra_q) * (double)n_kv * cell_mb;
+    *path = t_scan < t_gather ? CK_PATH_SCAN : CK_PATH_GATHER;
+    return CK_OK;
 }
 
 int ck_decode_attn_workspace_size(const ck_decode_shape* shape, int32_t W, int num_splits, size_t* bytes) {

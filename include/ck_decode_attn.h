@@ -161,6 +161,36 @@ int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const voi
                           int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
                           int num_splits, void* stream);
 
+/* Gather or scan for a top-k selection: which of ck_decode_attn_gather
+ * (over the index lists) and ck_decode_attn with keep_mask (a scan of the
+ * window with the same cells kept) is faster for this shape on MI355X.
+ * The pages gate their gather by the cache depth: the scan reads the window
+ * once for all queries while their gather moves the selected cells twice,
+ * so they meet at n_kv = 2 * n_tps * width (llama.cpp PR "qwen4exp: attend
+ * the selected cells instead of masking the window", PR body; per-token
+ * lists in the discussion of llama.cpp PR "qwen4exp : gather-based sparse
+ * attention for QSA decode"), and that PR's author gates at 4 x the top-k
+ * width.  The gather here moves each selected cell once, straight from the
+ * cache, and has the lower fixed cost, so it is faster unless the lists
+ * cover most of a long window.  The choice compares two time models fitted
+ * to MI355X measurements of both entry points, with a cell = B*Hkv*4*D
+ * bytes (K and V of every KV head at one position):
+ *   gather: 9.6 us + 0.150 us per MB of the n_q * W listed cells
+ *   scan:   12.3 us + 0.85 us * (n_q - 1)
+ *           + (0.137 + 0.027 * (n_q - 1)) us per MB of the n_kv window cells
+ * and returns the smaller (the scan term assumes every tile holds a kept
+ * cell; clustered selections only make the scan cheaper).
+ *   shape : as for the entry points (W >= 1 selects the gather plan checks)
+ *   W     : list length per query
+ *   n_kv  : host-side bound of the lengths the scan would cover (the largest
+ *           length, or cap); >= 0
+ *   path  : receives CK_PATH_GATHER or CK_PATH_SCAN
+ * Pure host arithmetic: no HIP call, nothing read from device memory, so the
+ * choice is fixed for a captured graph.  Returns CK_OK or an argument error. */
+#define CK_PATH_GATHER 0
+#define CK_PATH_SCAN 1
+int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv, int32_t* path);
+
 /* Step rows merged into prefix attention: the n_q verification queries of
  * an MTP step attend the cache prefix [0, L) plus their own draft rows,
  * whose K/V are passed separately instead of being written into the cache

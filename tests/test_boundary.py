@@ -46,6 +46,16 @@ def test_plan_fills_the_chip_at_batch_one():
     assert p["workspace_bytes"] > 0
 
 
+@pytest.mark.parametrize("B,Hkv,n_q,W", [(3, 4, 1, 0), (1, 2, 6, 4160), (5, 8, 1, 0), (1, 4, 5, 2112)])
+def test_plan_keeps_workgroups_in_one_round(B, Hkv, n_q, W):
+    # unit counts that do not divide the CU count: the split target rounds
+    # down, so units x splits never exceeds one workgroup per CU
+    p = ck.plan(shape(B=B, Hq=4 * Hkv, Hkv=Hkv, n_q=n_q, D=128, cap=65536), W=W, num_cus=256)
+    assert p["units"] * p["split_target"] <= 256
+    assert p["units"] * (p["split_target"] + 1) > 256
+    assert p["units"] * p["splits"] <= 256
+
+
 def test_plan_single_sequence_has_no_chunk_limit():
     p = ck.plan(shape(), num_cus=256)
     assert p["chunk_max"] == 0
@@ -190,3 +200,43 @@ def test_q8_append_rejects(kw, status):
     st = ck.lib().ck_kv_append_q8(ctypes.byref(sh), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x48000),
                                   ctypes.c_void_p(start) if start else None, ctypes.byref(c), None)
     assert st == status
+
+
+# ------------------------------------------------ gather-vs-scan choice ----
+
+@pytest.mark.parametrize("D,Hkv,n_q,W,n_kv,want", [
+    (128, 2, 1, 2112, 131072, "gather"),   # the sparse workload: lists far shorter than the window
+    (128, 2, 6, 2048, 2048, "gather"),     # short window: the scan's fixed cost dominates
+    (128, 2, 1, 32768, 32768, "gather"),   # whole window listed once: measured 16.1 vs 17.2 us
+    (128, 2, 3, 32768, 32768, "scan"),     # listed three times: measured 28.7 vs 23.8 us
+    (256, 4, 6, 4096, 8192, "gather"),     # measured 24.6 vs 25.7 us
+    (256, 4, 3, 16384, 32768, "scan"),     # measured 41.1 vs 34.1 us
+])
+def test_sparse_path_follows_measurements(D, Hkv, n_q, W, n_kv, want):
+    s = shape(B=1, n_q=n_q, Hq=4 * Hkv, Hkv=Hkv, D=D, cap=max(n_kv, 1))
+    assert ck.sparse_path(s, W, n_kv) == want
+
+
+def test_sparse_path_switches_once_as_lists_grow():
+    # more listed cells only make the gather costlier: once the scan wins it keeps winning
+    for D, Hkv, n_q, n_kv in ((128, 2, 1, 65536), (128, 2, 6, 16384), (256, 4, 3, 8192)):
+        s = shape(n_q=n_q, Hq=4 * Hkv, Hkv=Hkv, D=D, cap=n_kv)
+        picks = [ck.sparse_path(s, W, n_kv) for W in range(64, 4 * n_kv + 1, 64)]
+        flips = sum(1 for a, b in zip(picks, picks[1:]) if a != b)
+        assert flips <= 1 and picks[0] == "gather"
+
+
+def test_sparse_path_ignores_capacity():
+    a = ck.sparse_path(shape(cap=8199), 2112, 8000)
+    b = ck.sparse_path(shape(cap=24007), 2112, 8000)
+    assert a == b
+
+
+@pytest.mark.parametrize("kw,W,n_kv,status", [
+    (dict(), 0, 1000, -1), (dict(), 64, -1, -1), (dict(D=64), 64, 1000, -2), (dict(n_q=7), 64, 1000, -2),
+])
+def test_sparse_path_rejects(kw, W, n_kv, status):
+    path = ctypes.c_int32(-7)
+    st = ck.lib().ck_decode_sparse_path(ctypes.byref(shape(**kw)), W, n_kv, ctypes.byref(path))
+    assert st == status and path.value == -7
+    assert ck.lib().ck_decode_sparse_path(ctypes.byref(shape()), 64, 1000, None) == -1

@@ -1,10 +1,12 @@
-"""GPU: the masked scan skips tiles that hold no kept cell.
+"""GPU: top-k selections through the masked scan (which skips tiles that
+hold no kept cell) and through the gather-or-scan choice.
 
 Skipping must not change which cells are attended: the tests compare with
 the oracle, recover exact cell sets with the counting construction (splits
 long enough to cross several 64-tile windows of the tile bitmap), and check
 that a mask stored where tiles cannot be skipped (rows not 16-byte aligned)
-gives the same result."""
+gives the same result.  decode_attn_sparse must run the entry point that
+ck_decode_sparse_path names and agree with the oracle either way."""
 import numpy as np
 import pytest
 import torch
@@ -166,3 +168,35 @@ def test_skipping_and_full_scan_agree(D):
     assert_close(a, ref, what="skipping")
     assert_close(u, ref, what="full scan")
     assert np.max(np.abs(a[0] - u[0])) <= 2e-3
+
+
+@pytest.mark.parametrize("D,Hkv,n_q,W,n_kv,want", [
+    (128, 2, 1, 2112, 8192, "gather"),
+    (256, 4, 3, 8192, 8192, "scan"),
+])
+def test_sparse_dispatch_routes_and_matches_oracle(D, Hkv, n_q, W, n_kv, want, monkeypatch):
+    B, Hq = 1, 4 * Hkv
+    note(f"sparse dispatch D={D} n_q={n_q} W={W} n_kv={n_kv}")
+    k, v = synth.kv_cache(B, n_kv, Hkv, D, [n_kv], 1010)
+    q = synth.queries(B, n_q, Hq, D, 1010)
+    idx = synth.topk_lists(B, n_q, Hkv, n_kv, W - 64, 64, seed=5400 + W)
+    mask = synth.mask_from_lists(idx, n_kv)
+    calls = []
+    scan, gather = ck.decode_attn, ck.decode_attn_gather
+    monkeypatch.setattr(ck, "decode_attn", lambda *a, **kw: calls.append("scan") or scan(*a, **kw))
+    monkeypatch.setattr(ck, "decode_attn_gather", lambda *a, **kw: calls.append("gather") or gather(*a, **kw))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lens_d = torch.tensor([n_kv], dtype=torch.int32, device=DEV)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    mask_d = torch.from_numpy(mask).to(DEV)
+    causal = n_q > 1
+    ref = oracle_ref(q, k, v, [n_kv], causal=causal, keep_mask=mask)
+    out, lse = ck.decode_attn_sparse(qd, kd, vd, lens_d, idx_d, keep_mask=mask_d, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert calls == [want]
+    assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what=f"sparse {want}")
+    calls.clear()  # without a mask only the gather can serve
+    out, lse = ck.decode_attn_sparse(qd, kd, vd, lens_d, idx_d, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert calls == ["gather"]
+    assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what="sparse without mask")
