@@ -63,6 +63,8 @@ def load(path: str | None = None):
     lib.ck_oracle_q8_quantize_rows.argtypes = [ctypes.c_longlong, ci, vp, vp, vp]
     lib.ck_oracle_q8_append.restype = ci
     lib.ck_oracle_q8_append.argtypes = [ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ck_oracle_topk.restype = ci
+    lib.ck_oracle_topk.argtypes = [ci, ci, ci, ci, vp, vp, ci, ci, ci, vp]
     lib.ck_oracle_nthreads_default.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -209,6 +211,27 @@ def q8_append(k_new, v_new, start, block_table, kq, vq, ksc, vsc, lib=None):
                                 ptr(bt), ptr(kq), ptr(vq), ptr(ksc), ptr(vsc))
     if r != 0:
         raise RuntimeError(f"oracle failed with status {r}")
+
+
+def topk(scores, kv_lens, k: int, tail: int = 0, causal: bool = False, lib=None) -> np.ndarray:
+    """Top-k index lists: for each row of scores [B, n_q, Hs, cap] (float32),
+    the min(k, n) best of the n cells before the window's last ``tail`` cells
+    (larger score first, then smaller cell; NaN as -inf), ascending, then the
+    tail cells, then -1.  Returns int32 [B, n_q, Hs, k + tail]."""
+    lib = lib or load()
+    sc = np.ascontiguousarray(np.asarray(scores, dtype=np.float32))
+    if sc.ndim != 4:
+        raise ValueError("scores must be [B, n_q, Hs, cap]")
+    B, n_q, Hs, cap = sc.shape
+    lens = _np(kv_lens, np.int32).reshape(-1)
+    if lens.shape[0] != B:
+        raise ValueError("kv_lens must have B entries")
+    out = np.empty((B, n_q, Hs, k + tail), dtype=np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    r = lib.ck_oracle_topk(B, n_q, Hs, cap, ptr(sc), ptr(lens), int(k), int(tail), 1 if causal else 0, ptr(out))
+    if r != 0:
+        raise RuntimeError(f"oracle failed with status {r}")
+    return out
 
 
 def attn_q8(q, kq, vq, ksc, vsc, block_table, kv_lens, scale: float, causal: bool = False,

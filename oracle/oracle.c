@@ -416,6 +416,86 @@ int ck_oracle_q8_append(int B, int n_new, int Hkv, int D, int page, int max_page
     return ORACLE_OK;
 }
 
+/*
+ * Top-k selection (ck_oracle_topk): the index lists the gather reads
+ * (llama.cpp PR "qwen4exp : gather-based sparse attention for QSA decode",
+ * discussion: the indexer's top-k over the whole score row every step; the
+ * selection always keeps the current tail, llama.cpp PR "qwen4exp: attend the
+ * selected cells instead of masking the window", PR body).  For each row
+ * (b, i, h) of scores [B, n_q, Hs, cap]: L and lim as above, the tail
+ * [max(0, lim - tail), lim), the candidates [0, n) with n = max(0, lim - tail).
+ * The selection is the first min(k, n) candidates in the order "larger score
+ * first, then smaller cell", with NaN taken as -inf (a sort serves this
+ * step); the row of idx [B, n_q, Hs, k + tail] holds those cells ascending,
+ * then the tail cells, then -1.
+ */
+typedef struct {
+    double v;
+    int32_t j;
+} scored_t;
+
+static int by_score_then_cell(const void *a, const void *b) {
+    const scored_t *x = (const scored_t *)a, *y = (const scored_t *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+static int by_cell(const void *a, const void *b) {
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+int ck_oracle_topk(int B, int n_q, int Hs, int cap, const float *scores, const int32_t *kv_lens, int k,
+                   int tail, int causal, int32_t *idx) {
+    if (B < 1 || n_q < 1 || Hs < 1 || cap < 1 || k < 1 || tail < 0) return ORACLE_ERR_ARG;
+    if (!scores || !kv_lens || !idx) return ORACLE_ERR_ARG;
+    const int W = k + tail;
+    scored_t *c = (scored_t *)malloc((size_t)cap * sizeof(scored_t));
+    int32_t *sel = (int32_t *)malloc((size_t)cap * sizeof(int32_t));
+    if (!c || !sel) {
+        free(c);
+        free(sel);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int b = 0; b < B; ++b) {
+        int L = kv_lens[b];
+        if (L < 0) L = 0;
+        if (L > cap) L = cap;
+        for (int i = 0; i < n_q; ++i) {
+            int lim = L;
+            if (causal) {
+                lim = L - n_q + i + 1;
+                if (lim < 0) lim = 0;
+                if (lim > L) lim = L;
+            }
+            int n = lim - tail;
+            if (n < 0) n = 0;
+            for (int h = 0; h < Hs; ++h) {
+                const float *row = scores + (((size_t)b * n_q + i) * Hs + h) * (size_t)cap;
+                for (int j = 0; j < n; ++j) {
+                    double v = (double)row[j];
+                    if (isnan(v)) v = -INFINITY;
+                    c[j].v = v;
+                    c[j].j = j;
+                }
+                qsort(c, (size_t)n, sizeof(scored_t), by_score_then_cell);
+                int m = n < k ? n : k;
+                for (int t = 0; t < m; ++t) sel[t] = c[t].j;
+                qsort(sel, (size_t)m, sizeof(int32_t), by_cell);
+                int32_t *out = idx + (((size_t)b * n_q + i) * Hs + h) * (size_t)W;
+                int s = 0;
+                for (int t = 0; t < m; ++t) out[s++] = sel[t];
+                for (int j = n; j < lim; ++j) out[s++] = j;
+                while (s < W) out[s++] = -1;
+            }
+        }
+    }
+    free(c);
+    free(sel);
+    return ORACLE_OK;
+}
+
 static int run_job(const job_t *JP, int nthreads) {
     const job_t J = *JP;
     const int B = J.B, n_q = J.n_q, Hq = J.Hq;

@@ -416,6 +416,90 @@ def check_q8_append(lib) -> float:
     return worst
 
 
+# ---------------------------------------------------------------- top-k ----
+
+def topk_brute(scores, lens, k, tail, causal):
+    """Pure-Python top-k lists: a candidate is selected when fewer than k
+    candidates beat it (a larger score, or the same score at a smaller cell;
+    NaN counts as -inf)."""
+    B, n_q, Hs, cap = scores.shape
+    out = np.full((B, n_q, Hs, k + tail), -1, dtype=np.int64)
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), cap)
+        for i in range(n_q):
+            lim = min(max(L - n_q + i + 1, 0), L) if causal else L
+            n = max(0, lim - tail)
+            for h in range(Hs):
+                v = [float(x) for x in scores[b, i, h, :n]]
+                v = [-math.inf if math.isnan(x) else x for x in v]
+                chosen = []
+                for c in range(n):
+                    beaten = sum(1 for d in range(n) if v[d] > v[c] or (v[d] == v[c] and d < c))
+                    if beaten < k:
+                        chosen.append(c)
+                row = chosen + list(range(n, lim))
+                out[b, i, h, :len(row)] = row
+    return out
+
+
+def check_topk_brute_force(lib) -> float:
+    """Against the brute force on small rows with many ties (small integer
+    scores), NaN, -inf / +inf and signed zeros, causal windows, two score
+    heads, lengths past the capacity and k larger than the candidates."""
+    bad = 0
+    gen = np.random.default_rng(101)
+    for trial in range(40):
+        B, n_q, Hs, cap = int(gen.integers(1, 3)), int(gen.integers(1, 4)), int(gen.integers(1, 3)), \
+            int(gen.integers(1, 40))
+        sc = gen.integers(-3, 4, size=(B, n_q, Hs, cap)).astype(np.float32)
+        specials = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0], dtype=np.float32)
+        pick = gen.random(sc.shape) < 0.15
+        sc[pick] = specials[gen.integers(0, len(specials), size=int(pick.sum()))]
+        lens = gen.integers(-2, cap + 3, size=B).astype(np.int32)
+        k, tail, causal = int(gen.integers(1, 12)), int(gen.integers(0, 5)), bool(trial % 2)
+        got = oracle.topk(sc, lens, k, tail, causal, lib=lib)
+        bad += int(not np.array_equal(got, topk_brute(sc, lens, k, tail, causal)))
+    return float(bad)
+
+
+def check_topk_closed_forms(lib) -> float:
+    """Scores rising with the cell select the last k candidates, falling
+    scores the first k, equal scores the first k (lowest cell first); with
+    k >= n every candidate; an empty window gives -1 throughout."""
+    bad = 0
+    cap, k, tail = 50, 7, 3
+    lens = np.array([50, 31, 2, 0], dtype=np.int32)
+    cells = np.arange(cap, dtype=np.float32)
+    for kind in ("rise", "fall", "flat"):
+        v = {"rise": cells, "fall": -cells, "flat": np.full(cap, 0.5, np.float32)}[kind]
+        sc = np.broadcast_to(v, (4, 1, 1, cap)).copy()
+        got = oracle.topk(sc, lens, k, tail, lib=lib)
+        for b, L in enumerate(lens):
+            n = max(0, int(L) - tail)
+            m = min(k, n)
+            sel = list(range(n - m, n)) if kind == "rise" else list(range(m))
+            want = sel + list(range(n, int(L)))
+            want += [-1] * (k + tail - len(want))
+            bad += int(list(got[b, 0, 0]) != want)
+    return float(bad)
+
+
+def check_topk_permutation(lib) -> float:
+    """Distinct scores moved between cells by a permutation: the selected
+    cells move with them."""
+    gen = np.random.default_rng(103)
+    cap, k, tail = 300, 40, 5
+    sc = gen.standard_normal((1, 1, 1, cap)).astype(np.float32)
+    lens = np.array([cap], dtype=np.int32)
+    n = cap - tail
+    perm = gen.permutation(n)
+    moved = sc.copy()
+    moved[0, 0, 0, perm] = sc[0, 0, 0, :n]  # score of cell c now sits at perm[c]
+    a = oracle.topk(sc, lens, k, tail, lib=lib)[0, 0, 0, :k]
+    b = oracle.topk(moved, lens, k, tail, lib=lib)[0, 0, 0, :k]
+    return float(not np.array_equal(np.sort(perm[a]), b))
+
+
 ALL_CHECKS = {
     "sdpa_dense": check_sdpa_dense,
     "sdpa_mask": check_sdpa_mask,
@@ -431,4 +515,7 @@ ALL_CHECKS = {
     "q8_sdpa": check_q8_sdpa,
     "q8_page_permutation": check_q8_page_permutation,
     "q8_append": check_q8_append,
+    "topk_brute_force": check_topk_brute_force,
+    "topk_closed_forms": check_topk_closed_forms,
+    "topk_permutation": check_topk_permutation,
 }

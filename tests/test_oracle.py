@@ -123,6 +123,14 @@ MUTANTS = {
         "size_t qo = (((size_t)b * J->n_q + i) * J->Hq + h) * (size_t)D;\n    double *o = J->out + qo;\n"
         "    qo = (((size_t)b * J->Hq + h) * J->n_q + i) * (size_t)D;"),
     "clamp_missing": ("if (L > J->cap) L = J->cap;", ""),
+    "topk_ties_highest_cell_first": ("return (x->j > y->j) - (x->j < y->j);",
+                                     "return (x->j < y->j) - (x->j > y->j);"),
+    "topk_nan_ranks_high": ("if (isnan(v)) v = -INFINITY;", "if (isnan(v)) v = INFINITY;"),
+    "topk_tail_among_candidates": ("int n = lim - tail;", "int n = lim;"),
+    "topk_one_short": ("int m = n < k ? n : k;", "int m = n < k ? n : k - 1;"),
+    "topk_unsorted_lists": ("qsort(sel, (size_t)m, sizeof(int32_t), by_cell);", ""),
+    "topk_smallest_first": ("if (x->v > y->v) return -1;", "if (x->v < y->v) return -1;"),
+    "topk_causal_off_by_one": ("                lim = L - n_q + i + 1;", "                lim = L - n_q + i;"),
 }
 
 
