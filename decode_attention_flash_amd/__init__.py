@@ -26,7 +26,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misalig
           -4: "workspace missing or too small", -5: "HIP runtime error"}
 EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
            "ck_kv_append_q8", "ck_decode_attn_workspace_size",
-           "ck_decode_attn_plan", "ck_decode_sparse_path", "ck_status_string")
+           "ck_decode_attn_plan", "ck_decode_sparse_path", "ck_decode_topk", "ck_decode_topk_plan",
+           "ck_decode_topk_workspace_size", "ck_status_string")
 
 
 class CkError(RuntimeError):
@@ -92,6 +93,13 @@ def lib():
         L.ck_kv_append_q8.restype = ctypes.c_int
         L.ck_decode_sparse_path.argtypes = [sp, i32, i64, ctypes.POINTER(i32)]
         L.ck_decode_sparse_path.restype = ctypes.c_int
+        L.ck_decode_topk.argtypes = [sp, vp, i32, vp, i32, i32, ctypes.c_int, vp, vp, sz, vp]
+        L.ck_decode_topk.restype = ctypes.c_int
+        L.ck_decode_topk_plan.argtypes = [sp, i32, i32, i32, ctypes.c_int, ctypes.POINTER(i32),
+                                          ctypes.POINTER(sz)]
+        L.ck_decode_topk_plan.restype = ctypes.c_int
+        L.ck_decode_topk_workspace_size.argtypes = [sp, i32, i32, i32, ctypes.POINTER(sz)]
+        L.ck_decode_topk_workspace_size.restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
         L.ck_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -275,6 +283,69 @@ def decode_attn_sparse(q, k_cache, v_cache, kv_lens, idx, *, keep_mask=None, n_k
     if path == "scan" and keep_mask is not None:
         return decode_attn(q, k_cache, v_cache, kv_lens, keep_mask=keep_mask, **kw)
     return decode_attn_gather(q, k_cache, v_cache, kv_lens, idx, **kw)
+
+
+def _topk_shape(scores: torch.Tensor, num_kv_heads: int | None) -> tuple[Shape, int]:
+    if scores.dim() != 4:
+        raise ValueError("scores must be [B, n_q, Hs, cap]")
+    B, n_q, Hs, cap = scores.shape
+    Hkv = Hs if num_kv_heads is None else int(num_kv_heads)
+    # Hq and D do not enter the selection; the shape carries placeholders.
+    return Shape(B, n_q, Hkv, Hkv, 128, cap), Hs
+
+
+def topk_plan(scores_shape, k: int, tail: int = 0, num_kv_heads: int | None = None,
+              num_cus: int | None = None) -> dict:
+    """Workgroups per row and workspace bytes of ``ck_decode_topk`` for scores
+    of shape [B, n_q, Hs, cap] (``ck_decode_topk_plan``)."""
+    B, n_q, Hs, cap = scores_shape
+    Hkv = Hs if num_kv_heads is None else int(num_kv_heads)
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    P, n = ctypes.c_int32(0), ctypes.c_size_t(0)
+    st = lib().ck_decode_topk_plan(ctypes.byref(Shape(B, n_q, Hkv, Hkv, 128, cap)), Hs, k, tail, num_cus,
+                                   ctypes.byref(P), ctypes.byref(n))
+    if st != 0:
+        raise CkError(st, "ck_decode_topk_plan")
+    return {"wgs_per_row": P.value, "workspace_bytes": n.value}
+
+
+_topk_ws = {}
+
+
+def decode_topk(scores, kv_lens, k: int, *, tail: int = 0, causal: bool = False, num_kv_heads: int | None = None,
+                out=None, workspace=None, stream=None):
+    """Top-k index lists (``ck_decode_topk``): for each (sequence, query, score
+    head) row of scores [B, n_q, Hs, cap] fp32, the k highest-scoring cells
+    before the window's last ``tail`` cells, then those tail cells, ascending,
+    padded with -1: int32 [B, n_q, Hs, k + tail], ready for decode_attn_gather
+    (Hs = 1 gives one list per query: pass it as [B, n_q, W])."""
+    _check(scores, "scores", torch.float32)
+    _check(kv_lens, "kv_lens", torch.int32)
+    shape, Hs = _topk_shape(scores, num_kv_heads)
+    W = int(k) + int(tail)
+    if out is None:
+        out = torch.empty((shape.B, shape.n_q, Hs, W), dtype=torch.int32, device=scores.device)
+    _check(out, "out", torch.int32)
+    if tuple(out.shape) != (shape.B, shape.n_q, Hs, W):
+        raise ValueError("out must be [B, n_q, Hs, k + tail]")
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        st = lib().ck_decode_topk_workspace_size(ctypes.byref(shape), Hs, int(k), int(tail), ctypes.byref(n))
+        if st != 0:
+            raise CkError(st, "ck_decode_topk_workspace_size")
+        if n.value:
+            key = (n.value, scores.device)
+            if key not in _topk_ws:
+                _topk_ws[key] = torch.zeros(n.value, dtype=torch.uint8, device=scores.device)
+            workspace = _topk_ws[key]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st_handle = stream if stream is not None else torch.cuda.current_stream(scores.device).cuda_stream
+    st = lib().ck_decode_topk(ctypes.byref(shape), _ptr(scores), Hs, _ptr(kv_lens), int(k), int(tail),
+                              1 if causal else 0, _ptr(out), _ptr(workspace), ws_bytes, ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_decode_topk")
+    return out
 
 
 def decode_attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, *, scale: float | None = None,

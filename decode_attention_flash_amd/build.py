@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "ck_decode_attn.hip")
+SRCS = [os.path.join(PKG, "csrc", "ck_decode_attn.hip"), os.path.join(PKG, "csrc", "ck_topk.hip")]
 LIB = os.path.join(PKG, "libck_decode_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,7 +22,7 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", LIB + ".tmp"]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", LIB + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)

@@ -99,6 +99,14 @@ def topk_lists(B: int, n_q: int, Hkv: int, n_kv: int, n_sel: int, tail: int, see
     return out
 
 
+def index_scores(B: int, n_q: int, Hs: int, cap: int, seed: int, device="cpu") -> torch.Tensor:
+    """Selection scores [B, n_q, Hs, cap] float32 ~ N(0, 1): one score per
+    cache cell for each query and score head (the indexer's output, which
+    needs trained weights, stands in as noise)."""
+    g = generator(seed, device)
+    return torch.randn((B, n_q, Hs, cap), generator=g, device=device, dtype=torch.float32)
+
+
 def block_lists(B: int, n_q: int, Hkv: int, n_kv: int, n_blocks: int, block: int, tail: int,
                 seed: int) -> np.ndarray:
     """Index lists [B, n_q, Hkv, n_blocks * block + tail] int32 whose cells

@@ -191,6 +191,49 @@ int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const voi
 #define CK_PATH_SCAN 1
 int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv, int32_t* path);
 
+/* Top-k selection: the index lists the gather reads, from one score per
+ * cache cell (llama.cpp PR "qwen4exp : gather-based sparse attention for QSA
+ * decode", discussion: the selection runs over the whole score row every
+ * decode step, so it is the cost that still grows with the context once the
+ * attention is gathered; radix/partial top-k paths serve it on other
+ * backends).  For each row (sequence b, query i, score head h):
+ *   L, lim   as in the definition above (causal: the window's query limit)
+ *   tail     the last `tail` cells of the window, [max(0, lim - tail), lim),
+ *            are always kept (the pages' selection always keeps the current
+ *            tail)
+ *   selected the min(k, n) highest-scoring of the n = max(0, lim - tail)
+ *            cells before the tail; equal scores are taken lowest cell first,
+ *            NaN ranks with -inf and -0 with +0, so the set is unique
+ *   idx row  the selected cells and then the tail cells, ascending, padded
+ *            with -1 to W = k + tail entries
+ * Scores at or past the window limit are never read.
+ *   shape     : B, n_q (<= CK_MAX_NQ), Hkv and cap are used; Hq and D are not
+ *   scores    : fp32 [B, n_q, Hs, cap], 4-byte aligned (16-byte aligned rows
+ *               read 4 scores per load)
+ *   Hs        : score heads: Hkv (a list per KV head) or 1 (one list per
+ *               query, shared by its heads: pass idx_head_stride 0 to the gather)
+ *   kv_lens   : int32 [B], device memory
+ *   k, tail   : k >= 1, tail >= 0
+ *   idx       : int32 [B, n_q, Hs, k + tail], device memory, written whole
+ *   workspace : as for the attention entries: ck_decode_topk_workspace_size
+ *               bytes (0 when one workgroup serves a row), 256-byte aligned,
+ *               zeroed once; every launch leaves it zeroed.
+ * Errors as for the attention entries; nothing is launched on error. */
+int ck_decode_topk(const ck_decode_shape* shape, const float* scores, int32_t Hs, const int32_t* kv_lens,
+                   int32_t k, int32_t tail, int causal, int32_t* idx, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Workgroups per row and workspace bytes of ck_decode_topk for `shape` on a
+ * device with num_cus compute units (pure host arithmetic).  A row's
+ * workgroups meet at barriers, so rows x workgroups never exceeds num_cus
+ * (one workgroup per row when the rows alone reach it). */
+int ck_decode_topk_plan(const ck_decode_shape* shape, int32_t Hs, int32_t k, int32_t tail, int num_cus,
+                        int32_t* wgs_per_row, size_t* workspace_bytes);
+
+/* Workspace bytes of ck_decode_topk for `shape` on the current device. */
+int ck_decode_topk_workspace_size(const ck_decode_shape* shape, int32_t Hs, int32_t k, int32_t tail,
+                                  size_t* bytes);
+
 /* Step rows merged into prefix attention: the n_q verification queries of
  * an MTP step attend the cache prefix [0, L) plus their own draft rows,
  * whose K/V are passed separately instead of being written into the cache

@@ -240,3 +240,44 @@ def test_sparse_path_rejects(kw, W, n_kv, status):
     st = ck.lib().ck_decode_sparse_path(ctypes.byref(shape(**kw)), W, n_kv, ctypes.byref(path))
     assert st == status and path.value == -7
     assert ck.lib().ck_decode_sparse_path(ctypes.byref(shape()), 64, 1000, None) == -1
+
+
+# ----------------------------------------------------------------- top-k ----
+
+@pytest.mark.parametrize("B,n_q,Hs,cap,cus", [(1, 1, 2, 131072, 256), (1, 3, 4, 24007, 256), (32, 1, 8, 32768, 256),
+                                              (2, 1, 1, 3000, 256), (1, 1, 1, 500, 256), (7, 2, 3, 65536, 80)])
+def test_topk_plan_keeps_row_workgroups_resident(B, n_q, Hs, cap, cus):
+    p = ck.topk_plan((B, n_q, Hs, cap), k=2048, tail=64, num_cus=cus)
+    rows = B * n_q * Hs
+    P = p["wgs_per_row"]
+    assert 1 <= P <= 256 and P <= (cap + 1023) // 1024
+    if P > 1:  # a row's workgroups wait for each other: all must fit at once
+        assert rows * P <= cus and p["workspace_bytes"] > 0
+    else:
+        assert p["workspace_bytes"] == 0
+    if rows >= cus:
+        assert P == 1
+
+
+@pytest.mark.parametrize("scores_shape,kw,status", [
+    ((1, 1, 3, 1000), dict(k=10, num_kv_heads=2), -1),  # score heads neither 1 nor Hkv
+    ((1, 1, 2, 1000), dict(k=0), -1),
+    ((1, 1, 2, 1000), dict(k=10, tail=-1), -1),
+    ((1, 7, 2, 1000), dict(k=10), -2),
+    ((0, 1, 2, 1000), dict(k=10), -1),
+])
+def test_topk_plan_rejects(scores_shape, kw, status):
+    with pytest.raises(ck.CkError) as e:
+        ck.topk_plan(scores_shape, num_cus=256, **kw)
+    assert e.value.status == status
+
+
+def test_topk_entry_rejects_before_launch():
+    # argument errors come back before any HIP call (no GPU here)
+    s = ck.Shape(1, 1, 2, 2, 128, 1000)
+    L = ck.lib()
+    assert L.ck_decode_topk(ctypes.byref(s), None, 2, None, 10, 0, 0, None, None, 0, None) == -1
+    assert L.ck_decode_topk(ctypes.byref(s), ctypes.c_void_p(16), 3, ctypes.c_void_p(16), 10, 0, 0,
+                            ctypes.c_void_p(16), None, 0, None) == -1
+    assert L.ck_decode_topk(ctypes.byref(s), ctypes.c_void_p(18), 2, ctypes.c_void_p(16), 10, 0, 0,
+                            ctypes.c_void_p(16), None, 0, None) == -3

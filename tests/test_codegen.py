@@ -13,7 +13,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "decode_attention_flash_amd", "csrc", "ck_decode_attn.hip")
+SRCS = [os.path.join(ROOT, "decode_attention_flash_amd", "csrc", name) for name in ("ck_decode_attn.hip", "ck_topk.hip")]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
@@ -21,16 +21,19 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 def asm(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "k.s"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
-           SRC, "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return out.read_text()
+    text = ""
+    for n, src in enumerate(SRCS):
+        out = tmp_path_factory.mktemp("asm") / f"k{n}.s"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "--cuda-device-only", "-S",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+               src, "-o", str(out)]
+        subprocess.run(cmd, check=True, capture_output=True)
+        text += out.read_text()
+    return text
 
 
 def kernels(text):
-    names = re.findall(r"^(_ZN4ckda\w+):", text, flags=re.M)
+    names = re.findall(r"^(_ZN4ck(?:da|tk)\w+):", text, flags=re.M)
     for n in names:
         i = text.index(n + ":")
         j = text.index(".Lfunc_end", i)
@@ -53,4 +56,4 @@ def test_no_scratch_spills(asm):
     for name, body in kernels(asm):
         n += 1
         assert "scratch_store" not in body and "scratch_load" not in body, f"{name}: spills to scratch"
-    assert n >= 18
+    assert n >= 19

@@ -1,0 +1,135 @@
+"""GPU: top-k index lists (ck_decode_topk) against the oracle, bit-exact.
+
+Covers the sparse workload's shape (two score rows of 131072 cells, many
+workgroups per row meeting at barriers), rows full of ties and special
+values, causal windows, one workgroup per row (a large batch), unaligned
+score rows, workspace reuse across calls and graph replays, and the lists
+feeding the gather."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_flash_amd as ck
+import oracle
+from decode_attention_flash_amd import synth
+from gpu_common import DEV, assert_close, gather_gpu, note, oracle_ref
+
+pytestmark = pytest.mark.gpu
+
+
+def topk_gpu(scores, lens, k, tail=0, causal=False, num_kv_heads=None):
+    out = ck.decode_topk(scores.to(DEV), torch.as_tensor(np.asarray(lens), dtype=torch.int32).to(DEV), k,
+                         tail=tail, causal=causal, num_kv_heads=num_kv_heads)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(scores, lens, k, tail=0, causal=False, what=""):
+    got = topk_gpu(scores, lens, k, tail, causal)
+    ref = oracle.topk(scores.numpy(), np.asarray(lens, dtype=np.int32), k, tail, causal)
+    bad = np.argwhere(np.any(got != ref, axis=-1))
+    assert bad.size == 0, f"{what}: rows {bad[:4].tolist()} differ"
+    return got
+
+
+@pytest.mark.parametrize("n_kv", [32768, 131072])
+def test_sparse_workload_lists(n_kv):
+    """Two score rows (one per KV head), 2048 best + the last 64 cells."""
+    note(f"topk sparse workload n_kv={n_kv}")
+    sc = synth.index_scores(1, 1, 2, n_kv, 7000 + n_kv)
+    got = check(sc, [n_kv], 2048, 64, what=f"n_kv={n_kv}")
+    assert got.shape == (1, 1, 2, 2112) and np.all(np.diff(got, axis=-1) > 0)
+
+
+def test_ties_specials_causal_ragged():
+    """Small-integer scores (many exact ties), NaN, +-inf and signed zeros;
+    three causal queries per sequence; lengths 0, short, long and past the
+    capacity (clamped); two score heads."""
+    note("topk ties / specials / causal")
+    B, n_q, Hs, cap = 4, 3, 2, 20000
+    rng = np.random.default_rng(71)
+    sc = rng.integers(-4, 5, size=(B, n_q, Hs, cap)).astype(np.float32)
+    m = rng.random(sc.shape) < 0.05
+    sc[m] = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0], np.float32)[rng.integers(0, 5, int(m.sum()))]
+    check(torch.from_numpy(sc), [0, 700, cap, cap + 999], 700, 17, causal=True, what="ties")
+
+
+def test_all_candidates_and_tiny_windows():
+    """k at or above the candidates: every cell before the tail, then the tail."""
+    note("topk k >= candidates")
+    sc = synth.index_scores(3, 1, 1, 4096, 72)
+    check(sc, [1, 64, 4000], 4000, 5, what="k >= n")
+    check(sc, [3, 2, 4096], 10, 4, what="windows shorter than the tail")
+
+
+def test_one_workgroup_per_row():
+    """256 rows fill the chip: each row is one workgroup (no barriers), and
+    its scores no longer fit the register cache (re-read per pass)."""
+    note("topk one workgroup per row")
+    B, Hs, cap = 32, 8, 32768
+    plan = ck.topk_plan((B, 1, Hs, cap), 2048, 64)
+    assert plan["wgs_per_row"] == 1
+    lens = synth.ragged_lens(B, 512, cap, 4000)
+    sc = synth.index_scores(B, 1, Hs, cap, 73)
+    check(sc, lens, 2048, 64, what="batch")
+
+
+def test_unaligned_rows_and_shared_lists():
+    """cap % 4 != 0 (scores read one at a time) and one score row per query
+    shared by the KV heads (Hs = 1)."""
+    note("topk unaligned rows")
+    sc = synth.index_scores(2, 2, 1, 5003, 74)
+    got = topk_gpu(sc, [5003, 4111], 300, 9, causal=True, num_kv_heads=4)
+    ref = oracle.topk(sc.numpy(), np.array([5003, 4111], np.int32), 300, 9, True)
+    assert np.array_equal(got, ref)
+
+
+def test_workspace_reuse_and_graph_replay():
+    """The workspace is left zeroed: repeated calls with new scores and new
+    lengths, eagerly and replayed from a captured graph, all match."""
+    note("topk replay")
+    B, Hs, cap, k, tail = 1, 2, 65536, 2048, 64
+    sc_d = torch.empty((B, 1, Hs, cap), dtype=torch.float32, device=DEV)
+    lens_d = torch.empty((B,), dtype=torch.int32, device=DEV)
+    out_d = torch.empty((B, 1, Hs, k + tail), dtype=torch.int32, device=DEV)
+    cases = [(synth.index_scores(B, 1, Hs, cap, 80 + r), np.array([cap - 977 * r], np.int32)) for r in range(4)]
+    for sc, lens in cases:  # eager
+        sc_d.copy_(sc)
+        lens_d.copy_(torch.from_numpy(lens))
+        ck.decode_topk(sc_d, lens_d, k, tail=tail, out=out_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_d.cpu().numpy(), oracle.topk(sc.numpy(), lens, k, tail))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ck.decode_topk(sc_d, lens_d, k, tail=tail, out=out_d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ck.decode_topk(sc_d, lens_d, k, tail=tail, out=out_d)
+    for sc, lens in cases:
+        sc_d.copy_(sc)
+        lens_d.copy_(torch.from_numpy(lens))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_d.cpu().numpy(), oracle.topk(sc.numpy(), lens, k, tail))
+
+
+def test_lists_feed_the_gather():
+    """Selection then gathered attention equals the oracle's attention over
+    the oracle's lists."""
+    note("topk -> gather")
+    B, n_q, Hq, Hkv, D, cap = 1, 3, 16, 2, 128, 32768
+    L = 30000
+    k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1011)
+    q = synth.queries(B, n_q, Hq, D, 1011)
+    sc = synth.index_scores(B, n_q, Hkv, cap, 1011)
+    lists = topk_gpu(sc, [L], 2048, 64, causal=True)
+    ref_lists = oracle.topk(sc.numpy(), np.array([L], np.int32), 2048, 64, True)
+    assert np.array_equal(lists, ref_lists)
+    gpu = gather_gpu(q, k, v, [L], lists, causal=True)
+    assert_close(gpu, oracle_ref(q, k, v, [L], causal=True, idx=ref_lists), what="topk -> gather")
