@@ -29,10 +29,11 @@
 namespace cktk {
 
 constexpr int kThreads = 256;
-constexpr int kBlock = 4 * kThreads;  // positions per block: four per thread
-constexpr int kCacheBlocks = 4;       // blocks a workgroup keeps in registers
+constexpr int kPerThread = 16;                  // positions per thread in a super-block
+constexpr int kSuper = kPerThread * kThreads;   // positions per super-block
 constexpr int kBins = 2048;           // widest digit: 11 bits
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kAuxDevice = 16;  // sc1: served from the device's point of coherence
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
 // Per-row workspace, in 32-bit words: barrier and completion counters, the
@@ -41,7 +42,8 @@ constexpr int kWsCounters = 64;
 constexpr int kWsHist = kWsCounters;
 constexpr int kWsCounts = kWsHist + 3 * kBins;
 constexpr int kMaxWgPerRow = 256;
-constexpr int kWsRowWords = kWsCounts + 2 * kMaxWgPerRow;
+constexpr int kWsCand = kWsCounts + 2 * kMaxWgPerRow;  // then (key, position) pairs, per workgroup
+constexpr int kCand = 4096;                               // threshold-bin cells gathered in LDS
 
 struct TParams {
     const float* scores;      // [B, n_q, Hs, cap]
@@ -52,6 +54,9 @@ struct TParams {
     int32_t k, tail, W;
     int32_t P;                // workgroups per row
     int32_t vec4;             // score rows 16-byte aligned
+    int32_t cand_per_wg;      // pair slots per workgroup (its largest range)
+    uint32_t cand_off;        // word offset of the pair slots in a row's workspace
+    uint64_t ws_row_words;    // workspace words per row
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -72,6 +77,12 @@ __device__ __forceinline__ int ld_dev(const uint32_t* p) {
     return (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every store and atomic this wave issued has completed.
@@ -104,14 +115,51 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
     __shared__ uint32_t lh[kBins];
     __shared__ uint32_t red[kThreads / 64 + 1];
-    __shared__ uint32_t pick[2];
+    __shared__ uint32_t pick[3];
     __shared__ uint32_t offs[2];
+    __shared__ uint32_t cpre[kMaxWgPerRow];
+    __shared__ uint32_t ck_key[kCand];
+    __shared__ int32_t ck_pos[kCand];
 
     const int tid = threadIdx.x;
     const int row = blockIdx.x / p.P, w = blockIdx.x % p.P;
     const int bi = row / p.Hs;  // row = (b * n_q + i) * Hs + h
     const int i = bi % p.n_q, b = bi / p.n_q;
-    if (tid < 2) pick[tid] = 0u;
+    if (tid < 3) pick[tid] = 0u;
+
+    // Positions of this workgroup: whole super-blocks of kSuper positions,
+    // split by the capacity, which is known before the length arrives, so
+    // the first score loads go out together with the length load.  Thread t
+    // holds positions 16t .. 16t+15 of each super-block.
+    const int nsb = (p.cap + kSuper - 1) / kSuper;
+    const int per = (nsb + p.P - 1) / p.P;
+    const int sb0 = min(nsb, w * per), sb1 = min(nsb, sb0 + per);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scores + (size_t)row * p.cap, (uint32_t)p.cap * 4u);
+    auto load_raw = [&](int sb, float x[kPerThread]) {
+        const uint32_t pos = (uint32_t)(sb * kSuper + kPerThread * tid);
+        if (p.vec4) {
+#pragma unroll
+            for (int c = 0; c < kPerThread / 4; ++c) {
+                const float4 v =
+                    __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (pos + 4 * c) * 4u, 0, 0));
+                x[4 * c] = v.x;
+                x[4 * c + 1] = v.y;
+                x[4 * c + 2] = v.z;
+                x[4 * c + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j)
+                x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (pos + j) * 4u, 0, 0));
+        }
+    };
+    float xc[kPerThread];
+    if (sb0 < sb1) {
+        load_raw(sb0, xc);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) xc[j] = 0.f;
+    }
 
     const int L_raw = p.kv_lens[b];
     const int L = L_raw < 0 ? 0 : (L_raw > p.cap ? p.cap : L_raw);
@@ -124,12 +172,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
     const int n_take = min(p.k, n_cand);
     int32_t* out = p.idx + (size_t)row * p.W;
 
-    // Positions of this workgroup: whole blocks, the same split in every
-    // workgroup of the row.
-    const int nblk = (n_cand + kBlock - 1) / kBlock;
-    const int per = (nblk + p.P - 1) / p.P;
-    const int blk0 = min(nblk, w * per), blk1 = min(nblk, blk0 + per);
-
     // The tail and the padding after the selection.
     if (w == 0) {
         for (int s = n_take + tid; s < p.W; s += kThreads) {
@@ -138,59 +180,37 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
         }
     }
     if (n_cand <= p.k) {  // every candidate is selected: position j goes to slot j
-        for (int pos = blk0 * kBlock + tid; pos < min(blk1 * kBlock, n_cand); pos += kThreads) out[pos] = pos;
+        for (int pos = sb0 * kSuper + tid; pos < min(sb1 * kSuper, n_cand); pos += kThreads) out[pos] = pos;
         return;
     }
 
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scores + (size_t)row * p.cap, (uint32_t)n_cand * 4u);
-    auto load_keys = [&](int blk, uint32_t kk[4]) {
-        const int pos = blk * kBlock + 4 * tid;
-        if (p.vec4) {
-            const uint32_t off = pos < n_cand ? (uint32_t)pos * 4u : 0x80000000u;
-            const float4 x = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-            kk[0] = key_of(x.x);
-            kk[1] = key_of(x.y);
-            kk[2] = key_of(x.z);
-            kk[3] = key_of(x.w);
-        } else {
+    // Keys of a super-block; positions past the candidates get key 0.
+    auto to_keys = [&](const float x[kPerThread], int sb, uint32_t kk[kPerThread]) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t off = pos + j < n_cand ? (uint32_t)(pos + j) * 4u : 0x80000000u;
-                kk[j] = key_of(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)));
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (pos + j >= n_cand) kk[j] = 0u;
+        for (int j = 0; j < kPerThread; ++j)
+            kk[j] = sb * kSuper + kPerThread * tid + j < n_cand ? key_of(x[j]) : 0u;
     };
-    uint32_t kc[kCacheBlocks][4];
-#pragma unroll
-    for (int c = 0; c < kCacheBlocks; ++c) {
-        if (blk0 + c < blk1) {
-            load_keys(blk0 + c, kc[c]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kc[c][j] = 0u;
-        }
-    }
-    // Calls f(key, position) for this thread's candidates, block by block.
+    uint32_t kc[kPerThread];  // the first super-block stays in registers
+    to_keys(xc, sb0, kc);
+    // Calls f(key, position) for this thread's positions, super-block by
+    // super-block (later ones are read again at each pass).
     auto for_keys = [&](auto&& f) {
+        if (sb0 < sb1) {
 #pragma unroll
-        for (int c = 0; c < kCacheBlocks; ++c)
-            if (blk0 + c < blk1) {
+            for (int j = 0; j < kPerThread; ++j) f(kc[j], sb0 * kSuper + kPerThread * tid + j);
+        }
+        for (int sb = sb0 + 1; sb < sb1; ++sb) {
+            float x[kPerThread];
+            uint32_t kk[kPerThread];
+            load_raw(sb, x);
+            to_keys(x, sb, kk);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) f(kc[c][j], (blk0 + c) * kBlock + 4 * tid + j);
-            }
-        for (int blk = blk0 + kCacheBlocks; blk < blk1; ++blk) {
-            uint32_t kk[4];
-            load_keys(blk, kk);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) f(kk[j], blk * kBlock + 4 * tid + j);
+            for (int j = 0; j < kPerThread; ++j) f(kk[j], sb * kSuper + kPerThread * tid + j);
         }
     };
 
     const bool shared_row = p.P > 1;
-    uint32_t* ws = p.ws + (size_t)row * kWsRowWords;
+    uint32_t* ws = p.ws + (size_t)row * p.ws_row_words;
     uint32_t* ctr = ws;  // [0] barrier arrivals, [1] completions
     int barriers = 0;
     auto row_barrier = [&]() {
@@ -208,14 +228,56 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
         __syncthreads();
     };
 
-    // ---- three radix levels: 11, 11 and 10 bits of the key, from the top ----
+    // Finds the digit whose bin holds the k_rem-th largest key, scanning
+    // bins from the largest digit down; hist is the row's histogram in the
+    // workspace (global) or this workgroup's in LDS.  Every thread gets the
+    // digit, the count of keys in larger bins and the bin's own count.
+    auto find_bin = [&](const uint32_t* hist, bool global, int nb, int k_need, uint32_t* n_above,
+                        uint32_t* n_bin) -> uint32_t {
+        const int bpt = nb / kThreads;  // thread t owns bins nb-1-(t*bpt+j)
+        uint32_t cnt[kBins / kThreads];
+        uint32_t tsum = 0;
+#pragma unroll
+        for (int j = 0; j < kBins / kThreads; ++j) {
+            uint32_t c = 0;
+            if (j < bpt) {
+                const int d = nb - 1 - (tid * bpt + j);
+                c = global ? (uint32_t)ld_dev(hist + d) : hist[d];
+            }
+            cnt[j] = c;
+            tsum += c;
+        }
+        uint32_t total;
+        const uint32_t before = block_scan(tsum, red, &total);
+        if (before < (uint32_t)k_need && (uint32_t)k_need <= before + tsum) {
+            uint32_t acc = before;
+#pragma unroll
+            for (int j = 0; j < kBins / kThreads; ++j) {
+                if (j < bpt && acc < (uint32_t)k_need && acc + cnt[j] >= (uint32_t)k_need) {
+                    pick[0] = (uint32_t)(nb - 1 - (tid * bpt + j));
+                    pick[1] = acc;
+                    pick[2] = cnt[j];
+                }
+                acc += cnt[j];
+            }
+        }
+        __syncthreads();
+        const uint32_t d = pick[0];
+        *n_above = pick[1];
+        *n_bin = pick[2];
+        __syncthreads();
+        return d;
+    };
+
+    // One radix level over the row: histogram of the digit below `above` of
+    // the keys whose higher digits equal prefix, summed over the row's
+    // workgroups, then its bin search.  Returns the chosen bin's count.
     uint32_t prefix = 0;
     int k_rem = p.k;
-#pragma unroll 1
-    for (int lvl = 0; lvl < 3; ++lvl) {
+    auto row_level = [&](int lvl) -> uint32_t {
         const int shift = lvl == 0 ? 21 : (lvl == 1 ? 10 : 0);
         const int nb = lvl == 2 ? 1024 : 2048;
-        const int above = lvl == 0 ? 32 : (lvl == 1 ? 21 : 10);  // bits fixed so far start here
+        const int above = lvl == 0 ? 32 : (lvl == 1 ? 21 : 10);
         for (int j = tid; j < nb; j += kThreads) lh[j] = 0u;
         __syncthreads();
         for_keys([&](uint32_t key, int) {
@@ -231,115 +293,190 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             }
             row_barrier();
         }
-        // Thread t owns bins nb-1-(t*bpt+j), j < bpt: the scan runs from the
-        // largest digit down.
-        const int bpt = nb / kThreads;
-        uint32_t cnt[kBins / kThreads];
-        uint32_t tsum = 0;
-#pragma unroll
-        for (int j = 0; j < kBins / kThreads; ++j) {
-            uint32_t c = 0;
-            if (j < bpt) {
-                const int d = nb - 1 - (tid * bpt + j);
-                c = shared_row ? (uint32_t)ld_dev(gh + d) : lh[d];
-            }
-            cnt[j] = c;
-            tsum += c;
-        }
-        uint32_t total;
-        const uint32_t before = block_scan(tsum, red, &total);
-        if (before < (uint32_t)k_rem && (uint32_t)k_rem <= before + tsum) {
-            uint32_t acc = before;
-#pragma unroll
-            for (int j = 0; j < kBins / kThreads; ++j) {
-                if (j < bpt && acc + cnt[j] >= (uint32_t)k_rem && acc < (uint32_t)k_rem) {
-                    pick[0] = (uint32_t)(nb - 1 - (tid * bpt + j));
-                    pick[1] = acc;
-                }
-                acc += cnt[j];
-            }
-        }
-        __syncthreads();
-        const uint32_t digit = pick[0], n_above = pick[1];
-        __syncthreads();
+        uint32_t n_above, n_bin;
+        const uint32_t digit = find_bin(shared_row ? gh : lh, shared_row, nb, k_rem, &n_above, &n_bin);
         prefix = (prefix << (lvl == 2 ? 10 : 11)) | digit;
         k_rem -= (int)n_above;
-    }
-    const uint32_t T = prefix;        // key of the k-th largest candidate
-    const int n_eq_take = k_rem;      // candidates with key T to take, lowest position first
+        return n_bin;
+    };
 
-    // ---- this workgroup's counts above / equal to T, and its output offset ----
-    uint32_t g_t = 0, e_t = 0;
-    for_keys([&](uint32_t key, int) {
-        g_t += key > T ? 1u : 0u;
-        e_t += key == T ? 1u : 0u;
-    });
-    uint32_t g_w, e_w;
-    block_scan(g_t, red, &g_w);
-    block_scan(e_t, red, &e_w);
+    // ---- level 0: the top 11 bits over the whole row ----
+    const uint32_t c_bin = row_level(0);
+    uint32_t T;           // key of the k-th largest candidate
+    int n_eq_take;        // candidates with key T to take, lowest position first
     uint32_t out_base = 0, eq_base = 0;
-    if (shared_row) {
-        uint32_t* counts = ws + kWsCounts;
+    uint32_t* counts = ws + kWsCounts;
+
+    if (shared_row && c_bin <= (uint32_t)kCand) {
+        // ---- the threshold bin fits in LDS: exchange it once and finish here ----
+        // Each workgroup publishes how many of its keys lie above the bin
+        // (all selected) and writes the bin's (key, position) pairs to its
+        // own slots; after one barrier every workgroup gathers the pairs and
+        // selects among them in LDS, so all reach the same threshold.
+        const uint32_t d0 = prefix;
+        uint32_t a_t = 0, c_t = 0;
+        for_keys([&](uint32_t key, int) {
+            a_t += key != 0u && (key >> 21) > d0 ? 1u : 0u;
+            c_t += key != 0u && (key >> 21) == d0 ? 1u : 0u;
+        });
+        uint32_t a_w, c_w;
+        block_scan(a_t, red, &a_w);
+        uint32_t slot = block_scan(c_t, red, &c_w);
+        uint64_t* mine = reinterpret_cast<uint64_t*>(ws + p.cand_off) + (size_t)w * p.cand_per_wg;
+        for_keys([&](uint32_t key, int pos) {
+            if (key != 0u && (key >> 21) == d0) st_dev64(mine + slot++, ((uint64_t)(uint32_t)pos << 32) | key);
+        });
         if (tid == 0) {
-            st_dev(counts + 2 * w, g_w);
-            st_dev(counts + 2 * w + 1, e_w);
+            st_dev(counts + 2 * w, a_w);
+            st_dev(counts + 2 * w + 1, c_w);
         }
         row_barrier();
-        // Thread t < P holds workgroup t's counts; scans give every
-        // workgroup's equal-key rank start and output offset.
-        const uint32_t g = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
-        const uint32_t e = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid + 1) : 0u;
-        uint32_t dummy;
-        const uint32_t E = block_scan(e, red, &dummy);
-        const int left = n_eq_take - (int)E;
-        const uint32_t take = g + (uint32_t)(left <= 0 ? 0 : (left < (int)e ? left : (int)e));
-        const uint32_t S = block_scan(take, red, &dummy);
-        if (tid == w) {
-            offs[0] = S;
-            offs[1] = E;
+        const uint32_t a = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
+        const uint32_t c = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid + 1) : 0u;
+        uint32_t a_tot, c_tot;
+        const uint32_t A = block_scan(a, red, &a_tot);
+        const uint32_t Cp = block_scan(c, red, &c_tot);
+        if (tid < p.P) cpre[tid] = Cp;
+        if (tid == w) offs[0] = A;
+        __syncthreads();
+        const int n_c = (int)min(c_tot, (uint32_t)kCand);
+        // Entry e comes from workgroup t with cpre[t] <= e < cpre[t + 1].  All
+        // of a thread's loads go out before the first is stored (one round trip).
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(ws + p.cand_off, (uint32_t)((size_t)p.P * p.cand_per_wg * 8u));
+        uint64_t got[kCand / kThreads];
+#pragma unroll
+        for (int u = 0; u < kCand / kThreads; ++u) {
+            const int e = tid + u * kThreads;
+            uint32_t off = 0x80000000u;
+            if (e < n_c) {
+                int lo = 0, hi = p.P - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (cpre[mid] <= (uint32_t)e) lo = mid;
+                    else hi = mid - 1;
+                }
+                off = (uint32_t)(((size_t)lo * p.cand_per_wg + (size_t)(e - (int)cpre[lo])) * 8u);
+            }
+            got[u] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, kAuxDevice));
+        }
+#pragma unroll
+        for (int u = 0; u < kCand / kThreads; ++u) {
+            const int e = tid + u * kThreads;
+            if (e < n_c) {
+                ck_key[e] = (uint32_t)got[u];
+                ck_pos[e] = (int32_t)(got[u] >> 32);
+            }
         }
         __syncthreads();
-        out_base = offs[0];
-        eq_base = offs[1];
+        // the remaining 21 bits in two LDS digits (11 and 10)
+#pragma unroll 1
+        for (int lvl = 1; lvl < 3; ++lvl) {
+            const int shift = lvl == 1 ? 10 : 0;
+            const int nb = lvl == 1 ? 2048 : 1024;
+            const int above = lvl == 1 ? 21 : 10;
+            for (int j = tid; j < nb; j += kThreads) lh[j] = 0u;
+            __syncthreads();
+            for (int e = tid; e < n_c; e += kThreads) {
+                const uint32_t key = ck_key[e];
+                if ((key >> above) == prefix) atomicAdd(&lh[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+            }
+            __syncthreads();
+            uint32_t n_above, n_bin;
+            const uint32_t digit = find_bin(lh, false, nb, k_rem, &n_above, &n_bin);
+            prefix = (prefix << (lvl == 2 ? 10 : 11)) | digit;
+            k_rem -= (int)n_above;
+        }
+        T = prefix;
+        n_eq_take = k_rem;
+        // selected pairs before this workgroup's range, and equal keys there
+        const int start = sb0 * kSuper;
+        uint32_t gb_t = 0, eb_t = 0;
+        for (int e = tid; e < n_c; e += kThreads) {
+            gb_t += ck_key[e] > T && ck_pos[e] < start ? 1u : 0u;
+            eb_t += ck_key[e] == T && ck_pos[e] < start ? 1u : 0u;
+        }
+        uint32_t gb, eb;
+        block_scan(gb_t, red, &gb);
+        block_scan(eb_t, red, &eb);
+        out_base = offs[0] + gb + min(eb, (uint32_t)n_eq_take);
+        eq_base = eb;
+    } else {
+        // ---- the next two digits over the row, then the counts exchange ----
+        row_level(1);
+        row_level(2);
+        T = prefix;
+        n_eq_take = k_rem;
+        uint32_t g_t = 0, e_t = 0;
+        for_keys([&](uint32_t key, int) {
+            g_t += key > T ? 1u : 0u;
+            e_t += key == T ? 1u : 0u;
+        });
+        uint32_t g_w, e_w;
+        block_scan(g_t, red, &g_w);
+        block_scan(e_t, red, &e_w);
+        if (shared_row) {
+            if (tid == 0) {
+                st_dev(counts + 2 * w, g_w);
+                st_dev(counts + 2 * w + 1, e_w);
+            }
+            row_barrier();
+            // Thread t < P holds workgroup t's counts; scans give every
+            // workgroup's equal-key rank start and output offset.
+            const uint32_t g = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
+            const uint32_t e = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid + 1) : 0u;
+            uint32_t dummy;
+            const uint32_t E = block_scan(e, red, &dummy);
+            const int left = n_eq_take - (int)E;
+            const uint32_t take = g + (uint32_t)(left <= 0 ? 0 : (left < (int)e ? left : (int)e));
+            const uint32_t S = block_scan(take, red, &dummy);
+            if (tid == w) {
+                offs[0] = S;
+                offs[1] = E;
+            }
+            __syncthreads();
+            out_base = offs[0];
+            eq_base = offs[1];
+        }
     }
 
     // ---- write the selected positions in position order ----
     uint32_t run_sel = out_base, run_eq = eq_base;
-    auto emit_block = [&](const uint32_t kk[4], int blk) {
+    auto emit = [&](const uint32_t kk[kPerThread], int sb) {
         uint32_t ne = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ne += kk[j] == T ? 1u : 0u;
+        for (int j = 0; j < kPerThread; ++j) ne += kk[j] == T ? 1u : 0u;
         uint32_t eq_tot;
         uint32_t eq_rank = run_eq + block_scan(ne, red, &eq_tot);
-        bool sel[4];
-        uint32_t ns = 0;
+        uint32_t sel = 0, ns = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kPerThread; ++j) {
             const bool eq = kk[j] == T;
-            sel[j] = kk[j] > T || (eq && eq_rank < (uint32_t)n_eq_take);
+            const bool take = kk[j] > T || (eq && eq_rank < (uint32_t)n_eq_take);
             eq_rank += eq ? 1u : 0u;
-            ns += sel[j] ? 1u : 0u;
+            sel |= (take ? 1u : 0u) << j;
+            ns += take ? 1u : 0u;
         }
         uint32_t sel_tot;
         uint32_t slot = run_sel + block_scan(ns, red, &sel_tot);
         // (slot < n_take always holds when the counts agree; the bound keeps
         // every store inside the row whatever they read)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (sel[j]) {
-                if (slot < (uint32_t)n_take) out[slot] = blk * kBlock + 4 * tid + j;
+        for (int j = 0; j < kPerThread; ++j)
+            if ((sel >> j) & 1u) {
+                if (slot < (uint32_t)n_take) out[slot] = sb * kSuper + kPerThread * tid + j;
                 ++slot;
             }
         run_sel += sel_tot;
         run_eq += eq_tot;
     };
-#pragma unroll
-    for (int c = 0; c < kCacheBlocks; ++c)
-        if (blk0 + c < blk1) emit_block(kc[c], blk0 + c);
-    for (int blk = blk0 + kCacheBlocks; blk < blk1; ++blk) {
-        uint32_t kk[4];
-        load_keys(blk, kk);
-        emit_block(kk, blk);
+    if (sb0 < sb1) emit(kc, sb0);
+    for (int sb = sb0 + 1; sb < sb1; ++sb) {
+        float x[kPerThread];
+        uint32_t kk[kPerThread];
+        load_raw(sb, x);
+        to_keys(x, sb, kk);
+        emit(kk, sb);
     }
 
     // ---- leave the row's workspace zeroed for the next launch ----
@@ -367,24 +504,35 @@ static int device_cus(int* cus) {
     return CK_OK;
 }
 
-static int plan(const ck_decode_shape* s, int32_t Hs, int32_t k, int32_t tail, int num_cus, int32_t* P,
-                size_t* ws_bytes) {
-    if (!s || !P || !ws_bytes) return CK_ERR_ARG;
+struct Plan {
+    int32_t P;            // workgroups per row
+    int32_t cand_per_wg;  // pair slots per workgroup
+    uint64_t row_words;   // workspace words per row
+    size_t ws_bytes;
+};
+
+static int plan(const ck_decode_shape* s, int32_t Hs, int32_t k, int32_t tail, int num_cus, Plan* pl) {
+    if (!s || !pl) return CK_ERR_ARG;
     if (s->B < 1 || s->n_q < 1 || s->Hkv < 1 || s->cap < 1) return CK_ERR_ARG;
     if (s->n_q > CK_MAX_NQ) return CK_ERR_UNSUPPORTED;
     if (Hs != 1 && Hs != s->Hkv) return CK_ERR_ARG;
     if (k < 1 || tail < 0 || (int64_t)k + tail >= ((int64_t)1 << 31) || num_cus < 1) return CK_ERR_ARG;
-    if ((int64_t)s->cap * 4 + kBlock * 4 >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+    if ((int64_t)s->cap * 4 + kSuper * 4 >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)s->B * s->n_q * Hs;
     if (rows * ((int64_t)k + tail) >= ((int64_t)1 << 40)) return CK_ERR_UNSUPPORTED;
-    const int64_t blocks = ((int64_t)s->cap + kBlock - 1) / kBlock;
+    const int64_t blocks = ((int64_t)s->cap + kSuper - 1) / kSuper;
     int64_t wg = rows >= num_cus ? 1 : num_cus / rows;  // all of a row's workgroups resident at once
+    // at least one super-block per workgroup: fewer workgroups meet sooner
+    // at the barriers and add fewer histogram atomics
     if (wg > blocks) wg = blocks;
     if (wg > kMaxWgPerRow) wg = kMaxWgPerRow;
     if (wg < 1) wg = 1;
     if (rows * wg >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
-    *P = (int32_t)wg;
-    *ws_bytes = wg > 1 ? (size_t)rows * kWsRowWords * sizeof(uint32_t) : 0;
+    const int64_t per_max = (blocks + wg - 1) / wg;
+    pl->P = (int32_t)wg;
+    pl->cand_per_wg = (int32_t)(per_max * kSuper);
+    pl->row_words = (uint64_t)kWsCand + (uint64_t)wg * (uint64_t)pl->cand_per_wg * 2u;
+    pl->ws_bytes = wg > 1 ? (size_t)rows * (size_t)pl->row_words * sizeof(uint32_t) : 0;
     return CK_OK;
 }
 
@@ -394,36 +542,45 @@ extern "C" {
 
 int ck_decode_topk_plan(const ck_decode_shape* shape, int32_t Hs, int32_t k, int32_t tail, int num_cus,
                         int32_t* wgs_per_row, size_t* workspace_bytes) {
-    return cktk::plan(shape, Hs, k, tail, num_cus, wgs_per_row, workspace_bytes);
+    if (!wgs_per_row || !workspace_bytes) return CK_ERR_ARG;
+    cktk::Plan pl;
+    const int st = cktk::plan(shape, Hs, k, tail, num_cus, &pl);
+    if (st != CK_OK) return st;
+    *wgs_per_row = pl.P;
+    *workspace_bytes = pl.ws_bytes;
+    return CK_OK;
 }
 
 int ck_decode_topk_workspace_size(const ck_decode_shape* shape, int32_t Hs, int32_t k, int32_t tail,
                                   size_t* bytes) {
-    int32_t P = 0;
-    int st = cktk::plan(shape, Hs, k, tail, 1, &P, bytes);
+    if (!bytes) return CK_ERR_ARG;
+    cktk::Plan pl;
+    int st = cktk::plan(shape, Hs, k, tail, 1, &pl);
     if (st != CK_OK) return st;
     int cus = 0;
     st = cktk::device_cus(&cus);
     if (st != CK_OK) return st;
-    return cktk::plan(shape, Hs, k, tail, cus, &P, bytes);
+    st = cktk::plan(shape, Hs, k, tail, cus, &pl);
+    if (st != CK_OK) return st;
+    *bytes = pl.ws_bytes;
+    return CK_OK;
 }
 
 int ck_decode_topk(const ck_decode_shape* shape, const float* scores, int32_t Hs, const int32_t* kv_lens,
                    int32_t k, int32_t tail, int causal, int32_t* idx, void* workspace, size_t workspace_bytes,
                    void* stream) {
-    int32_t P = 0;
-    size_t need = 0;
-    int st = cktk::plan(shape, Hs, k, tail, 1, &P, &need);
+    cktk::Plan pl;
+    int st = cktk::plan(shape, Hs, k, tail, 1, &pl);
     if (st != CK_OK) return st;
     if (!scores || !kv_lens || !idx) return CK_ERR_ARG;
     if (((uintptr_t)scores & 3) || ((uintptr_t)kv_lens & 3) || ((uintptr_t)idx & 3)) return CK_ERR_ALIGN;
     int cus = 0;
     st = cktk::device_cus(&cus);
     if (st != CK_OK) return st;
-    st = cktk::plan(shape, Hs, k, tail, cus, &P, &need);
+    st = cktk::plan(shape, Hs, k, tail, cus, &pl);
     if (st != CK_OK) return st;
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need) return CK_ERR_WORKSPACE;
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return CK_ERR_WORKSPACE;
         if ((uintptr_t)workspace & 255) return CK_ERR_ALIGN;
     }
     cktk::TParams p{};
@@ -439,10 +596,13 @@ int ck_decode_topk(const ck_decode_shape* shape, const float* scores, int32_t Hs
     p.k = k;
     p.tail = tail;
     p.W = k + tail;
-    p.P = P;
+    p.P = pl.P;
     p.vec4 = ((uintptr_t)scores & 15) == 0 && shape->cap % 4 == 0 ? 1 : 0;
+    p.cand_per_wg = pl.cand_per_wg;
+    p.cand_off = (uint32_t)cktk::kWsCand;
+    p.ws_row_words = pl.row_words;
     const int rows = shape->B * shape->n_q * Hs;
-    hipLaunchKernelGGL(cktk::topk_kernel, dim3((unsigned)(rows * P)), dim3(cktk::kThreads), 0,
+    hipLaunchKernelGGL(cktk::topk_kernel, dim3((unsigned)(rows * pl.P)), dim3(cktk::kThreads), 0,
                        (hipStream_t)stream, p);
     return hipGetLastError() == hipSuccess ? CK_OK : CK_ERR_HIP;
 }
