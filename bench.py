@@ -216,6 +216,40 @@ def gather_case(stack, n_kv, W_sel, tail, steps, warmup, n_layers=None, block=0)
                 kv_gbs=kv_bytes / us / 1e3, frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS), idxs
 
 
+def topk_case(B, n_q, Hs, cap, lens, k, tail, steps, warmup, with_gather=None):
+    """Top-k index lists over per-layer score buffers (decode_topk); with
+    with_gather = (stack, Hq, D), each layer's lists also feed the gathered
+    attention in the same graph (the whole sparse step of a layer)."""
+    import torch
+    import decode_attention_flash_amd as ck
+    from decode_attention_flash_amd import synth
+    score_bytes = B * n_q * Hs * cap * 4
+    n = layers_for(score_bytes)
+    if with_gather is not None:
+        n = min(n, len(with_gather[0].k))
+    scs = [synth.index_scores(B, n_q, Hs, cap, 90 + l, device="cuda") for l in range(n)]
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
+    idxs = [torch.empty((B, n_q, Hs, k + tail), dtype=torch.int32, device="cuda") for _ in range(n)]
+    if with_gather is None:
+        def launch(l):
+            ck.decode_topk(scs[l], lens_d, k, tail=tail, out=idxs[l])
+    else:
+        st, Hq, D = with_gather
+        qs = [synth.queries(B, n_q, Hq, D, 13 + l, device="cuda") for l in range(n)]
+        outs = [torch.empty((B, n_q, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+        ws = ck.new_workspace(ck.shape_of(qs[0], st.k[0]), W=k + tail)
+
+        def launch(l):
+            ck.decode_topk(scs[l], lens_d, k, tail=tail, out=idxs[l])
+            ck.decode_attn_gather(qs[l], st.k[l], st.v[l], lens_d, idxs[l], out=outs[l], workspace=ws)
+    ms, us = time_graph(launch, n, steps, warmup)
+    _, us_torch = time_graph(lambda l: torch.topk(scs[l][..., :int(max(lens)) - tail], k, dim=-1, sorted=False),
+                             n, steps, warmup)
+    P = ck.topk_plan((B, n_q, Hs, cap), k, tail)["wgs_per_row"]
+    return dict(us=us, ms_per_replay=ms, layers=n, score_bytes=score_bytes, wgs_per_row=P,
+                torch_topk_us=us_torch)
+
+
 def calibrate_copy(nbytes: int = 1 << 28, reps: int = 3) -> None:
     """A plain device copy of known size, so that a counter profile of this
     run can scale its byte counters (FETCH_SIZE / WRITE_SIZE) against it."""
@@ -370,8 +404,28 @@ def main():
                     f"(chosen: {path})")
                 sweep["sparse"].append(dict(n_kv=n_kv, selection=sel, chosen=path, gather=rg, masked=rm))
                 del masks
+            # the whole sparse step of a layer: top-k lists from scores, then the gather
+            rs = topk_case(1, 1, 2, n_kv, [n_kv], W_sel, tail, args.steps, args.warmup,
+                           with_gather=(st, 16, 128))
+            log(f"sparse n_kv={n_kv}: top-k + gather {rs['us']:.2f} us")
+            sweep["sparse"].append(dict(n_kv=n_kv, selection="top-k of scores", select_and_gather=rs))
             del st
             torch.cuda.empty_cache()
+
+    if not args.headline_only:
+        # top-k index lists from one score per cell: the sparse workload's two
+        # rows (2048 + 64 cells), then selection and gathered attention as one
+        # step, and a large batch (one workgroup per row)
+        from decode_attention_flash_amd import synth
+        sweep["topk"] = []
+        for n_kv in (32768, 65536, 131072):
+            r = topk_case(1, 1, 2, n_kv, [n_kv], 2048, 64, args.steps, args.warmup)
+            log(f"top-k n_kv={n_kv}: {r['us']:.2f} us (torch.topk {r['torch_topk_us']:.2f})")
+            sweep["topk"].append(dict(n_kv=n_kv, k=2048, tail=64, **r))
+        lens = synth.ragged_lens(32, 512, 32768, 4000)
+        r = topk_case(32, 1, 8, 32768, lens.tolist(), 2048, 64, args.steps, args.warmup)
+        log(f"top-k B=32 x 8 heads: {r['us']:.2f} us (torch.topk {r['torch_topk_us']:.2f})")
+        sweep["topk_batch"] = dict(B=32, Hs=8, cap=32768, k=2048, tail=64, **r)
 
     if not args.headline_only:
         # paged INT8 cache: the same head_dim-256 layer and the ragged batch
