@@ -310,11 +310,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--kv-len", type=int, default=8000)
     ap.add_argument("--headline-only", action="store_true", help="skip the sweeps and the CPU leg")
+    ap.add_argument("--only", default="",
+                    help="comma-separated sweep groups to run (dense, sparse, topk, q8); skips the CPU leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (reference for counter profiles)")
     args = ap.parse_args()
+    groups = {"dense", "sparse", "topk", "q8"}
+    if args.headline_only:
+        groups = set()
+    elif args.only:
+        groups = {g.strip() for g in args.only.split(",") if g.strip()}
+        unknown = groups - {"dense", "sparse", "topk", "q8"}
+        if unknown:
+            ap.error(f"unknown sweep groups: {sorted(unknown)}")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -333,7 +343,7 @@ def main():
     Hq, Hkv, D, cap = 16, 4, 256, 24007
     L0 = args.kv_len
     lens_sweep = [1000, 3000, 8000, 24000]
-    n_max = 4 if args.headline_only else max(layers_for(4 * Hkv * D * L) for L in lens_sweep + [L0])
+    n_max = max(layers_for(4 * Hkv * D * L) for L in lens_sweep + [L0]) if "dense" in groups else 4
     n_max = max(n_max, layers_for(4 * Hkv * D * L0))
     log(f"allocating {n_max} layer caches of capacity {cap}")
     stack = Stack(n_max, 1, cap, Hkv, D, 1002)
@@ -346,7 +356,7 @@ def main():
         calibrate_copy()
 
     sweep = {}
-    if not args.headline_only:
+    if "dense" in groups:
         sweep["kv_len"] = []
         for L in lens_sweep:
             r = dense_case(stack, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup)
@@ -384,6 +394,8 @@ def main():
         sweep["ragged_batch"] = dict(B=32, sum_kv_len=int(lens.sum()), **r)
         del st
         torch.cuda.empty_cache()
+    if "sparse" in groups:
+        from decode_attention_flash_amd import synth
         # sparse: gathered top-k lists vs the masked full-window scan, with the
         # 2048 cells drawn one by one or as 32 aligned runs of 64 (tiles skip)
         sweep["sparse"] = []
@@ -412,7 +424,7 @@ def main():
             del st
             torch.cuda.empty_cache()
 
-    if not args.headline_only:
+    if "topk" in groups:
         # top-k index lists from one score per cell: the sparse workload's two
         # rows (2048 + 64 cells), then selection and gathered attention as one
         # step, and a large batch (one workgroup per row)
@@ -427,7 +439,7 @@ def main():
         log(f"top-k B=32 x 8 heads: {r['us']:.2f} us (torch.topk {r['torch_topk_us']:.2f})")
         sweep["topk_batch"] = dict(B=32, Hs=8, cap=32768, k=2048, tail=64, **r)
 
-    if not args.headline_only:
+    if "q8" in groups:
         # paged INT8 cache: the same head_dim-256 layer and the ragged batch
         sweep["q8_kv_len"] = []
         n_q8 = max(layers_for(2 * Hkv * (D + 4) * L) for L in lens_sweep)
@@ -448,7 +460,7 @@ def main():
         torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu and not args.headline_only:
+    if not args.no_cpu and not args.headline_only and not args.only:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(args.cpu_seconds)
 
