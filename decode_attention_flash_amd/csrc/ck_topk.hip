@@ -88,33 +88,50 @@ __device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
 // Wait until every store and atomic this wave issued has completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// within each row of 16 lanes, shifts by 1, 2 and 3 of the input, then by 4
+// and 8 of the running sum (on the lanes that have such a predecessor); then
+// row 0's total goes to row 1 and row 2's to row 3 (broadcast of lane 15),
+// and lane 31's running total to rows 2 and 3.  Lanes a move does not reach
+// add 0.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+    uint32_t v = x;
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x113, 0xf, 0xf, true);  // row_shr:3
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xe, true);  // row_shr:4, lanes 4-15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xc, true);  // row_shr:8, lanes 8-15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, true);  // row_bcast:15 -> rows 1, 3
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, true);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
 // Exclusive prefix sum over the workgroup's threads in thread order; also
-// returns the total.  `red` is LDS scratch of kThreads/64 + 1 words.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t* total) {
+// returns the total.  Calls alternate between the two halves of `red`
+// (2 x kThreads/64 words of LDS), so the one barrier of a call also
+// orders the previous call's reads before the next call's writes.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, int& parity, uint32_t* total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(inc, d);
-        if (lane >= d) inc += o;
-    }
-    if (lane == 63) red[wave] = inc;
+    uint32_t* r = red + parity * (kThreads / 64);
+    parity ^= 1;
+    const uint32_t inc = wave_scan(v);
+    if (lane == 63) r[wave] = inc;
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) {
-        const uint32_t s = red[w];
+        const uint32_t s = r[w];
         before += w < wave ? s : 0u;
         all += s;
     }
-    __syncthreads();  // red may be reused by the next call
     *total = all;
     return before + inc - v;
 }
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
     __shared__ uint32_t lh[kBins];
-    __shared__ uint32_t red[kThreads / 64 + 1];
+    __shared__ uint32_t red[2 * (kThreads / 64)];
+    int parity = 0;  // which half of red the next block_scan uses
     __shared__ uint32_t pick[3];
     __shared__ uint32_t offs[2];
     __shared__ uint32_t cpre[kMaxWgPerRow];
@@ -229,26 +246,29 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
     };
 
     // Finds the digit whose bin holds the k_rem-th largest key, scanning
-    // bins from the largest digit down; hist is the row's histogram in the
-    // workspace (global) or this workgroup's in LDS.  Every thread gets the
-    // digit, the count of keys in larger bins and the bin's own count.
-    auto find_bin = [&](const uint32_t* hist, bool global, int nb, int k_need, uint32_t* n_above,
-                        uint32_t* n_bin) -> uint32_t {
+    // bins from the largest digit down; gh is the row's histogram in the
+    // workspace (device-coherent buffer loads, all issued before the first
+    // is used), or null for this workgroup's histogram in LDS.  Every thread
+    // gets the digit, the count of keys in larger bins and the bin's own count.
+    auto find_bin = [&](const uint32_t* gh, int nb, int k_need, uint32_t* n_above, uint32_t* n_bin) -> uint32_t {
         const int bpt = nb / kThreads;  // thread t owns bins nb-1-(t*bpt+j)
         uint32_t cnt[kBins / kThreads];
+        if (gh) {
+            const __amdgpu_buffer_rsrc_t rh = make_rsrc(gh, (uint32_t)nb * 4u);
+#pragma unroll
+            for (int j = 0; j < kBins / kThreads; ++j) {
+                const uint32_t off = j < bpt ? (uint32_t)(nb - 1 - (tid * bpt + j)) * 4u : 0x80000000u;
+                cnt[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rh, off, 0, kAuxDevice);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kBins / kThreads; ++j) cnt[j] = j < bpt ? lh[nb - 1 - (tid * bpt + j)] : 0u;
+        }
         uint32_t tsum = 0;
 #pragma unroll
-        for (int j = 0; j < kBins / kThreads; ++j) {
-            uint32_t c = 0;
-            if (j < bpt) {
-                const int d = nb - 1 - (tid * bpt + j);
-                c = global ? (uint32_t)ld_dev(hist + d) : hist[d];
-            }
-            cnt[j] = c;
-            tsum += c;
-        }
+        for (int j = 0; j < kBins / kThreads; ++j) tsum += cnt[j];
         uint32_t total;
-        const uint32_t before = block_scan(tsum, red, &total);
+        const uint32_t before = block_scan(tsum, red, parity, &total);
         if (before < (uint32_t)k_need && (uint32_t)k_need <= before + tsum) {
             uint32_t acc = before;
 #pragma unroll
@@ -294,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             row_barrier();
         }
         uint32_t n_above, n_bin;
-        const uint32_t digit = find_bin(shared_row ? gh : lh, shared_row, nb, k_rem, &n_above, &n_bin);
+        const uint32_t digit = find_bin(shared_row ? gh : nullptr, nb, k_rem, &n_above, &n_bin);
         prefix = (prefix << (lvl == 2 ? 10 : 11)) | digit;
         k_rem -= (int)n_above;
         return n_bin;
@@ -320,11 +340,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             c_t += key != 0u && (key >> 21) == d0 ? 1u : 0u;
         });
         uint32_t a_w, c_w;
-        block_scan(a_t, red, &a_w);
-        uint32_t slot = block_scan(c_t, red, &c_w);
+        block_scan(a_t, red, parity, &a_w);
+        uint32_t slot = block_scan(c_t, red, parity, &c_w);
         uint64_t* mine = reinterpret_cast<uint64_t*>(ws + p.cand_off) + (size_t)w * p.cand_per_wg;
         for_keys([&](uint32_t key, int pos) {
-            if (key != 0u && (key >> 21) == d0) st_dev64(mine + slot++, ((uint64_t)(uint32_t)pos << 32) | key);
+            if (key != 0u && (key >> 21) == d0) {
+                // (slot < cand_per_wg always holds when the scan is right)
+                if (slot < (uint32_t)p.cand_per_wg) st_dev64(mine + slot, ((uint64_t)(uint32_t)pos << 32) | key);
+                ++slot;
+            }
         });
         if (tid == 0) {
             st_dev(counts + 2 * w, a_w);
@@ -334,8 +358,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
         const uint32_t a = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
         const uint32_t c = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid + 1) : 0u;
         uint32_t a_tot, c_tot;
-        const uint32_t A = block_scan(a, red, &a_tot);
-        const uint32_t Cp = block_scan(c, red, &c_tot);
+        const uint32_t A = block_scan(a, red, parity, &a_tot);
+        const uint32_t Cp = block_scan(c, red, parity, &c_tot);
         if (tid < p.P) cpre[tid] = Cp;
         if (tid == w) offs[0] = A;
         __syncthreads();
@@ -383,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             }
             __syncthreads();
             uint32_t n_above, n_bin;
-            const uint32_t digit = find_bin(lh, false, nb, k_rem, &n_above, &n_bin);
+            const uint32_t digit = find_bin(nullptr, nb, k_rem, &n_above, &n_bin);
             prefix = (prefix << (lvl == 2 ? 10 : 11)) | digit;
             k_rem -= (int)n_above;
         }
@@ -397,8 +421,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             eb_t += ck_key[e] == T && ck_pos[e] < start ? 1u : 0u;
         }
         uint32_t gb, eb;
-        block_scan(gb_t, red, &gb);
-        block_scan(eb_t, red, &eb);
+        block_scan(gb_t, red, parity, &gb);
+        block_scan(eb_t, red, parity, &eb);
         out_base = offs[0] + gb + min(eb, (uint32_t)n_eq_take);
         eq_base = eb;
     } else {
@@ -413,8 +437,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             e_t += key == T ? 1u : 0u;
         });
         uint32_t g_w, e_w;
-        block_scan(g_t, red, &g_w);
-        block_scan(e_t, red, &e_w);
+        block_scan(g_t, red, parity, &g_w);
+        block_scan(e_t, red, parity, &e_w);
         if (shared_row) {
             if (tid == 0) {
                 st_dev(counts + 2 * w, g_w);
@@ -426,10 +450,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             const uint32_t g = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
             const uint32_t e = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid + 1) : 0u;
             uint32_t dummy;
-            const uint32_t E = block_scan(e, red, &dummy);
+            const uint32_t E = block_scan(e, red, parity, &dummy);
             const int left = n_eq_take - (int)E;
             const uint32_t take = g + (uint32_t)(left <= 0 ? 0 : (left < (int)e ? left : (int)e));
-            const uint32_t S = block_scan(take, red, &dummy);
+            const uint32_t S = block_scan(take, red, parity, &dummy);
             if (tid == w) {
                 offs[0] = S;
                 offs[1] = E;
@@ -447,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) ne += kk[j] == T ? 1u : 0u;
         uint32_t eq_tot;
-        uint32_t eq_rank = run_eq + block_scan(ne, red, &eq_tot);
+        uint32_t eq_rank = run_eq + block_scan(ne, red, parity, &eq_tot);
         uint32_t sel = 0, ns = 0;
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
@@ -458,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             ns += take ? 1u : 0u;
         }
         uint32_t sel_tot;
-        uint32_t slot = run_sel + block_scan(ns, red, &sel_tot);
+        uint32_t slot = run_sel + block_scan(ns, red, parity, &sel_tot);
         // (slot < n_take always holds when the counts agree; the bound keeps
         // every store inside the row whatever they read)
 #pragma unroll
