@@ -133,3 +133,25 @@ def test_lists_feed_the_gather():
     assert np.array_equal(lists, ref_lists)
     gpu = gather_gpu(q, k, v, [L], lists, causal=True)
     assert_close(gpu, oracle_ref(q, k, v, [L], causal=True, idx=ref_lists), what="topk -> gather")
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling", "flat", "two_values"])
+def test_concentrated_and_tied_rows_full_size(kind):
+    """Full-size rows (131072 cells, 32 workgroups) where the threshold bin
+    sits in one workgroup's range (rising / falling scores), where every
+    score ties (flat: the digit-by-digit path with tie ranks spanning all
+    workgroups), and two values (a bin too large to gather)."""
+    note(f"topk full-size {kind}")
+    n_kv = 131072
+    cells = torch.arange(n_kv, dtype=torch.float32)
+    if kind == "rising":
+        row = cells / n_kv
+    elif kind == "falling":
+        row = -cells / n_kv
+    elif kind == "flat":
+        row = torch.full((n_kv,), 0.25)
+    else:
+        row = (torch.arange(n_kv) % 3 == 0).to(torch.float32)
+    sc = torch.stack([row, row.flip(0)]).view(1, 1, 2, n_kv).contiguous()
+    check(sc, [n_kv], 2048, 64, what=kind)
+    check(sc, [n_kv - 12345], 2048, 64, causal=False, what=f"{kind} shorter")
