@@ -5,8 +5,6 @@ workgroups per row meeting at barriers), rows full of ties and special
 values, causal windows, one workgroup per row (a large batch), unaligned
 score rows, workspace reuse across calls and graph replays, and the lists
 feeding the gather."""
-import math
-
 import numpy as np
 import pytest
 import torch
