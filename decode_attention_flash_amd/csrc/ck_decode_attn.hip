@@ -52,7 +52,11 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // Completion counters of one unit live in their own 1 KiB block: the started,
 // arrived and finished counters on separate cache lines, then one claim flag
 // per merge slice.
-constexpr int kCntStride = 256, kStarted = 0, kArrived = 32, kFinished = 64, kSliceFlag = 96;
+// Per unit, kCntStride ints of the workspace: a parity word naming the
+// counter set the next launch uses, then two counter sets (splits started,
+// splits arrived, slice claim flags), each field on its own 128-byte line.
+constexpr int kCntStride = 512, kParity = 0, kSet0 = 128, kSetStride = 128;
+constexpr int kStarted = 0, kArrived = 32, kSliceFlag = 64;
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
@@ -410,6 +414,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     // The query rows are the B operand of every QK^T MFMA.  They are the same
     // for the four waves, so the workgroup loads them once, cooperatively, into
     // LDS in operand order ([row tile][k-step][lane], 16 bytes each).
+    // The unit's counter parity goes out with the length (it is needed as
+    // soon as the split knows it is active); a plan with one split has no
+    // workspace and no counters.
+    int32_t* const ucnt = p.ws_cnt + kCntStride * unit;
+    const int par_word = p.splits > 1 ? atomic_ld(ucnt + kParity) : 0;
     const int L_raw = p.kv_lens[b];
     constexpr int QF = RT * KS * 64 / kThreads;  // fragments per thread
     bf16x8 qfrag[QF];
@@ -440,7 +449,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     const int C = chunk_len(span, p);
     const int n_active = span > 0 ? (span + C - 1) / C : 1;
     if (s >= n_active) return;
-    int32_t* cnt = p.ws_cnt + kCntStride * unit;
+    // The unit's counter set for this launch.  Every active split has read
+    // the parity before it arrives, and only the last arrival changes it.
+    const int par = __builtin_amdgcn_readfirstlane(par_word) & 1;  // uniform: the counters stay scalar
+    int32_t* const cnt = ucnt + kSet0 + par * kSetStride;
     if (n_active > 1 && tid == 0) atomicAdd(cnt + kStarted, 1);  // this split has started
     const int pos_begin = s * C;
     const int pos_end = min(pos_begin + C, span);
@@ -945,6 +957,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
     if (tid == 0) ms.flag = atomicAdd(cnt + kArrived, 1);  // arrival rank
     __syncthreads();
     const int rank = ms.flag;
+    if (rank == n_active - 1 && wave == 0) {
+        // Last arrival: every active split has read the parity, so the other
+        // counter set (this unit's previous launch used it) is cleared for
+        // the next launch and the parity points at it.  Nothing waits on
+        // these stores; the launch boundary orders them before the next use.
+        int32_t* const other = ucnt + kSet0 + (par ^ 1) * kSetStride;
+        atomic_st(other + kSliceFlag + lane, 0);
+        if (lane == 0) {
+            atomic_st(other + kStarted, 0);
+            atomic_st(other + kArrived, 0);
+            atomic_st(ucnt + kParity, par ^ 1);
+        }
+    }
 
     // ---- merge: the unit's last split and the ns-1 splits that arrived just
     // before it share the ns column slices.  The last split always takes slice
@@ -988,16 +1013,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
         }
         __syncthreads();
         if (ms.flag) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
-    }
-    if (tid == 0) {
-        // The ns participants each report once; the final report returns the
-        // unit's counters and claim flags to zero for the next launch.
-        if (atomicAdd(cnt + kFinished, 1) == ns - 1) {
-            atomic_st(cnt + kStarted, 0);
-            atomic_st(cnt + kArrived, 0);
-            atomic_st(cnt + kFinished, 0);
-            for (int c = 1; c < ns; ++c) atomic_st(cnt + kSliceFlag + c, 0);
-        }
     }
 }
 
@@ -1144,7 +1159,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
         pl->workspace_bytes = 0;
     } else {
         const size_t parts = (size_t)units * (size_t)splits * (size_t)rows_per_group;
-        pl->workspace_bytes = align256((size_t)units * 256 * sizeof(int32_t)) +
+        pl->workspace_bytes = align256((size_t)units * kCntStride * sizeof(int32_t)) +
                               align256(parts * s->D * sizeof(float)) + align256(parts * 2 * sizeof(float));
     }
     return CK_OK;
@@ -1255,7 +1270,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
         const size_t parts = (size_t)pl.units * pl.splits * pl.rows_per_group;
         char* w = static_cast<char*>(workspace);
         kp.ws_cnt = reinterpret_cast<int32_t*>(w);
-        w += align256((size_t)pl.units * 256 * sizeof(int32_t));
+        w += align256((size_t)pl.units * kCntStride * sizeof(int32_t));
         kp.ws_o = reinterpret_cast<float*>(w);
         w += align256(parts * s->D * sizeof(float));
         kp.ws_ml = reinterpret_cast<float*>(w);

@@ -42,11 +42,11 @@
  *
  * Workspace: when the plan splits the KV range (see
  * ck_decode_attn_workspace_size) the caller passes a device buffer of at
- * least that many bytes, 256-byte aligned.  It starts with a 1 KiB block of
- * int32 completion counters per unit, which must be zero when a launch
- * starts;
- * every launch leaves its counters at zero again (the partial results after
- * them are scratch).  So a buffer ZEROED ONCE serves any number of launches
+ * least that many bytes, 256-byte aligned.  It starts with a 2 KiB block of
+ * int32 counters per unit: a parity word and two counter sets.  A launch uses
+ * the set the parity names, which is zero when it starts, clears the other
+ * set and flips the parity for the next launch (the partial results after the
+ * counters are scratch).  So a buffer ZEROED ONCE serves any number of launches
  * of the same plan (same shape, W, num_splits and device), eager or replayed
  * from a captured HIP graph without a memset node.  A buffer used for one
  * plan must be zeroed again before it serves a different plan, and launches

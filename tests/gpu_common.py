@@ -130,3 +130,15 @@ def check_counts(out, visible_sets, G, nbits=17):
                 got = n * o[:nbits]
                 assert np.max(np.abs(got - counts)) < 0.01, (b, i, h)
                 assert np.array_equal(np.rint(got).astype(np.int64), counts), (b, i, h)
+
+
+def counters_ready(ws: torch.Tensor, units: int) -> bool:
+    """The workspace's counter blocks are ready for another launch: for each
+    unit (2 KiB: a parity word, then two sets of 128 ints), the set the
+    parity names is all zero."""
+    blk = ws[:units * 2048].view(torch.int32).view(units, 512).cpu().numpy()
+    for u in range(units):
+        par = int(blk[u, 0]) & 1
+        if np.any(blk[u, 128 + 128 * par:256 + 128 * par] != 0):
+            return False
+    return True
