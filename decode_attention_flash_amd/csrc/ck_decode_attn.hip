@@ -49,12 +49,10 @@ constexpr int kMaxQueries = CK_MAX_NQ;         // query rows per sequence (n_q)
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994530942f;
-// Completion counters of one unit live in their own 1 KiB block: the started,
-// arrived and finished counters on separate cache lines, then one claim flag
-// per merge slice.
 // Per unit, kCntStride ints of the workspace: a parity word naming the
 // counter set the next launch uses, then two counter sets (splits started,
-// splits arrived, slice claim flags), each field on its own 128-byte line.
+// splits arrived, one claim flag per merge slice), each field on its own
+// 128-byte line.
 constexpr int kCntStride = 512, kParity = 0, kSet0 = 128, kSetStride = 128;
 constexpr int kStarted = 0, kArrived = 32, kSliceFlag = 64;
 constexpr int kSpinLimit = 1 << 22;
