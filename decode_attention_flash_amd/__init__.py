@@ -134,8 +134,9 @@ def workspace_size(shape: Shape, W: int = 0, num_splits: int = 0) -> int:
 
 def new_workspace(shape: Shape, W: int = 0, num_splits: int = 0, device=None) -> torch.Tensor | None:
     """A zeroed workspace for this plan (None when none is needed).  Keep one
-    per stream and plan: launches leave its counters zeroed, so it can be
-    reused and captured, but another plan needs its own (or a re-zeroed) one."""
+    per stream and plan: every launch leaves it ready for the next launch of
+    the same plan, so it can be reused and captured without a memset, but
+    another plan needs its own (or a re-zeroed) one."""
     n = workspace_size(shape, W, num_splits)
     if n == 0:
         return None
@@ -145,12 +146,17 @@ def new_workspace(shape: Shape, W: int = 0, num_splits: int = 0, device=None) ->
 _ws_cache: dict = {}
 
 
-def _cached_workspace(shape: Shape, W: int, num_splits: int, device) -> torch.Tensor | None:
+def _stream_handle(stream, device) -> int:
+    return stream if stream is not None else torch.cuda.current_stream(device).cuda_stream
+
+
+def _cached_workspace(shape: Shape, W: int, num_splits: int, device, stream_handle) -> torch.Tensor | None:
     n = workspace_size(shape, W, num_splits)
     if n == 0:
         return None
-    # a workspace belongs to one plan: its counters are laid out for it
-    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream,
+    # A workspace belongs to one plan (its counters are laid out for it) and
+    # to one stream (launches that may overlap need different workspaces).
+    key = (torch.device(device).index, int(stream_handle or 0),
            tuple(getattr(shape, f) for f, _ in Shape._fields_), W, num_splits)
     ws = _ws_cache.get(key)
     if ws is None:
@@ -208,10 +214,10 @@ def decode_attn(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, cau
         _check(keep_mask, "keep_mask", torch.uint8)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
+    st_handle = _stream_handle(stream, q.device)
     if workspace is None:
-        workspace = _cached_workspace(shape, 0, num_splits, q.device)
+        workspace = _cached_workspace(shape, 0, num_splits, q.device, st_handle)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().ck_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(kv_lens), ctypes.c_float(scale), 1 if causal else 0,
                               _ptr(keep_mask), _ptr(out), odt, _ptr(lse), _ptr(workspace),
@@ -243,10 +249,10 @@ def decode_attn_gather(q, k_cache, v_cache, kv_lens, idx, *, scale: float | None
         raise ValueError("idx must be 3-D or 4-D")
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
+    st_handle = _stream_handle(stream, q.device)
     if workspace is None:
-        workspace = _cached_workspace(shape, W, num_splits, q.device)
+        workspace = _cached_workspace(shape, W, num_splits, q.device, st_handle)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().ck_decode_attn_gather(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(kv_lens), _ptr(idx), W, head_stride,
                                      ctypes.c_float(scale), 1 if causal else 0, _ptr(out), odt,
@@ -329,18 +335,21 @@ def decode_topk(scores, kv_lens, k: int, *, tail: int = 0, causal: bool = False,
     _check(out, "out", torch.int32)
     if tuple(out.shape) != (shape.B, shape.n_q, Hs, W):
         raise ValueError("out must be [B, n_q, Hs, k + tail]")
+    st_handle = _stream_handle(stream, scores.device)
     if workspace is None:
         n = ctypes.c_size_t(0)
         st = lib().ck_decode_topk_workspace_size(ctypes.byref(shape), Hs, int(k), int(tail), ctypes.byref(n))
         if st != 0:
             raise CkError(st, "ck_decode_topk_workspace_size")
         if n.value:
-            key = (n.value, scores.device)
+            # Every launch leaves the workspace zeroed, so any plan may reuse
+            # it afterwards; launches on different streams may overlap and
+            # get their own.
+            key = (n.value, scores.device, int(st_handle or 0))
             if key not in _topk_ws:
                 _topk_ws[key] = torch.zeros(n.value, dtype=torch.uint8, device=scores.device)
             workspace = _topk_ws[key]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st_handle = stream if stream is not None else torch.cuda.current_stream(scores.device).cuda_stream
     st = lib().ck_decode_topk(ctypes.byref(shape), _ptr(scores), Hs, _ptr(kv_lens), int(k), int(tail),
                               1 if causal else 0, _ptr(out), _ptr(workspace), ws_bytes, ctypes.c_void_p(st_handle))
     if st != 0:
@@ -364,10 +373,10 @@ def decode_attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, *, scale: fl
         raise ValueError(f"k_step and v_step must be [B, n_q, Hkv, D] = {want}")
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
+    st_handle = _stream_handle(stream, q.device)
     if workspace is None:
-        workspace = _cached_workspace(shape, 0, num_splits, q.device)
+        workspace = _cached_workspace(shape, 0, num_splits, q.device, st_handle)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().ck_decode_attn_steps(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(kv_lens), _ptr(k_step), _ptr(v_step), ctypes.c_float(scale),
                                     _ptr(out), odt, _ptr(lse), _ptr(workspace), ws_bytes, num_splits,
@@ -427,7 +436,7 @@ def kv_append_q8(cache: PagedQ8Cache, k_new, v_new, start, stream=None):
         raise ValueError("k_new / v_new must be [B, n_new, Hkv, D] matching the cache")
     shape = Shape(B, n_new, Hkv, Hkv, D, cache.capacity)
     cs = cache.c_struct()
-    st_handle = stream if stream is not None else torch.cuda.current_stream(k_new.device).cuda_stream
+    st_handle = _stream_handle(stream, k_new.device)
     st = lib().ck_kv_append_q8(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(start), ctypes.byref(cs),
                                ctypes.c_void_p(st_handle))
     if st != 0:
@@ -457,11 +466,11 @@ def decode_attn_q8(q, cache: PagedQ8Cache, kv_lens, *, scale: float | None = Non
     odt = CK_DT_BF16 if out_dtype == torch.bfloat16 else CK_DT_F32
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    st_handle = _stream_handle(stream, q.device)
     if workspace is None:
-        workspace = _cached_workspace(shape, 0, num_splits, q.device)
+        workspace = _cached_workspace(shape, 0, num_splits, q.device, st_handle)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     cs = cache.c_struct()
-    st_handle = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().ck_decode_attn_q8(ctypes.byref(shape), _ptr(q), ctypes.byref(cs), _ptr(kv_lens),
                                  ctypes.c_float(scale), 1 if causal else 0, _ptr(out), odt, _ptr(lse),
                                  _ptr(workspace), ws_bytes, num_splits, ctypes.c_void_p(st_handle))
