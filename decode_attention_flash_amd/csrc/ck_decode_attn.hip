@@ -220,17 +220,38 @@ __device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float
     w2 = fast_exp2(m2 - mu);
 }
 
+// Byte K of w, sign-extended, as a float: one SDWA conversion that selects
+// and sign-extends the byte itself (left to itself the compiler first shifts
+// bytes 1 and 3 down with a separate instruction).
+template <int K>
+__device__ __forceinline__ float sbyte_f32(uint32_t w) {
+    float r;
+    if constexpr (K == 0)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (K == 1)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (K == 2)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+
 // 16 int8 codes to 16 bf16 values (exact: |code| <= 128 needs 8 significant
-// bits), as two 16-byte halves.
+// bits), as two 16-byte halves: per code one conversion to fp32, per pair
+// one packing conversion to bf16.
 __device__ __forceinline__ void i8x16_to_bf16(u32x4 w, u32x4& lo, u32x4& hi) {
-    bf16x8 a, c;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t d[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = (__bf16)(float)(int8_t)(w[e >> 2] >> (8 * (e & 3)));
-        c[e] = (__bf16)(float)(int8_t)(w[2 + (e >> 2)] >> (8 * (e & 3)));
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 a = {(__bf16)sbyte_f32<0>(w[i]), (__bf16)sbyte_f32<1>(w[i])};
+        const bf16x2 c = {(__bf16)sbyte_f32<2>(w[i]), (__bf16)sbyte_f32<3>(w[i])};
+        d[2 * i] = __builtin_bit_cast(uint32_t, a);
+        d[2 * i + 1] = __builtin_bit_cast(uint32_t, c);
     }
-    lo = __builtin_bit_cast(u32x4, a);
-    hi = __builtin_bit_cast(u32x4, c);
+    lo = u32x4{d[0], d[1], d[2], d[3]};
+    hi = u32x4{d[4], d[5], d[6], d[7]};
 }
 
 // Bit e set where byte e of w is nonzero (4 keep_mask cells).
