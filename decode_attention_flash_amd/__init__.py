@@ -165,6 +165,16 @@ def _cached_workspace(shape: Shape, W: int, num_splits: int, device, stream_hand
     return ws
 
 
+def release_workspaces() -> None:
+    """Drop the workspaces the entry points allocated for themselves (one
+    per device, stream and plan when no ``workspace`` is passed), e.g. after
+    the batch shapes in use have changed.  The next call allocates a fresh
+    zeroed one.  Graphs captured with a dropped workspace still point at its
+    memory: release them first."""
+    _ws_cache.clear()
+    _topk_ws.clear()
+
+
 def _check(t: torch.Tensor, name: str, dtype) -> None:
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")

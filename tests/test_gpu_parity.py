@@ -429,3 +429,23 @@ def test_workspace_errors_on_device():
     out = ck.decode_attn(q, k, k, lens, workspace=ws[256:])
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_released_workspaces_are_rebuilt():
+    """Calls after release_workspaces get fresh zeroed workspaces and the
+    same results as before (the counters of the old ones are not reused)."""
+    note("release workspaces")
+    q = synth.queries(1, 1, 16, 256, 1002)
+    k, v = synth.kv_cache(1, 3000, 4, 256, [2500], 1002)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lens = torch.tensor([2500], dtype=torch.int32, device=DEV)
+    sc = synth.index_scores(1, 1, 4, 3000, 1002).to(DEV)
+    a = ck.decode_attn(qd, kd, vd, lens, return_lse=True)
+    la = ck.decode_topk(sc, lens, 256, tail=8)
+    torch.cuda.synchronize()
+    ck.release_workspaces()
+    b = ck.decode_attn(qd, kd, vd, lens, return_lse=True)
+    lb = ck.decode_topk(sc, lens, 256, tail=8)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(la, lb)
+    assert_close((b[0].cpu().numpy(), b[1].cpu().numpy()), oracle_ref(q, k, v, [2500]), what="after release")
