@@ -553,6 +553,8 @@ static int plan(const ck_decode_shape* s, int32_t Hs, int32_t k, int32_t tail, i
     if (wg < 1) wg = 1;
     if (rows * wg >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     const int64_t per_max = (blocks + wg - 1) / wg;
+    // a row's (key, position) slots are read through one 32-bit buffer range
+    if (wg > 1 && wg * per_max * kSuper * 8 >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     pl->P = (int32_t)wg;
     pl->cand_per_wg = (int32_t)(per_max * kSuper);
     pl->row_words = (uint64_t)kWsCand + (uint64_t)wg * (uint64_t)pl->cand_per_wg * 2u;

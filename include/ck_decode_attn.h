@@ -218,7 +218,10 @@ int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv,
  *   workspace : as for the attention entries: ck_decode_topk_workspace_size
  *               bytes (0 when one workgroup serves a row), 256-byte aligned,
  *               zeroed once; every launch leaves it zeroed.
- * Errors as for the attention entries; nothing is launched on error. */
+ * Errors as for the attention entries; nothing is launched on error.
+ * CK_ERR_UNSUPPORTED also when cap * 4 bytes reaches 2 GiB, or when the
+ * rows' workgroups would need 2 GiB of (key, position) slots for one row
+ * (about 2^28 positions). */
 int ck_decode_topk(const ck_decode_shape* shape, const float* scores, int32_t Hs, const int32_t* kv_lens,
                    int32_t k, int32_t tail, int causal, int32_t* idx, void* workspace, size_t workspace_bytes,
                    void* stream);

@@ -265,11 +265,18 @@ def test_topk_plan_keeps_row_workgroups_resident(B, n_q, Hs, cap, cus):
     ((1, 1, 2, 1000), dict(k=10, tail=-1), -1),
     ((1, 7, 2, 1000), dict(k=10), -2),
     ((0, 1, 2, 1000), dict(k=10), -1),
+    ((1, 1, 1, 1 << 28), dict(k=10), -2),  # one row's pair slots would pass 2 GiB (32-bit offsets)
 ])
 def test_topk_plan_rejects(scores_shape, kw, status):
     with pytest.raises(ck.CkError) as e:
         ck.topk_plan(scores_shape, num_cus=256, **kw)
     assert e.value.status == status
+
+
+def test_topk_plan_largest_rows():
+    # 2^27 positions in one row: 256 workgroups, 1 GiB of pair slots
+    p = ck.topk_plan((1, 1, 1, 1 << 27), k=2048, tail=64, num_cus=256)
+    assert p["wgs_per_row"] == 256 and p["workspace_bytes"] > (1 << 30)
 
 
 def test_topk_entry_rejects_before_launch():
