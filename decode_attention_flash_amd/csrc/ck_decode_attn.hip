@@ -211,15 +211,6 @@ struct Acc {
     float m[RT], l[RT];
 };
 
-// Weights that merge two softmax states (log2 domain) into one with max m.
-// Fully masked states have m = -inf and get weight 0.
-__device__ __forceinline__ void merge_scale(float m1, float m2, float& w1, float& w2, float& m) {
-    m = fmaxf(m1, m2);
-    float mu = (m == -INFINITY) ? 0.f : m;
-    w1 = fast_exp2(m1 - mu);
-    w2 = fast_exp2(m2 - mu);
-}
-
 // Byte K of w, sign-extended, as a float: one SDWA conversion that selects
 // and sign-extends the byte itself (left to itself the compiler first shifts
 // bytes 1 and 3 down with a separate instruction).

@@ -1,7 +1,6 @@
 """GPU parity: the HIP library against the fp64 oracle on the same seeded
 inputs, for every decode workload shape, plus the exactness properties
 (garbage and capacity invariance, bit-exact index and mask handling)."""
-import math
 
 import numpy as np
 import pytest

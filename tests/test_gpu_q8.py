@@ -11,7 +11,7 @@ import torch
 import decode_attention_flash_amd as ck
 import oracle
 from decode_attention_flash_amd import synth
-from gpu_common import DEV, TOL_BF16, TOL_F32, assert_close, counters_ready, note
+from gpu_common import DEV, assert_close, counters_ready, note
 
 pytestmark = pytest.mark.gpu
 

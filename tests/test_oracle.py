@@ -6,7 +6,6 @@ tests/oracle_pins.py.  The mutation test at the end plants plausible
 mistakes in copies of the oracle source and checks that these pins catch
 every one of them.
 """
-import math
 import os
 import subprocess
 import sys
