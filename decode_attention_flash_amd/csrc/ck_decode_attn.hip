@@ -13,7 +13,8 @@
 // finishes a unit's last split merges the splits in the same launch (same
 // comfy-kitchen PR, GQA decode), so the launch has a fixed shape.
 //
-// Per wave and tile (TT tokens, TT*D*2 = 16 KiB of K and as much of V):
+// Per wave and tile (TT tokens, TT*D*2 = 16 KiB of K and as much of V; 8 KiB
+// at D = 128 with one row tile, where two workgroups share a CU):
 //   K,V : row-major buffer loads (each instruction reads whole cache rows,
 //         which streams faster than the 16-row x 64-byte pattern of an MFMA
 //         operand), staged in LDS; rows past the split or the visible limit
@@ -59,9 +60,18 @@ constexpr int kSpinLimit = 1 << 22;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 
-template <int D>
+// Bytes of K per wave tile.  At D = 128 with one row tile the kernel needs
+// under 256 VGPRs, so with 8 KiB tiles (under 80 KiB of LDS) two workgroups
+// share a CU: two waves per SIMD, and one wave's conversions, softmax and
+// stores run while the other waits for its loads.  Elsewhere the registers
+// allow one wave per SIMD, which takes 16 KiB tiles.  (D = 256 cannot halve
+// its tile: 32 tokens are one k-block of PV.)
+constexpr int tile_bytes(int D, int RT) { return D == 128 && RT == 1 ? 8192 : 16384; }
+constexpr int waves_per_simd(int D, int RT) { return D == 128 && RT == 1 ? 2 : 1; }
+
+template <int D, int TB>
 struct Geo {
-    static constexpr int TT = 16384 / (2 * D);  // tokens per wave tile
+    static constexpr int TT = TB / (2 * D);  // tokens per wave tile
     static constexpr int MB = TT / 16;          // 16-token blocks per tile (QK M side)
     static constexpr int KS = D / 32;           // k-steps of the QK contraction
     static constexpr int KB = TT / 32;          // 32-token k-blocks of PV
@@ -379,8 +389,8 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
 // MODE 0: dense, 1: dense with keep_mask, 2: gather, 3: dense over the paged
 // INT8 cache.
 template <int D, int RT, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(const KParams p) {
-    using Gm = Geo<D>;
+__global__ __launch_bounds__(kThreads, waves_per_simd(D, RT)) void decode_kernel(const KParams p) {
+    using Gm = Geo<D, tile_bytes(D, RT)>;
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS, RSK = Gm::RSK;
     constexpr bool GATHER = (MODE == 2);
@@ -1091,6 +1101,9 @@ __global__ __launch_bounds__(kThreads) void q8_append_kernel(const AppendParams 
 
 constexpr int kWgPerCu = 1;
 
+// Split boundaries fall on multiples of this many tokens: the kernel's tile
+// at D = 256, and at D = 128 a multiple of both of its tiles (32 tokens with
+// one row tile, 64 with two).
 static int tile_tokens(int D) { return D == 256 ? 32 : 64; }
 // When the units alone fill the chip, a long sequence is still cut into
 // ranges of at most this many K+V bytes, so ragged batches balance over the
