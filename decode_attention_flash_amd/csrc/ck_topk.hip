@@ -44,6 +44,12 @@ constexpr int kWsCounts = kWsHist + 3 * kBins;
 constexpr int kMaxWgPerRow = 256;
 constexpr int kWsCand = kWsCounts + 2 * kMaxWgPerRow;  // then (key, position) pairs, per workgroup
 constexpr int kCand = 4096;                               // threshold-bin cells gathered in LDS
+// Super-blocks of a workgroup whose keys stay in registers: 1 when a
+// workgroup holds one (a row split over many workgroups), else 8.  Each
+// cached super-block unrolls every pass over the keys once more, and the
+// larger code costs a one-block workgroup several microseconds, so each case
+// gets its own kernel.
+constexpr int kCacheMany = 8;
 
 struct TParams {
     const float* scores;      // [B, n_q, Hs, cap]
@@ -125,6 +131,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, int& p
     return before + inc - v;
 }
 
+template <int CSB>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
     __shared__ uint32_t lh[kBins];
     __shared__ uint32_t red[2 * (kThreads / 64)];
@@ -167,12 +174,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
                 x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (pos + j) * 4u, 0, 0));
         }
     };
-    float xc[kPerThread];
-    if (sb0 < sb1) {
-        load_raw(sb0, xc);
-    } else {
+    // The first CSB super-blocks of the range are loaded at once (one
+    // round trip) and stay in registers as keys for every pass; any further
+    // ones are read again at each pass.
+    float xc[CSB][kPerThread];
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) xc[j] = 0.f;
+    for (int c = 0; c < CSB; ++c) {
+        if (sb0 + c < sb1) {
+            load_raw(sb0 + c, xc[c]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) xc[c][j] = 0.f;
+        }
     }
 
     const int L_raw = p.kv_lens[b];
@@ -204,16 +217,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
         for (int j = 0; j < kPerThread; ++j)
             kk[j] = sb * kSuper + kPerThread * tid + j < n_cand ? key_of(x[j]) : 0u;
     };
-    uint32_t kc[kPerThread];  // the first super-block stays in registers
-    to_keys(xc, sb0, kc);
-    // Calls f(key, position) for this thread's positions, super-block by
-    // super-block (later ones are read again at each pass).
-    auto for_keys = [&](auto&& f) {
-        if (sb0 < sb1) {
+    uint32_t kc[CSB][kPerThread];
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) f(kc[j], sb0 * kSuper + kPerThread * tid + j);
+    for (int c = 0; c < CSB; ++c) to_keys(xc[c], sb0 + c, kc[c]);
+    // Calls f(key, position) for this thread's positions, super-block by
+    // super-block (those past the register cache are read again).
+    auto for_keys = [&](auto&& f) {
+#pragma unroll
+        for (int c = 0; c < CSB; ++c) {
+            if (sb0 + c < sb1) {
+#pragma unroll
+                for (int j = 0; j < kPerThread; ++j) f(kc[c][j], (sb0 + c) * kSuper + kPerThread * tid + j);
+            }
         }
-        for (int sb = sb0 + 1; sb < sb1; ++sb) {
+        for (int sb = sb0 + CSB; sb < sb1; ++sb) {
             float x[kPerThread];
             uint32_t kk[kPerThread];
             load_raw(sb, x);
@@ -491,8 +508,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
         run_sel += sel_tot;
         run_eq += eq_tot;
     };
-    if (sb0 < sb1) emit(kc, sb0);
-    for (int sb = sb0 + 1; sb < sb1; ++sb) {
+#pragma unroll
+    for (int c = 0; c < CSB; ++c)
+        if (sb0 + c < sb1) emit(kc[c], sb0 + c);
+    for (int sb = sb0 + CSB; sb < sb1; ++sb) {
         float x[kPerThread];
         uint32_t kk[kPerThread];
         load_raw(sb, x);
@@ -625,8 +644,12 @@ int ck_decode_topk(const ck_decode_shape* shape, const float* scores, int32_t Hs
     p.cand_off = (uint32_t)cktk::kWsCand;
     p.ws_row_words = pl.row_words;
     const int rows = shape->B * shape->n_q * Hs;
-    hipLaunchKernelGGL(cktk::topk_kernel, dim3((unsigned)(rows * pl.P)), dim3(cktk::kThreads), 0,
-                       (hipStream_t)stream, p);
+    if (pl.cand_per_wg <= cktk::kSuper)  // one super-block per workgroup
+        hipLaunchKernelGGL(cktk::topk_kernel<1>, dim3((unsigned)(rows * pl.P)), dim3(cktk::kThreads), 0,
+                           (hipStream_t)stream, p);
+    else
+        hipLaunchKernelGGL(cktk::topk_kernel<cktk::kCacheMany>, dim3((unsigned)(rows * pl.P)),
+                           dim3(cktk::kThreads), 0, (hipStream_t)stream, p);
     return hipGetLastError() == hipSuccess ? CK_OK : CK_ERR_HIP;
 }
 

@@ -74,6 +74,22 @@ def test_one_workgroup_per_row():
     check(sc, lens, 2048, 64, what="batch")
 
 
+@pytest.mark.parametrize("B,Hs,cap", [(32, 8, 40000), (4, 8, 131072), (8, 8, 200000)])
+def test_cached_and_reread_super_blocks(B, Hs, cap):
+    """Workgroups holding several 4096-cell blocks: one per row with 10
+    blocks (8 kept in registers, 2 read again per pass), 8 per row with 4
+    blocks each, and 4 per row with 13 blocks each (the cache plus 5 read
+    again), on ragged lengths."""
+    plan = ck.topk_plan((B, 1, Hs, cap), 2048, 64)
+    blocks = -(-cap // 4096)
+    per = -(-blocks // plan["wgs_per_row"])
+    note(f"topk cached blocks B={B} Hs={Hs} cap={cap} P={plan['wgs_per_row']} blocks/wg={per}")
+    assert per > 1
+    lens = synth.ragged_lens(B, cap // 2, cap, 75)
+    sc = synth.index_scores(B, 1, Hs, cap, 76)
+    check(sc, lens, 2048, 64, what=f"cap={cap}")
+
+
 def test_unaligned_rows_and_shared_lists():
     """cap % 4 != 0 (scores read one at a time) and one score row per query
     shared by the KV heads (Hs = 1)."""
