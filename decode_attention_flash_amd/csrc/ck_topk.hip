@@ -12,7 +12,8 @@
 // 11, 11 and 10 bits.  Each level histograms the digit of the candidates
 // that share the digits fixed so far, and the bin holding the k-th largest
 // is kept.  P workgroups share a row: each holds a contiguous range of
-// positions (its scores stay in registers across the levels), adds its LDS
+// positions (the keys of up to 8 super-blocks of 4096 stay in registers
+// across the levels), adds its LDS
 // histogram into the row's histogram in the workspace, and meets the others
 // at a row barrier.  Every workgroup of a row is resident at once (the host
 // sizes the grid to the CU count), so the barriers never wait on a

@@ -64,7 +64,7 @@ def test_all_candidates_and_tiny_windows():
 
 def test_one_workgroup_per_row():
     """256 rows fill the chip: each row is one workgroup (no barriers), and
-    its scores no longer fit the register cache (re-read per pass)."""
+    its 8 super-blocks of keys all stay in registers across the passes."""
     note("topk one workgroup per row")
     B, Hs, cap = 32, 8, 32768
     plan = ck.topk_plan((B, 1, Hs, cap), 2048, 64)
