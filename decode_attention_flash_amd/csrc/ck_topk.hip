@@ -13,9 +13,8 @@
 // that share the digits fixed so far, and the bin holding the k-th largest
 // is kept.  P workgroups share a row: each holds a contiguous range of
 // positions (the keys of up to 8 super-blocks of 4096 stay in registers
-// across the levels), adds its LDS
-// histogram into the row's histogram in the workspace, and meets the others
-// at a row barrier.  Every workgroup of a row is resident at once (the host
+// across the levels), adds its LDS histogram into the row's histogram in
+// the workspace, and meets the others at a row barrier.  Every workgroup of a row is resident at once (the host
 // sizes the grid to the CU count), so the barriers never wait on a
 // workgroup that is not running.  A final pass writes the selected positions
 // in position order: each workgroup's output offset follows from the
