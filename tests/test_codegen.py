@@ -4,7 +4,10 @@ results cannot see:
   * a buffer descriptor the compiler cannot prove uniform makes it wrap every
     buffer load in a readfirstlane loop ("waterfall"), which once slowed the
     ragged batch by a fifth;
-  * register spills to scratch memory."""
+  * register spills to scratch memory;
+  * a D=128 kernel with one row tile that no longer fits twice on a CU (at
+    most 80 KiB of LDS and 256 VGPRs), which the INT8 batch and the masked
+    scan need for their speed."""
 import os
 import re
 import shutil
@@ -57,3 +60,28 @@ def test_no_scratch_spills(asm):
         n += 1
         assert "scratch_store" not in body and "scratch_load" not in body, f"{name}: spills to scratch"
     assert n >= 19
+
+
+def kernel_resources(text):
+    """(LDS bytes, VGPRs incl. AGPRs) per kernel, from the code object metadata."""
+    meta = text[text.index("amdhsa.kernels:"):]
+    res = {}
+    for block in meta.split("\n  - ")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        lds = re.search(r"\.group_segment_fixed_size:\s+(\d+)", block)
+        vgpr = re.search(r"\.vgpr_count:\s+(\d+)", block)
+        if name and lds and vgpr:
+            res[name.group(1)] = (int(lds.group(1)), int(vgpr.group(1)))
+    return res
+
+
+def test_d128_one_row_tile_kernels_fit_twice_per_cu(asm):
+    res = kernel_resources(asm)
+    found = 0
+    for name, (lds, vgpr) in res.items():
+        if "decode_kernelILi128ELi1E" not in name:
+            continue
+        found += 1
+        assert lds <= 80 * 1024, f"{name}: {lds} bytes of LDS, two workgroups no longer fit on a CU"
+        assert vgpr <= 256, f"{name}: {vgpr} VGPRs, two waves no longer fit on a SIMD"
+    assert found == 4  # modes 0-3
