@@ -90,9 +90,11 @@ def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_l
     import torch
     import decode_attention_flash_amd as ck
     from decode_attention_flash_amd import synth
-    kv_bytes = int(sum(4 * Hkv * D * min(int(L), stack.k[0].shape[1]) for L in lens))
+    cap = stack.k[0].shape[1]
+    kv_bytes = int(sum(4 * Hkv * D * min(int(L), cap) for L in lens))
+    window_bytes = kv_bytes
     if masks is not None:
-        kv_bytes_mask = int(sum(n_q * Hkv * int(L) for L in lens))
+        kv_bytes_mask = int(sum(n_q * Hkv * min(int(L), cap) for L in lens))
     else:
         kv_bytes_mask = 0
     n = n_layers or layers_for(kv_bytes)
@@ -102,6 +104,10 @@ def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_l
     lens_d = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
     shape = ck.shape_of(qs[0], stack.k[0])
     ws = ck.new_workspace(shape)
+    if masks is not None and cap % 16 == 0 and all(m.data_ptr() % 16 == 0 for m in masks[:n]):
+        # The scan reads only the tiles that hold a kept cell of the unit's
+        # query rows (rows below the length), so count those, per layer.
+        kv_bytes = int(sum(masked_read_tokens(masks[l], lens, ck.plan(shape)["tile"]) for l in range(n)) * 4 * D / n)
 
     def launch(l):
         ck.decode_attn(qs[l], stack.k[l], stack.v[l], lens_d, causal=causal, out=outs[l],
@@ -109,9 +115,30 @@ def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_l
 
     ms, us = time_graph(launch, n, steps, warmup)
     algo = kv_bytes + kv_bytes_mask + 2 * B * n_q * Hq * D + 4 * B * n_q * Hq * D + 4 * B
-    return dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, algo_bytes=algo,
-                kv_gbs=kv_bytes / us / 1e3, algo_gbs=algo / us / 1e3,
-                frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
+    res = dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, algo_bytes=algo,
+               kv_gbs=kv_bytes / us / 1e3, algo_gbs=algo / us / 1e3,
+               frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
+    if masks is not None:
+        res["window_bytes"] = window_bytes
+    return res
+
+
+def masked_read_tokens(mask, lens, tile):
+    """Cache positions a tile-skipping scan reads, summed over (sequence, KV
+    head): those below the length in tiles where some query row keeps a
+    cell.  mask [B, n_q, Hkv, cap] on the device."""
+    import torch
+    total = 0
+    for b, L in enumerate(lens):
+        L = min(int(L), mask.shape[-1])
+        if L == 0:
+            continue
+        keep = (mask[b, :, :, :L] != 0).any(dim=0)  # [Hkv, L]
+        nt = -(-L // tile)
+        keep = torch.nn.functional.pad(keep, (0, nt * tile - L)).view(keep.shape[0], nt, tile).any(-1)
+        last = L - (nt - 1) * tile  # positions of the last tile below the length
+        total += int(keep[:, :-1].sum().item()) * tile + int(keep[:, -1].sum().item()) * last
+    return total
 
 
 def steps_case(stack, n_q, Hq, Hkv, D, L, steps, warmup, n_layers=None):

@@ -53,7 +53,7 @@ class Plan(ctypes.Structure):
                 ("chunk_max", ctypes.c_int32),
                 ("granule", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("row_groups", ctypes.c_int32), ("rows_per_group", ctypes.c_int32),
-                ("slices", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("slices", ctypes.c_int32), ("tile", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

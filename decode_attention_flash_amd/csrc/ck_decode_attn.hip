@@ -1178,6 +1178,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     int64_t slices = 1;
     while (slices * 32768 < merge_bytes && slices < s->D / 4 && slices < kMaxSlices) slices *= 2;
     pl->slices = (int32_t)slices;
+    pl->tile = tile_bytes(s->D, rows_per_group / 16) / (2 * s->D);
     if (splits == 1) {
         pl->workspace_bytes = 0;
     } else {

@@ -111,6 +111,9 @@ typedef struct ck_decode_plan {
     int32_t row_groups;      /* units per (sequence, query, KV head)         */
     int32_t rows_per_group;  /* rows handled by one workgroup (16 or 32)     */
     int32_t slices;          /* column slices the split merge is cut into    */
+    int32_t tile;            /* cache positions (or list entries) per wave
+                                tile: a masked scan reads whole tiles that
+                                hold a kept cell and skips the others        */
     size_t workspace_bytes;  /* 0 when no launch of this plan can split      */
 } ck_decode_plan;
 

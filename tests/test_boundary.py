@@ -56,6 +56,17 @@ def test_plan_keeps_workgroups_in_one_round(B, Hkv, n_q, W):
     assert p["units"] * p["splits"] <= 256
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,n_q,tile", [
+    (128, 8, 2, 1, 32),    # up to 16 packed rows: 8 KiB tiles, two workgroups per CU
+    (128, 16, 2, 3, 64),   # 24 rows, two row tiles: 16 KiB tiles
+    (256, 16, 4, 1, 32),
+    (256, 16, 4, 6, 32),   # D=256 keeps 32 tokens (one PV k-block)
+])
+def test_plan_reports_the_kernel_tile(D, Hq, Hkv, n_q, tile):
+    p = ck.plan(shape(n_q=n_q, Hq=Hq, Hkv=Hkv, D=D), num_cus=256)
+    assert p["tile"] == tile and p["granule"] % p["tile"] == 0
+
+
 def test_plan_single_sequence_has_no_chunk_limit():
     p = ck.plan(shape(), num_cus=256)
     assert p["chunk_max"] == 0
