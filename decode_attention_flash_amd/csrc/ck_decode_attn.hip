@@ -1142,7 +1142,9 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     if (num_splits == 0) {
         // As many splits as keep every unit's workgroups in one round (one
         // workgroup per CU): one more would leave a few workgroups for a
-        // second round and double the time.
+        // second round and double the time.  Where two workgroups fit on a
+        // CU (D = 128, one row tile) the target stays one per CU: twice the
+        // splits measured slower on long single sequences.
         target = (int64_t)num_cus * kWgPerCu / units;
         cmax = 2 * units >= num_cus ? chunk_max_tokens(s->D) : 0;
         cmin = (kTokensPerRow * rows_eff + TT - 1) / TT * TT;
