@@ -14,7 +14,7 @@
 // comfy-kitchen PR, GQA decode), so the launch has a fixed shape.
 //
 // Per wave and tile (TT tokens, TT*D*2 = 16 KiB of K and as much of V; 8 KiB
-// at D = 128 with one row tile, where two workgroups share a CU):
+// with one row tile, where two workgroups share a CU):
 //   K,V : row-major buffer loads (each instruction reads whole cache rows,
 //         which streams faster than the 16-row x 64-byte pattern of an MFMA
 //         operand), staged in LDS; rows past the split or the visible limit
@@ -60,14 +60,14 @@ constexpr int kSpinLimit = 1 << 22;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 
-// Bytes of K per wave tile.  At D = 128 with one row tile the kernel needs
-// under 256 VGPRs, so with 8 KiB tiles (under 80 KiB of LDS) two workgroups
-// share a CU: two waves per SIMD, and one wave's conversions, softmax and
-// stores run while the other waits for its loads.  Elsewhere the registers
-// allow one wave per SIMD, which takes 16 KiB tiles.  (D = 256 cannot halve
-// its tile: 32 tokens are one k-block of PV.)
-constexpr int tile_bytes(int D, int RT) { return D == 128 && RT == 1 ? 8192 : 16384; }
-constexpr int waves_per_simd(int D, int RT) { return D == 128 && RT == 1 ? 2 : 1; }
+// Bytes of K per wave tile.  With one row tile (up to 16 packed rows) the
+// kernel needs under 256 VGPRs, so with 8 KiB tiles (32 tokens at D = 128,
+// 16 at D = 256; under 80 KiB of LDS) two workgroups share a CU: two waves
+// per SIMD, and one wave's conversions, softmax and stores run while the
+// other waits for its loads.  Two row tiles need 350-510 VGPRs: one wave per
+// SIMD, which takes 16 KiB tiles.
+constexpr int tile_bytes(int RT) { return RT == 1 ? 8192 : 16384; }
+constexpr int waves_per_simd(int RT) { return RT == 1 ? 2 : 1; }
 
 template <int D, int TB>
 struct Geo {
@@ -176,9 +176,16 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// 16x16x16 bf16 MFMA (a 16-token k-block): lane l holds 4 k-values of row
+// (A) or column (B) l % 16, k-group l / 16.
+__device__ __forceinline__ f32x4 mfma_k16(lds_bf16x4 a, lds_bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                     0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposed LDS read (gfx950): within each 16-lane group, lane j receives
 // element j%4 of the 64-bit words read by lanes 4e+j/4, e = 0..3.
@@ -389,8 +396,8 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
 // MODE 0: dense, 1: dense with keep_mask, 2: gather, 3: dense over the paged
 // INT8 cache.
 template <int D, int RT, int MODE>
-__global__ __launch_bounds__(kThreads, waves_per_simd(D, RT)) void decode_kernel(const KParams p) {
-    using Gm = Geo<D, tile_bytes(D, RT)>;
+__global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(const KParams p) {
+    using Gm = Geo<D, tile_bytes(RT)>;
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS, RSK = Gm::RSK;
     constexpr bool GATHER = (MODE == 2);
@@ -799,7 +806,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(D, RT)) void decode_kernel
         if (tid == 0 && tile == first && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
 
         // -- online softmax (log2 domain) -----------------------------------
-        bf16x8 pb[RT][KB];
+        bf16x8 pb[RT][KB > 0 ? KB : 1];  // PV B operands of the 32-token k-blocks
+        lds_bf16x4 p16[RT];               // of a 16-token tile
         // Paged INT8 cache: the K scale multiplies the score of its token, the
         // V scale the probability that weights its codes.
         // Each probability is rounded to bf16 after the V scale is applied;
@@ -872,12 +880,26 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(D, RT)) void decode_kernel
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pb[rt][kb][e] = e < 4 ? ph[2 * kb][e] : ph[2 * kb + 1][e - 4];
+            if constexpr (TT == 16) p16[rt] = lds_bf16x4{ph[0][0], ph[0][1], ph[0][2], ph[0][3]};
         }
 
         // -- O^T += V^T P^T with V^T read transposed from LDS ---------------
         // Lane (group q4, k = l16) reads 4 head-dim values of token row
-        // 32kb + 4q4 + k/4 (and + 16 for the upper half of the k-slots).
+        // 32kb + 4q4 + k/4 (and + 16 for the upper half of the k-slots).  It
+        // receives head-dim column l16 of tokens 32kb + 4q4 .. +3 (+16).
         wave_lds_sync();
+        if constexpr (TT == 16) {
+            // A 16-token tile is one k-block of 16x16x16 MFMAs: the
+            // transposed read is the A operand and the lane's 4 probabilities
+            // (tokens 4q4 .. 4q4+3 of its row) the B operand, unpermuted.
+            const unsigned char* row_lo = vlds + (4 * q4 + (l16 >> 2)) * RS + (l16 & 3) * 8;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const lds_bf16x4 va = lds_read_tr(row_lo + 32 * n);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) st.o[rt][n] = mfma_k16(va, p16[rt], st.o[rt][n]);
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const unsigned char* row_lo = vlds + (32 * kb + 4 * q4 + (l16 >> 2)) * RS + (l16 & 3) * 8;
@@ -1101,9 +1123,9 @@ __global__ __launch_bounds__(kThreads) void q8_append_kernel(const AppendParams 
 
 constexpr int kWgPerCu = 1;
 
-// Split boundaries fall on multiples of this many tokens: the kernel's tile
-// at D = 256, and at D = 128 a multiple of both of its tiles (32 tokens with
-// one row tile, 64 with two).
+// Split boundaries fall on multiples of this many tokens, a multiple of the
+// kernel's tiles with one and with two row tiles (16 and 32 tokens at
+// D = 256, 32 and 64 at D = 128).
 static int tile_tokens(int D) { return D == 256 ? 32 : 64; }
 // When the units alone fill the chip, a long sequence is still cut into
 // ranges of at most this many K+V bytes, so ragged batches balance over the
@@ -1180,7 +1202,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     int64_t slices = 1;
     while (slices * 32768 < merge_bytes && slices < s->D / 4 && slices < kMaxSlices) slices *= 2;
     pl->slices = (int32_t)slices;
-    pl->tile = tile_bytes(s->D, rows_per_group / 16) / (2 * s->D);
+    pl->tile = tile_bytes(rows_per_group / 16) / (2 * s->D);
     if (splits == 1) {
         pl->workspace_bytes = 0;
     } else {

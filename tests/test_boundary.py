@@ -59,8 +59,8 @@ def test_plan_keeps_workgroups_in_one_round(B, Hkv, n_q, W):
 @pytest.mark.parametrize("D,Hq,Hkv,n_q,tile", [
     (128, 8, 2, 1, 32),    # up to 16 packed rows: 8 KiB tiles, two workgroups per CU
     (128, 16, 2, 3, 64),   # 24 rows, two row tiles: 16 KiB tiles
-    (256, 16, 4, 1, 32),
-    (256, 16, 4, 6, 32),   # D=256 keeps 32 tokens (one PV k-block)
+    (256, 16, 4, 1, 16),   # 8 KiB: 16 tokens, PV in 16-token k-blocks
+    (256, 16, 4, 6, 32),   # 24 rows: 16 KiB
 ])
 def test_plan_reports_the_kernel_tile(D, Hq, Hkv, n_q, tile):
     p = ck.plan(shape(n_q=n_q, Hq=Hq, Hkv=Hkv, D=D), num_cus=256)

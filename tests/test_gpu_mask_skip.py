@@ -97,9 +97,9 @@ def test_window_crossings_recover_exact_cell_sets(D, L, splits):
     the bitmap; three causal queries with their own masks; each output
     recovers exactly its visible cell set (counting construction)."""
     n_q, Hq, Hkv = 3, 8, 2
-    TT = 16384 // (2 * D)
     lens = [L, L // 3 + 11]
     cap = ((L + 40) // 16) * 16
+    TT = ck.plan(ck.Shape(len(lens), n_q, Hq, Hkv, D, cap))["tile"]  # the kernel's tile
     note(f"mask skip: window crossings D={D} L={L} splits={splits}")
     q, k, v = counting_case(n_q, Hq, Hkv, D, cap, lens, 13)
     mask = crossing_mask(len(lens), n_q, Hkv, cap, lens, 14 + D, TT)
@@ -149,7 +149,7 @@ def test_skipping_and_full_scan_agree(D):
     the same tiles in the same order: bit-identical.  With block selections
     the waves share the kept tiles differently: equal to rounding."""
     B, n_q, Hq, Hkv, cap = 1, 1, 16, 2, 24576
-    TT = 16384 // (2 * D)
+    TT = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, cap))["tile"]  # the kernel's tile
     L = 24000
     note(f"mask skip: aligned vs unaligned D={D}")
     k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1009)
