@@ -395,8 +395,9 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
 
 // MODE 0: dense, 1: dense with keep_mask, 2: gather, 3: dense over the paged
 // INT8 cache.
-template <int D, int RT, int MODE>
+template <int D, int RT, int MODE, bool CO>
 __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(const KParams p) {
+    static_assert(!CO || RT == 1, "row groups share tiles only with one row tile");
     using Gm = Geo<D, tile_bytes(RT)>;
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS, RSK = Gm::RSK;
@@ -420,8 +421,22 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // the 8 XCDs; rotating the unit by the split index moves consecutive
     // splits of one unit to different XCDs, so each XCD gets a fair share of
     // long and short sequences.
-    const int s = blockIdx.x / p.units;
-    const int unit = (blockIdx.x % p.units + s) % p.units;
+    // CO (several 16-row groups): the row groups of one (sequence, head,
+    // split) read the same tiles.  They take blocks 8 apart, so they run on
+    // the same XCD and the later reads of a tile hit its L2.  Blocks come in
+    // chunks of 8 x RG; the host pads the grid to whole chunks and the
+    // padding blocks leave here, before any barrier.
+    int s, unit;
+    if constexpr (CO) {
+        const int per = 8 * p.RG, within = blockIdx.x % per;
+        const int idx = blockIdx.x / per * 8 + within % 8, units_nr = p.units / p.RG;
+        if (idx >= units_nr * p.splits) return;
+        s = idx / units_nr;
+        unit = (idx % units_nr + s) % units_nr * p.RG + within / 8;
+    } else {
+        s = blockIdx.x / p.units;
+        unit = (blockIdx.x % p.units + s) % p.units;
+    }
     int t = unit;
     const int rg = t % p.RG;
     t /= p.RG;
@@ -598,12 +613,21 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ksc + prow, sbytes);
             const __amdgpu_buffer_rsrc_t rvs8 = make_rsrc(p.vsc + prow, sbytes);
             constexpr int CPR8 = Gm::CPR8, RPI8 = Gm::RPI8;
+            uint32_t o8[Gm::VI8];
 #pragma unroll
             for (int n = 0; n < Gm::VI8; ++n)
-                k8[n] = bload128<2>(rk8, (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u);
+                o8[n] = (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u;
+            if constexpr (CO) {  // the other row groups read these tiles again: keep them in L2
 #pragma unroll
-            for (int n = 0; n < Gm::VI8; ++n)
-                v8[n] = bload128<2>(rv8, (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u);
+                for (int n = 0; n < Gm::VI8; ++n) k8[n] = bload128<0>(rk8, o8[n]);
+#pragma unroll
+                for (int n = 0; n < Gm::VI8; ++n) v8[n] = bload128<0>(rv8, o8[n]);
+            } else {
+#pragma unroll
+                for (int n = 0; n < Gm::VI8; ++n) k8[n] = bload128<2>(rk8, o8[n]);
+#pragma unroll
+                for (int n = 0; n < Gm::VI8; ++n) v8[n] = bload128<2>(rv8, o8[n]);
+            }
             const uint32_t soff = (uint32_t)lane * 4u;
             ksv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, soff, 0, 0));
             vsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs8, soff, 0, 0));
@@ -649,10 +673,17 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
         const uint32_t coff = (uint32_t)(lane % CPR) * 16u;
         const __amdgpu_buffer_rsrc_t rkt = st_tile ? rks : rk;
         const __amdgpu_buffer_rsrc_t rvt = st_tile ? rvs : rv;
+        if constexpr (CO) {  // the other row groups read these tiles again: keep them in L2
 #pragma unroll
-        for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rkt, roff[n] + coff);
+            for (int n = 0; n < VI; ++n) kraw[n] = bload128<0>(rkt, roff[n] + coff);
 #pragma unroll
-        for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rvt, roff[n] + coff);
+            for (int n = 0; n < VI; ++n) vraw[n] = bload128<0>(rvt, roff[n] + coff);
+        } else {
+#pragma unroll
+            for (int n = 0; n < VI; ++n) kraw[n] = bload128<2>(rkt, roff[n] + coff);
+#pragma unroll
+            for (int n = 0; n < VI; ++n) vraw[n] = bload128<2>(rvt, roff[n] + coff);
+        }
     };
 
     // keep_mask: tiles that hold no kept cell of the workgroup's mask rows
@@ -1136,6 +1167,9 @@ static int chunk_max_tokens(int D) { return (int)(kChunkMaxBytes / (4 * D)); }
 // against 4*D bytes of K+V per token it streams: at least 5 tokens per packed
 // row keeps that round trip under 40 % of the split's cache traffic.
 constexpr int kTokensPerRow = 5;
+// Fewest splits per group at which 17-32 packed rows still take two 16-row
+// groups rather than one of 32 (see plan_impl).
+constexpr int64_t kPairSplits = 16;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1155,9 +1189,18 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     if (W == 0 && (int64_t)s->n_q * s->Hkv * s->cap + TT >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     if ((int64_t)s->n_q * s->Hq * s->D * 2 >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
     const int64_t R = W > 0 ? G : (int64_t)s->n_q * G;
-    const int rows_per_group = R <= 16 ? 16 : 32;
+    const int64_t heads = (W > 0 ? (int64_t)s->B * s->n_q : (int64_t)s->B) * s->Hkv;
+    // Rows are packed in 16-row groups (one row tile, two waves per SIMD;
+    // the groups of a head read its tiles once from HBM and again from L2)
+    // except for 17-32 rows on many heads: when each group would get fewer
+    // than kPairSplits splits, the 32-row tile (one read of each tile, one
+    // wave per SIMD) is faster on long caches.  Beyond 32 rows a 32-row
+    // tile needs several groups as well, and 16-row groups are faster.
+    const int64_t RG16 = (R + 15) / 16;
+    const int rows_per_group =
+        RG16 != 2 || (int64_t)num_cus * kWgPerCu / (heads * RG16) >= kPairSplits ? 16 : 32;
     const int64_t RG = (R + rows_per_group - 1) / rows_per_group;
-    const int64_t units = (W > 0 ? (int64_t)s->B * s->n_q : (int64_t)s->B) * s->Hkv * RG;
+    const int64_t units = heads * RG;
     const int64_t span_max = W > 0 ? W : s->cap;
     const int64_t rows_eff = R < rows_per_group ? R : rows_per_group;
     int64_t target, cmax, cmin = TT;
@@ -1185,7 +1228,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     if (splits > most) splits = most;
     if (splits > CK_MAX_SPLITS) splits = CK_MAX_SPLITS;
     if (splits < 1) splits = 1;
-    if (units * splits >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
+    if (units * splits + 8 * RG >= ((int64_t)1 << 31)) return CK_ERR_UNSUPPORTED;
 
     pl->units = (int32_t)units;
     pl->splits = (int32_t)splits;
@@ -1235,17 +1278,22 @@ static int device_cus(int* cus) {
 
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-template <int D, int RT, int MODE>
+template <int D, int RT, int MODE, bool CO>
 static hipError_t launch_one(const KParams& kp, int grid, hipStream_t st) {
     void* args[] = {const_cast<KParams*>(&kp)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE>), dim3(grid),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE, CO>), dim3(grid),
                            dim3(kThreads), args, 0, st);
 }
 
+template <int D, int MODE>
+static hipError_t launch_d(int RT, bool co, const KParams& kp, int grid, hipStream_t st) {
+    if (RT == 2) return launch_one<D, 2, MODE, false>(kp, grid, st);
+    return co ? launch_one<D, 1, MODE, true>(kp, grid, st) : launch_one<D, 1, MODE, false>(kp, grid, st);
+}
+
 template <int MODE>
-static hipError_t launch_mode(int D, int RT, const KParams& kp, int grid, hipStream_t st) {
-    if (D == 128) return RT == 1 ? launch_one<128, 1, MODE>(kp, grid, st) : launch_one<128, 2, MODE>(kp, grid, st);
-    return RT == 1 ? launch_one<256, 1, MODE>(kp, grid, st) : launch_one<256, 2, MODE>(kp, grid, st);
+static hipError_t launch_mode(int D, int RT, bool co, const KParams& kp, int grid, hipStream_t st) {
+    return D == 128 ? launch_d<128, MODE>(RT, co, kp, grid, st) : launch_d<256, MODE>(RT, co, kp, grid, st);
 }
 
 static int run(const ck_decode_shape* s, const void* q, const void* k, const void* v, const int32_t* kv_lens,
@@ -1349,17 +1397,20 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.row_bytes = (uint32_t)(s->Hkv * s->D * 2);
 
     const int RT = pl.rows_per_group / 16;
-    const int grid = pl.units * pl.splits;
+    // Several 16-row groups: whole chunks of 8 x row_groups blocks (the
+    // kernel's XCD co-location), the padding blocks exit at once.
+    const bool co = RT == 1 && pl.row_groups > 1;
+    const int grid = co ? (pl.units / pl.row_groups * pl.splits + 7) / 8 * 8 * pl.row_groups : pl.units * pl.splits;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (q8)
-        e = launch_mode<3>(s->D, RT, kp, grid, hs);
+        e = launch_mode<3>(s->D, RT, co, kp, grid, hs);
     else if (W > 0)
-        e = launch_mode<2>(s->D, RT, kp, grid, hs);
+        e = launch_mode<2>(s->D, RT, co, kp, grid, hs);
     else if (keep_mask)
-        e = launch_mode<1>(s->D, RT, kp, grid, hs);
+        e = launch_mode<1>(s->D, RT, co, kp, grid, hs);
     else
-        e = launch_mode<0>(s->D, RT, kp, grid, hs);
+        e = launch_mode<0>(s->D, RT, co, kp, grid, hs);
     return e == hipSuccess ? CK_OK : CK_ERR_HIP;
 }
 

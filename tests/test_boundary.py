@@ -56,14 +56,16 @@ def test_plan_keeps_workgroups_in_one_round(B, Hkv, n_q, W):
     assert p["units"] * p["splits"] <= 256
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,n_q,tile", [
-    (128, 8, 2, 1, 32),    # up to 16 packed rows: 8 KiB tiles, two workgroups per CU
-    (128, 16, 2, 3, 64),   # 24 rows, two row tiles: 16 KiB tiles
-    (256, 16, 4, 1, 16),   # 8 KiB: 16 tokens, PV in 16-token k-blocks
-    (256, 16, 4, 6, 32),   # 24 rows: 16 KiB
+@pytest.mark.parametrize("B,D,Hq,Hkv,n_q,tile", [
+    (1, 128, 8, 2, 1, 32),    # up to 16 packed rows: 8 KiB tiles, two workgroups per CU
+    (1, 128, 16, 2, 3, 32),   # 24 rows as two 16-row groups, 64 splits each
+    (8, 128, 16, 2, 3, 64),   # 24 rows, 8 splits at most: one group, two row tiles, 16 KiB tiles
+    (1, 256, 16, 4, 1, 16),   # 8 KiB: 16 tokens, PV in 16-token k-blocks
+    (1, 256, 16, 4, 6, 16),   # 24 rows as two 16-row groups
+    (8, 256, 16, 4, 6, 32),   # 24 rows in one group: 16 KiB
 ])
-def test_plan_reports_the_kernel_tile(D, Hq, Hkv, n_q, tile):
-    p = ck.plan(shape(n_q=n_q, Hq=Hq, Hkv=Hkv, D=D), num_cus=256)
+def test_plan_reports_the_kernel_tile(B, D, Hq, Hkv, n_q, tile):
+    p = ck.plan(shape(B=B, n_q=n_q, Hq=Hq, Hkv=Hkv, D=D), num_cus=256)
     assert p["tile"] == tile and p["granule"] % p["tile"] == 0
 
 
@@ -89,17 +91,30 @@ def test_plan_minimum_range_grows_with_rows():
     # at least 5 tokens per packed row, in whole tiles
     assert ck.plan(shape(), num_cus=256)["chunk_min"] == 32
     assert ck.plan(shape(n_q=3), num_cus=256)["chunk_min"] == 64
-    assert ck.plan(shape(n_q=6), num_cus=256)["chunk_min"] == 128
+    assert ck.plan(shape(n_q=6), num_cus=256)["chunk_min"] == 96  # 16-row groups
+    assert ck.plan(shape(B=8, n_q=6), num_cus=256)["chunk_min"] == 128  # one 24-row group
     assert ck.plan(shape(B=32, Hq=32, Hkv=8, D=128, cap=32768), num_cus=256)["chunk_min"] == 64
     # a forced split count is used as given
     assert ck.plan(shape(n_q=6), num_splits=64, num_cus=256)["chunk_min"] == 32
 
 
 def test_plan_causal_window_row_groups():
+    # 17-32 packed rows: two 16-row groups while each keeps at least 16
+    # splits, else one 32-row group; more than 32 rows: 16-row groups
     p = ck.plan(shape(n_q=6), num_cus=256)
-    assert p["rows"] == 24 and p["rows_per_group"] == 32 and p["row_groups"] == 1
-    p = ck.plan(shape(n_q=6, Hq=32, Hkv=4), num_cus=256)  # 48 rows -> two groups
-    assert p["rows"] == 48 and p["row_groups"] == 2 and p["units"] == 8
+    assert p["rows"] == 24 and p["rows_per_group"] == 16 and p["row_groups"] == 2 and p["units"] == 8
+    p = ck.plan(shape(n_q=6, Hq=32, Hkv=4), num_cus=256)  # 48 rows -> three groups
+    assert p["rows"] == 48 and p["rows_per_group"] == 16 and p["row_groups"] == 3 and p["units"] == 12
+    p = ck.plan(shape(B=4, n_q=6), num_cus=256)  # 32 units of 16 rows: 8 splits
+    assert p["rows_per_group"] == 32 and p["row_groups"] == 1 and p["units"] == 16
+    p = ck.plan(shape(B=8, n_q=6, Hq=32, Hkv=4), num_cus=256)
+    assert p["rows"] == 48 and p["rows_per_group"] == 16 and p["row_groups"] == 3 and p["units"] == 96
+    p = ck.plan(shape(B=2, n_q=6), num_cus=256)  # 16 units of 16 rows: 16 splits each
+    assert p["rows_per_group"] == 16 and p["row_groups"] == 2 and p["units"] == 16
+    p = ck.plan(shape(n_q=6), num_cus=64)  # a smaller chip: 8 units of 16 rows would get 8 splits
+    assert p["rows_per_group"] == 32 and p["row_groups"] == 1
+    p = ck.plan(shape(Hq=128, Hkv=4), num_cus=256)  # 32-wide GQA groups, one query
+    assert p["rows"] == 32 and p["rows_per_group"] == 16 and p["row_groups"] == 2
 
 
 def test_plan_gather_units_per_query():

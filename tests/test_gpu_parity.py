@@ -397,6 +397,44 @@ def test_group_shapes(Hq, Hkv, n_q):
     assert_close(gpu, oracle_ref(q, k, v, lens, causal=True), what="groups")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,n_q,D,num_splits,rpg,rg", [
+    (1, 16, 4, 6, 256, 0, 16, 2),   # two 16-row groups per head, blocks paired on an XCD
+    (1, 16, 4, 5, 256, 7, 16, 2),   # 28 (head, split) pairs: the grid's last chunk is padded
+    (1, 24, 3, 3, 128, 0, 16, 2),   # three heads: 21 splits, 63 pairs
+    (1, 32, 4, 6, 128, 5, 16, 3),   # three groups of 16, 20 pairs padded to 24
+    (8, 16, 4, 6, 256, 0, 32, 1),   # batch of 8: 24 rows in one group, two row tiles
+    (4, 16, 4, 5, 128, 0, 32, 1),   # batch of 4: 20 rows in one group
+    (8, 32, 4, 6, 128, 0, 16, 3),   # 48 rows: 16-row groups at any batch, 2 splits
+])
+def test_row_group_layouts(B, Hq, Hkv, n_q, D, num_splits, rpg, rg):
+    """More than 16 packed rows: 16-row groups sharing tiles (one XCD,
+    padded grid) for few heads or more than 32 rows, one 32-row group for
+    17-32 rows on many heads; both against the oracle."""
+    cap = 2600
+    lens = [2500 - 297 * b for b in range(B)]
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, cap), num_splits=num_splits)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["rows_per_group"] == rpg and p["row_groups"] == rg
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 71)
+    q = synth.queries(B, n_q, Hq, D, 71)
+    note(f"row groups B={B} Hq={Hq} Hkv={Hkv} n_q={n_q} D={D} S={num_splits}")
+    gpu = dense_gpu(q, k, v, lens, causal=True, num_splits=num_splits)
+    assert_close(gpu, oracle_ref(q, k, v, lens, causal=True), what="row groups")
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_gather_wide_group(num_splits):
+    """32 query heads on one KV head: two 16-row groups share the gathered
+    rows."""
+    B, n_q, Hq, Hkv, D, n_kv = 1, 2, 32, 1, 128, 20000
+    k, v = synth.kv_cache(B, n_kv, Hkv, D, [n_kv], 72)
+    q = synth.queries(B, n_q, Hq, D, 72)
+    idx = synth.topk_lists(B, n_q, Hkv, n_kv, 2048, 64, seed=73)
+    note(f"gather G=32 S={num_splits}")
+    gpu = gather_gpu(q, k, v, [n_kv], idx, causal=True, num_splits=num_splits)
+    assert_close(gpu, oracle_ref(q, k, v, [n_kv], causal=True, idx=idx), what="gather G=32")
+
+
 def test_head_permutation_within_group(layer_d256):
     k, v, (kd, vd) = layer_d256
     q = synth.queries(1, 2, 16, 256, 61)
