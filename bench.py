@@ -338,7 +338,8 @@ def main():
     ap.add_argument("--kv-len", type=int, default=8000)
     ap.add_argument("--headline-only", action="store_true", help="skip the sweeps and the CPU leg")
     ap.add_argument("--only", default="",
-                    help="comma-separated sweep groups to run (dense, sparse, topk, q8); skips the CPU leg")
+                    help="comma-separated sweep groups to run (dense, sparse, topk, q8; window: only the "
+                         "n_q=6 causal window at kv_len 4000, for counter profiles); skips the CPU leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -349,7 +350,7 @@ def main():
         groups = set()
     elif args.only:
         groups = {g.strip() for g in args.only.split(",") if g.strip()}
-        unknown = groups - {"dense", "sparse", "topk", "q8"}
+        unknown = groups - {"dense", "sparse", "topk", "q8", "window"}
         if unknown:
             ap.error(f"unknown sweep groups: {sorted(unknown)}")
 
@@ -383,6 +384,11 @@ def main():
         calibrate_copy()
 
     sweep = {}
+    if "window" in groups:
+        # 24 packed rows on 4 KV heads: two 16-row groups per head sharing tiles
+        r = dense_case(stack, 1, 6, Hq, Hkv, D, [4000], args.steps, args.warmup, causal=True)
+        log(f"window n_q=6 L=4000: {r['us']:.2f} us")
+        sweep["window_n6"] = dict(kv_len=4000, n_q=6, **r)
     if "dense" in groups:
         sweep["kv_len"] = []
         for L in lens_sweep:
