@@ -128,6 +128,24 @@ def test_mtp_window_with_per_query_block_masks(n_q):
                      what=f"MTP mask n_q={n_q}")
 
 
+def test_mtp_window_masks_one_32_row_group():
+    """A batch of verification windows (24 packed rows on 16 sequence x KV
+    head pairs: one 32-row group, two row tiles) with per-query block masks
+    and ragged lengths."""
+    B, n_q, Hq, Hkv, D, cap = 4, 6, 16, 4, 256, 4096
+    lens = [4000, 2500, 1, 3999]
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, cap))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["rows_per_group"] == 32
+    note("mask skip: MTP batch, one 32-row group")
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 1011)
+    q = synth.queries(B, n_q, Hq, D, 1011)
+    idx = synth.block_lists(B, n_q, Hkv, 4000, 8, 64, 16, seed=5500)
+    mask = synth.mask_from_lists(idx, cap)
+    gpu = masked_gpu(q, k, v, lens, mask, causal=True)
+    assert_close(gpu, oracle_ref(q, k, v, lens, causal=True, keep_mask=mask), what="MTP batch mask")
+
+
 def test_all_masked_rows_are_empty():
     """No kept cell anywhere in range: every split skips all its tiles; the
     output is 0 and the lse -inf."""

@@ -174,6 +174,22 @@ def test_d128_step_rows_batch(out_dtype):
     assert_close(gpu, steps_ref(q, k, v, lens, ks, vs), out_dtype, "steps D=128")
 
 
+def test_step_rows_one_32_row_group():
+    """24 packed rows on 16 (sequence, KV head) pairs: one 32-row group with
+    two row tiles; ragged prefixes, one empty."""
+    B, n_q, Hq, Hkv, D, cap = 4, 6, 16, 4, 256, 1600
+    lens = [900, 0, 1501, 37]
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, cap))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["rows_per_group"] == 32 and p["row_groups"] == 1
+    note("step rows one 32-row group")
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 1060)
+    q = synth.queries(B, n_q, Hq, D, 1061)
+    ks, vs = _steps(B, n_q, Hkv, D, 1062)
+    gpu = steps_gpu(q, k, v, lens, ks, vs)
+    assert_close(gpu, steps_ref(q, k, v, lens, ks, vs), what="steps 32-row group")
+
+
 def test_step_rows_equal_causal_window_in_cache(layer_d256):
     """The same window computed both ways on the GPU: drafts beside the cache,
     and drafts written into the cache at [L, L + n_q) with the causal mask."""
@@ -422,15 +438,18 @@ def test_row_group_layouts(B, Hq, Hkv, n_q, D, num_splits, rpg, rg):
     assert_close(gpu, oracle_ref(q, k, v, lens, causal=True), what="row groups")
 
 
-@pytest.mark.parametrize("num_splits", [0, 3])
-def test_gather_wide_group(num_splits):
-    """32 query heads on one KV head: two 16-row groups share the gathered
-    rows."""
-    B, n_q, Hq, Hkv, D, n_kv = 1, 2, 32, 1, 128, 20000
+@pytest.mark.parametrize("n_q,Hq,Hkv,num_splits", [(2, 32, 1, 0), (2, 32, 1, 3), (3, 128, 4, 0)])
+def test_gather_wide_group(n_q, Hq, Hkv, num_splits):
+    """32 query heads per KV head: two 16-row groups share the gathered rows
+    (2 units of lists), or one 32-row group (12 units of lists)."""
+    B, D, n_kv = 1, 128, 20000
     k, v = synth.kv_cache(B, n_kv, Hkv, D, [n_kv], 72)
     q = synth.queries(B, n_q, Hq, D, 72)
     idx = synth.topk_lists(B, n_q, Hkv, n_kv, 2048, 64, seed=73)
-    note(f"gather G=32 S={num_splits}")
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, n_kv), W=idx.shape[-1], num_splits=num_splits)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["rows_per_group"] == (32 if Hkv == 4 else 16)
+    note(f"gather G=32 n_q={n_q} Hkv={Hkv} S={num_splits}")
     gpu = gather_gpu(q, k, v, [n_kv], idx, causal=True, num_splits=num_splits)
     assert_close(gpu, oracle_ref(q, k, v, [n_kv], causal=True, idx=idx), what="gather G=32")
 

@@ -126,6 +126,26 @@ def test_d256_causal_window_matches_oracle(n_q):
         assert_close((out.float().cpu().numpy(), lse.cpu().numpy()), ref, out_dtype, f"q8 window {n_q}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,lens,rpg", [
+    (4, 16, 4, 256, [2000, 1234, 0, 2500], 32),  # 24 rows on 16 pairs: one 32-row group
+    (1, 32, 4, 128, [2500], 16),                 # 48 rows: three 16-row groups sharing tiles
+])
+def test_window_row_groups(B, Hq, Hkv, D, lens, rpg):
+    n_q, page, max_pages = 6, 64, 40
+    note(f"q8 window B={B} Hq={Hq} D={D}")
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, page * max_pages))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["rows_per_group"] == rpg
+    bt, pages, num_pages = filled_case(B, Hkv, D, page, max_pages, lens, 2300 + B)
+    c = make_cache(bt, pages, num_pages, page, Hkv, D)
+    q = synth.queries(B, n_q, Hq, D, 2301)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out, lse = ck.decode_attn_q8(q.to(DEV), c, lens_d, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.attn_q8(q, *pages, bt, np.array(lens, np.int32), 1 / math.sqrt(D), True)
+    assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what=f"q8 window B={B}")
+
+
 def test_d128_ragged_batch_matches_oracle():
     """B=6 ragged lengths (one empty, one at a page boundary), one table entry
     inside a sequence pointing outside the pool (its tokens read as zeros)."""
