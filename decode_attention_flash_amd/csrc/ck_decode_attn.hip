@@ -7,6 +7,8 @@
 // queries -- ride as the N side of 16x16x32 bf16 MFMAs against 16-token
 // tiles of K, so every K/V byte is read once for all of them (comfy-kitchen
 // PR "Performance improvements for qwen 3.x LLM (Part 1)", GQA decode).
+// More rows than one group holds go to several 16-row groups, whose
+// workgroups run on one XCD and share each tile through its L2.
 // Only positions below the device-side length are read (ComfyUI issue
 // "Qwen3.5 text generation attends over the full KV capacity every step…",
 // Feature Idea), an online softmax runs per split, and the workgroup that
@@ -1059,6 +1061,10 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     if (last) {
         merge_slice<D>(p, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
         // ns <= 64: lane c of wave 0 claims slice c, one ballot collects them.
+        // The claims wait until slice 0 is merged: claimed at arrival they
+        // take slices from helpers that arrived just before (their claims
+        // still in flight), and merging those one after another cost 1.5-2.5
+        // us on short sequences.
         if (wave == 0) {
             const bool own = lane >= 1 && lane < ns && atomicExch(cnt + kSliceFlag + lane, 1) == 0;
             const uint64_t mask = __ballot(own);

@@ -98,8 +98,11 @@ enum {
 
 /* Launch plan, exposed so that callers and tests can see how a shape is cut.
  * units = independent (sequence, [query,] KV head, row group) work items;
- * splits = workgroups per unit along the KV range (grid = splits x units);
- * rows = packed query rows per unit (n_q*G dense, G gather). */
+ * splits = workgroups per unit along the KV range (grid = splits x units,
+ * padded to whole chunks of 8 x row_groups workgroups when several 16-row
+ * groups share the tiles of one head; padding workgroups exit at once);
+ * rows = packed query rows per (sequence, [query,] KV head): n_q*G dense,
+ * G gather. */
 typedef struct ck_decode_plan {
     int32_t units;
     int32_t splits;          /* grid splits per unit                         */
@@ -109,7 +112,9 @@ typedef struct ck_decode_plan {
     int32_t granule;         /* split ranges are multiples of this           */
     int32_t rows;            /* query rows per unit                          */
     int32_t row_groups;      /* units per (sequence, query, KV head)         */
-    int32_t rows_per_group;  /* rows handled by one workgroup (16 or 32)     */
+    int32_t rows_per_group;  /* rows handled by one workgroup: 16, or 32 for
+                                17-32 rows when two 16-row groups would get
+                                fewer than 16 splits each                    */
     int32_t slices;          /* column slices the split merge is cut into    */
     int32_t tile;            /* cache positions (or list entries) per wave
                                 tile: a masked scan reads whole tiles that
