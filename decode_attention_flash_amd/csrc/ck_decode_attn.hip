@@ -1434,20 +1434,21 @@ int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv,
     ck_decode_plan pl;
     const int st = ckda::plan_impl(shape, W, 0, 1, &pl);  // validates the shape
     if (st != CK_OK) return st;
-    // Time model fitted to MI355X timings of both paths (cold caches, B = 1,
-    // D 128 and 256, 2 and 4 KV heads, n_q 1/3/6, n_kv 1k-64k, W 128-32k,
-    // scattered cells), in us, with a cell = B * Hkv * 4 * D bytes (the K
-    // and V rows of every KV head at one position):
-    //   gather = 8.0 + 0.150 * MB of listed cells            (n_q * W cells)
-    //   scan   = 10.5 + 1.06 * (n_q - 1) + (0.119 + 0.030 * (n_q - 1)) * MB of window   (n_kv cells)
-    // It names the faster path at 155 of the 158 measured points; the other
-    // three are within 0.5 us of a tie.  The scan
-    // term is its cost with every tile holding a kept cell; clustered
-    // selections make the scan cheaper (skipped tiles), never the gather.
+    // Time model fitted (least relative error) to MI355X timings of both
+    // paths (cold caches, B = 1, D 128 and 256, 2 and 4 KV heads, n_q 1-6,
+    // n_kv 2k-64k, W 128-32k, scattered cells), in us, with a cell =
+    // B * Hkv * 4 * D bytes (the K and V rows of every KV head at one
+    // position):
+    //   gather = 8.4 + 0.141 * MB of listed cells            (n_q * W cells)
+    //   scan   = 10.2 + 0.30 * (n_q - 1) + (0.131 + 0.0167 * (n_q - 1)) * MB of window   (n_kv cells)
+    // It names the faster path at 129 of the 135 measured points; the other
+    // six are within 0.9 us of a tie.  The scan term is its cost with every
+    // tile holding a kept cell; clustered selections make the scan cheaper
+    // (skipped tiles), never the gather.
     const double cell_mb = (double)shape->B * shape->Hkv * 4.0 * shape->D / 1e6;
     const double extra_q = (double)(shape->n_q - 1);
-    const double t_gather = 8.0 + 0.150 * (double)shape->n_q * (double)W * cell_mb;
-    const double t_scan = 10.5 + 1.06 * extra_q + (0.119 + 0.030 * extra_q) * (double)n_kv * cell_mb;
+    const double t_gather = 8.4 + 0.141 * (double)shape->n_q * (double)W * cell_mb;
+    const double t_scan = 10.2 + 0.30 * extra_q + (0.131 + 0.0167 * extra_q) * (double)n_kv * cell_mb;
     *path = t_scan < t_gather ? CK_PATH_SCAN : CK_PATH_GATHER;
     return CK_OK;
 }

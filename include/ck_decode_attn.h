@@ -183,9 +183,9 @@ int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const voi
  * cover most of a long window.  The choice compares two time models fitted
  * to MI355X measurements of both entry points, with a cell = B*Hkv*4*D
  * bytes (K and V of every KV head at one position):
- *   gather: 9.6 us + 0.150 us per MB of the n_q * W listed cells
- *   scan:   12.3 us + 0.85 us * (n_q - 1)
- *           + (0.137 + 0.027 * (n_q - 1)) us per MB of the n_kv window cells
+ *   gather: 8.4 us + 0.141 us per MB of the n_q * W listed cells
+ *   scan:   10.2 us + 0.30 us * (n_q - 1)
+ *           + (0.131 + 0.0167 * (n_q - 1)) us per MB of the n_kv window cells
  * and returns the smaller (the scan term assumes every tile holds a kept
  * cell; clustered selections only make the scan cheaper).
  *   shape : as for the entry points (W >= 1 selects the gather plan checks)
