@@ -438,6 +438,22 @@ def test_row_group_layouts(B, Hq, Hkv, n_q, D, num_splits, rpg, rg):
     assert_close(gpu, oracle_ref(q, k, v, lens, causal=True), what="row groups")
 
 
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_row_groups_edge_lengths(num_splits):
+    """Three 16-row groups sharing tiles (48 rows) over empty, one-cell,
+    tile-boundary and ragged sequences, with one split (no merge, padded
+    grid) or several."""
+    B, n_q, Hq, Hkv, D, cap = 5, 6, 16, 2, 128, 300
+    lens = np.array([0, 1, 32, 65, 299], dtype=np.int32)
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, cap), num_splits=num_splits)
+    assert p["rows_per_group"] == 16 and p["row_groups"] == 3
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 74)
+    q = synth.queries(B, n_q, Hq, D, 74)
+    note(f"row groups edge lengths S={num_splits}")
+    gpu = dense_gpu(q, k, v, lens, causal=True, num_splits=num_splits)
+    assert_close(gpu, oracle_ref(q, k, v, lens, causal=True), what="row group edges")
+
+
 @pytest.mark.parametrize("n_q,Hq,Hkv,num_splits", [(2, 32, 1, 0), (2, 32, 1, 3), (3, 128, 4, 0)])
 def test_gather_wide_group(n_q, Hq, Hkv, num_splits):
     """32 query heads per KV head: two 16-row groups share the gathered rows
