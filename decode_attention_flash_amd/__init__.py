@@ -27,7 +27,9 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misalig
 EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
            "ck_kv_append_q8", "ck_decode_attn_workspace_size",
            "ck_decode_attn_plan", "ck_decode_sparse_path", "ck_decode_topk", "ck_decode_topk_plan",
-           "ck_decode_topk_workspace_size", "ck_status_string")
+           "ck_decode_topk_workspace_size", "ck_workspace_status", "ck_set_spin_limit", "ck_status_string")
+CK_WS_ERR_MERGE = 1
+CK_WS_ERR_TOPK = 2
 
 
 class CkError(RuntimeError):
@@ -100,6 +102,10 @@ def lib():
         L.ck_decode_topk_plan.restype = ctypes.c_int
         L.ck_decode_topk_workspace_size.argtypes = [sp, i32, i32, i32, ctypes.POINTER(sz)]
         L.ck_decode_topk_workspace_size.restype = ctypes.c_int
+        L.ck_workspace_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
+        L.ck_workspace_status.restype = ctypes.c_int
+        L.ck_set_spin_limit.argtypes = [i32]
+        L.ck_set_spin_limit.restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
         L.ck_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -156,6 +162,9 @@ def _cached_workspace(shape: Shape, W: int, num_splits: int, device, stream_hand
         return None
     # A workspace belongs to one plan (its counters are laid out for it) and
     # to one stream (launches that may overlap need different workspaces).
+    # Graphs captured without an explicit workspace all record the one of
+    # their capture stream: replay such graphs one after another on one
+    # stream, or give each graph that may run concurrently its own workspace.
     key = (torch.device(device).index, int(stream_handle or 0),
            tuple(getattr(shape, f) for f, _ in Shape._fields_), W, num_splits)
     ws = _ws_cache.get(key)
@@ -163,6 +172,32 @@ def _cached_workspace(shape: Shape, W: int, num_splits: int, device, stream_hand
         ws = torch.zeros(n, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
+
+
+def workspace_status(workspace: torch.Tensor, stream=None) -> int:
+    """The sticky status bits of a workspace (``ck_workspace_status``):
+    CK_WS_ERR_MERGE when a split merge gave up waiting, CK_WS_ERR_TOPK when a
+    top-k row barrier did; 0 when every launch since the buffer was zeroed
+    completed its waits.  Synchronizes the stream."""
+    v = ctypes.c_int32(0)
+    st = lib().ck_workspace_status(_ptr(workspace), ctypes.c_void_p(_stream_handle(stream, workspace.device)),
+                                   ctypes.byref(v))
+    if st != 0:
+        raise CkError(st, "ck_workspace_status")
+    return v.value
+
+
+def set_spin_limit(polls: int) -> None:
+    """Polls a bounded wait makes before giving up (``ck_set_spin_limit``;
+    0 restores the default).  For tests of the failure path."""
+    st = lib().ck_set_spin_limit(int(polls))
+    if st != 0:
+        raise CkError(st, "ck_set_spin_limit")
+
+
+def cached_workspaces() -> list:
+    """The workspaces the entry points allocated for themselves."""
+    return list(_ws_cache.values()) + list(_topk_ws.values())
 
 
 def release_workspaces() -> None:
@@ -188,24 +223,46 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _outputs(q, out_dtype, out, lse, return_lse):
+    """Checks (or allocates) out [B, n_q, Hq, D] and lse [B, n_q, Hq]: the
+    kernels size their stores from q's shape."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _check(out, "out", out_dtype)
+        _check_shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check(lse, "lse", torch.float32)
+        _check_shape(lse, "lse", q.shape[:3])
+    return out, lse
+
+
+def _check_lens(kv_lens: torch.Tensor, B: int, name: str = "kv_lens") -> None:
+    _check(kv_lens, name, torch.int32)
+    if kv_lens.dim() != 1 or kv_lens.numel() != B:
+        raise ValueError(f"{name} must have shape ({B},), got {tuple(kv_lens.shape)}")
+
+
 def _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse):
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
     _check(q, "q", torch.bfloat16)
     _check(k_cache, "k_cache", torch.bfloat16)
     _check(v_cache, "v_cache", torch.bfloat16)
-    _check(kv_lens, "kv_lens", torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, n_q, Hq, D] and k_cache [B, cap, Hkv, D]")
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must have the same shape")
     shape = shape_of(q, k_cache)
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    else:
-        _check(out, "out", out_dtype)
-    if lse is None and return_lse:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    elif lse is not None:
-        _check(lse, "lse", torch.float32)
+    _check_lens(kv_lens, shape.B)
+    out, lse = _outputs(q, out_dtype, out, lse, return_lse)
     odt = CK_DT_BF16 if out_dtype == torch.bfloat16 else CK_DT_F32
     return shape, out, lse, odt
 
@@ -222,6 +279,7 @@ def decode_attn(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, cau
     shape, out, lse, odt = _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse)
     if keep_mask is not None:
         _check(keep_mask, "keep_mask", torch.uint8)
+        _check_shape(keep_mask, "keep_mask", (shape.B, shape.n_q, shape.Hkv, shape.cap))
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     st_handle = _stream_handle(stream, q.device)
@@ -337,8 +395,8 @@ def decode_topk(scores, kv_lens, k: int, *, tail: int = 0, causal: bool = False,
     padded with -1: int32 [B, n_q, Hs, k + tail], ready for decode_attn_gather
     (Hs = 1 gives one list per query: pass it as [B, n_q, W])."""
     _check(scores, "scores", torch.float32)
-    _check(kv_lens, "kv_lens", torch.int32)
     shape, Hs = _topk_shape(scores, num_kv_heads)
+    _check_lens(kv_lens, shape.B)
     W = int(k) + int(tail)
     if out is None:
         out = torch.empty((shape.B, shape.n_q, Hs, W), dtype=torch.int32, device=scores.device)
@@ -440,8 +498,10 @@ def kv_append_q8(cache: PagedQ8Cache, k_new, v_new, start, stream=None):
     device (usually kv_lens, which the caller then advances)."""
     _check(k_new, "k_new", torch.bfloat16)
     _check(v_new, "v_new", torch.bfloat16)
-    _check(start, "start", torch.int32)
+    if k_new.dim() != 4:
+        raise ValueError("k_new must be [B, n_new, Hkv, D]")
     B, n_new, Hkv, D = k_new.shape
+    _check_lens(start, B, "start")
     if tuple(v_new.shape) != tuple(k_new.shape) or (B, Hkv, D) != (cache.B, cache.Hkv, cache.D):
         raise ValueError("k_new / v_new must be [B, n_new, Hkv, D] matching the cache")
     shape = Shape(B, n_new, Hkv, Hkv, D, cache.capacity)
@@ -460,19 +520,14 @@ def decode_attn_q8(q, cache: PagedQ8Cache, kv_lens, *, scale: float | None = Non
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
     _check(q, "q", torch.bfloat16)
-    _check(kv_lens, "kv_lens", torch.int32)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, n_q, Hq, D]")
     B, n_q, Hq, D = q.shape
     if B != cache.B or D != cache.D:
         raise ValueError("q and the cache disagree on B or D")
+    _check_lens(kv_lens, B)
     shape = Shape(B, n_q, Hq, cache.Hkv, D, cache.capacity)
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    else:
-        _check(out, "out", out_dtype)
-    if lse is None and return_lse:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    elif lse is not None:
-        _check(lse, "lse", torch.float32)
+    out, lse = _outputs(q, out_dtype, out, lse, return_lse)
     odt = CK_DT_BF16 if out_dtype == torch.bfloat16 else CK_DT_F32
     if scale is None:
         scale = 1.0 / math.sqrt(D)

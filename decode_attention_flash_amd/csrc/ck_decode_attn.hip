@@ -58,7 +58,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // 128-byte line.
 constexpr int kCntStride = 512, kParity = 0, kSet0 = 128, kSetStride = 128;
 constexpr int kStarted = 0, kArrived = 32, kSliceFlag = 64;
-constexpr int kSpinLimit = 1 << 22;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 
@@ -110,7 +109,9 @@ struct KParams {
     float* lse;
     float* ws_o;
     float* ws_ml;
-    int32_t* ws_cnt;  // per unit kCntStride ints: counters and slice claim flags
+    int32_t* ws_cnt;     // per unit kCntStride ints: counters and slice claim flags
+    int32_t* ws_status;  // sticky error bits (CK_WS_*), set with an atomic OR
+    int32_t spin_limit;  // polls a merge helper makes before it gives up
     // paged INT8 cache (MODE 3)
     const int8_t* kq;
     const int8_t* vq;
@@ -392,6 +393,22 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
             store4<D>(p, orow, 4 * col, acc * inv);
             if (col == 0 && p.lse != nullptr) p.lse[orow] = den > 0.f ? (Mg + __log2f(den)) * kLn2 : -INFINITY;
         }
+    }
+}
+
+// A merge that gave up: its column slice of the output (and the lse of its
+// rows) reads NaN, so the failure is visible in the results as well as in
+// the workspace status word.
+template <int D>
+__device__ void fill_slice_nan(const KParams& p, int nrows, int c, int ns, int b, int g, int iq, bool gather,
+                               int row0) {
+    constexpr int D4 = D / 4;
+    const int col_lo = c * D4 / ns, col_hi = (c + 1) * D4 / ns, ncol = col_hi - col_lo;
+    for (int k = threadIdx.x; k < nrows * ncol; k += kThreads) {
+        const int rr = k / ncol, col = col_lo + k % ncol;
+        const size_t orow = out_row(p, b, g, row0 + rr, iq, gather);
+        store4<D>(p, orow, 4 * col, f32x4{NAN, NAN, NAN, NAN});
+        if (col == 0 && p.lse != nullptr) p.lse[orow] = NAN;
     }
 }
 
@@ -1076,14 +1093,19 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     } else {
         const int c = n_active - 1 - rank;
         if (tid == 0) {
+            // 0: not ours, 1: merge, 2: gave up waiting
             int ok = 0;
             if (started_seen == n_active && atomicExch(cnt + kSliceFlag + c, 1) == 0) {
                 ok = 1;
                 int spins = 0;
                 while (atomic_ld(cnt + kArrived) < n_active) {
                     __builtin_amdgcn_s_sleep(2);
-                    if (++spins > kSpinLimit) {  // cannot happen while every split runs
-                        ok = 0;
+                    // Cannot happen while every split runs (they all started
+                    // before the claim); if the GPU is held elsewhere that
+                    // long, report it instead of waiting on.
+                    if (++spins > p.spin_limit) {
+                        ok = 2;
+                        atomicOr(p.ws_status, CK_WS_ERR_MERGE);
                         break;
                     }
                 }
@@ -1091,7 +1113,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             ms.flag = ok;
         }
         __syncthreads();
-        if (ms.flag) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+        if (ms.flag == 1) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+        if (ms.flag == 2) fill_slice_nan<D>(p, nrows, c, ns, b, g, iq, GATHER, row0);
     }
 }
 
@@ -1178,6 +1201,16 @@ constexpr int kTokensPerRow = 5;
 constexpr int64_t kPairSplits = 16;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// The workspace opens with 256 bytes whose first int32 is the status word.
+constexpr size_t kWsHeader = 256;
+
+// Polls a merge helper (or a top-k row barrier) makes before it gives up.
+// At about a microsecond per poll the default is seconds: far beyond any
+// launch whose workgroups all run, so it only ends a wait that cannot finish.
+constexpr int32_t kDefaultSpinLimit = 1 << 22;
+static std::atomic<int32_t> g_spin_limit{kDefaultSpinLimit};
+
+int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
 
 static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int num_cus,
                      ck_decode_plan* pl) {
@@ -1256,7 +1289,7 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
         pl->workspace_bytes = 0;
     } else {
         const size_t parts = (size_t)units * (size_t)splits * (size_t)rows_per_group;
-        pl->workspace_bytes = align256((size_t)units * kCntStride * sizeof(int32_t)) +
+        pl->workspace_bytes = kWsHeader + align256((size_t)units * kCntStride * sizeof(int32_t)) +
                               align256(parts * s->D * sizeof(float)) + align256(parts * 2 * sizeof(float));
     }
     return CK_OK;
@@ -1371,6 +1404,8 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     if (pl.workspace_bytes > 0) {
         const size_t parts = (size_t)pl.units * pl.splits * pl.rows_per_group;
         char* w = static_cast<char*>(workspace);
+        kp.ws_status = reinterpret_cast<int32_t*>(w);
+        w += kWsHeader;
         kp.ws_cnt = reinterpret_cast<int32_t*>(w);
         w += align256((size_t)pl.units * kCntStride * sizeof(int32_t));
         kp.ws_o = reinterpret_cast<float*>(w);
@@ -1393,6 +1428,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.c_max = pl.chunk_max;
     kp.gran = pl.granule;
     kp.slices = pl.slices;
+    kp.spin_limit = spin_limit();
     kp.W = W;
     kp.idx_head_stride = idx_head_stride;
     kp.scale_log2 = (float)((double)scale * 1.4426950408889634074);
@@ -1540,6 +1576,23 @@ int ck_kv_append_q8(const ck_decode_shape* shape, const void* k_new, const void*
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(ckda::kThreads), args, 0,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CK_OK : CK_ERR_HIP;
+}
+
+int ck_workspace_status(const void* workspace, void* stream, int32_t* status) {
+    if (!workspace || !status) return CK_ERR_ARG;
+    if (!ckda::aligned(workspace, 256)) return CK_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, hs) != hipSuccess) return CK_ERR_HIP;
+    if (hipStreamSynchronize(hs) != hipSuccess) return CK_ERR_HIP;
+    *status = v;
+    return CK_OK;
+}
+
+int ck_set_spin_limit(int32_t polls) {
+    if (polls < 0) return CK_ERR_ARG;
+    ckda::g_spin_limit.store(polls == 0 ? ckda::kDefaultSpinLimit : polls, std::memory_order_relaxed);
+    return CK_OK;
 }
 
 const char* ck_status_string(int status) {

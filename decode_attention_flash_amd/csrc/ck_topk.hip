@@ -26,13 +26,16 @@
 
 #include "ck_decode_attn.h"
 
+namespace ckda {
+int spin_limit();  // polls a bounded wait makes before it gives up (ck_decode_attn.hip)
+}
+
 namespace cktk {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;                  // positions per thread in a super-block
 constexpr int kSuper = kPerThread * kThreads;   // positions per super-block
 constexpr int kBins = 2048;           // widest digit: 11 bits
-constexpr int kSpinLimit = 1 << 22;
 constexpr int kAuxDevice = 16;  // sc1: served from the device's point of coherence
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
@@ -44,6 +47,7 @@ constexpr int kWsCounts = kWsHist + 3 * kBins;
 constexpr int kMaxWgPerRow = 256;
 constexpr int kWsCand = kWsCounts + 2 * kMaxWgPerRow;  // then (key, position) pairs, per workgroup
 constexpr int kCand = 4096;                               // threshold-bin cells gathered in LDS
+constexpr size_t kWsHeader = 256;                         // the status word, then the rows
 // Super-blocks of a workgroup whose keys stay in registers: 1 when a
 // workgroup holds one (a row split over many workgroups), else 8.  Each
 // cached super-block unrolls every pass over the keys once more, and the
@@ -56,6 +60,8 @@ struct TParams {
     const int32_t* kv_lens;   // [B]
     int32_t* idx;             // [B, n_q, Hs, W]
     uint32_t* ws;             // rows x kWsRowWords (P > 1)
+    int32_t* status;          // the workspace's status word (P > 1)
+    int32_t spin_limit;       // polls at a row barrier before giving up
     int32_t B, n_q, Hs, cap, causal;
     int32_t k, tail, W;
     int32_t P;                // workgroups per row
@@ -253,7 +259,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             int spins = 0;
             while (ld_dev(ctr) < barriers * p.P) {
                 __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) break;  // cannot happen while the row's workgroups run
+                // Cannot happen while the row's workgroups run: report it and
+                // go on (every store below stays inside the row whatever the
+                // counts say), so the kernel still ends.
+                if (++spins > p.spin_limit) {
+                    __hip_atomic_fetch_or(p.status, CK_WS_ERR_TOPK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
             }
         }
         __syncthreads();
@@ -574,7 +586,8 @@ static int plan(const ck_decode_shape* s, int32_t Hs, int32_t k, int32_t tail, i
     pl->P = (int32_t)wg;
     pl->cand_per_wg = (int32_t)(per_max * kSuper);
     pl->row_words = (uint64_t)kWsCand + (uint64_t)wg * (uint64_t)pl->cand_per_wg * 2u;
-    pl->ws_bytes = wg > 1 ? (size_t)rows * (size_t)pl->row_words * sizeof(uint32_t) : 0;
+    // 256 bytes of header (the status word) before the rows
+    pl->ws_bytes = wg > 1 ? kWsHeader + (size_t)rows * (size_t)pl->row_words * sizeof(uint32_t) : 0;
     return CK_OK;
 }
 
@@ -629,7 +642,9 @@ int ck_decode_topk(const ck_decode_shape* shape, const float* scores, int32_t Hs
     p.scores = scores;
     p.kv_lens = kv_lens;
     p.idx = idx;
-    p.ws = (uint32_t*)workspace;
+    p.status = (int32_t*)workspace;
+    p.ws = workspace ? (uint32_t*)((char*)workspace + cktk::kWsHeader) : nullptr;
+    p.spin_limit = ckda::spin_limit();
     p.B = shape->B;
     p.n_q = shape->n_q;
     p.Hs = Hs;

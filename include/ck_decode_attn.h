@@ -42,15 +42,17 @@
  *
  * Workspace: when the plan splits the KV range (see
  * ck_decode_attn_workspace_size) the caller passes a device buffer of at
- * least that many bytes, 256-byte aligned.  It starts with a 2 KiB block of
- * int32 counters per unit: a parity word and two counter sets.  A launch uses
- * the set the parity names, which is zero when it starts, clears the other
- * set and flips the parity for the next launch (the partial results after the
- * counters are scratch).  So a buffer ZEROED ONCE serves any number of launches
- * of the same plan (same shape, W, num_splits and device), eager or replayed
- * from a captured HIP graph without a memset node.  A buffer used for one
- * plan must be zeroed again before it serves a different plan, and launches
- * that may run concurrently (different streams) need different workspaces.
+ * least that many bytes, 256-byte aligned.  It starts with a 256-byte header
+ * whose first int32 is the status word (see ck_workspace_status), then a
+ * 2 KiB block of int32 counters per unit: a parity word and two counter sets.
+ * A launch uses the set the parity names, which is zero when it starts,
+ * clears the other set and flips the parity for the next launch (the partial
+ * results after the counters are scratch).  So a buffer ZEROED ONCE serves
+ * any number of launches of the same plan (same shape, W, num_splits and
+ * device), eager or replayed from a captured HIP graph without a memset
+ * node.  A buffer used for one plan must be zeroed again before it serves a
+ * different plan, and launches that may run concurrently (different streams,
+ * or graphs replayed on different streams) need different workspaces.
  *
  * Launch shape depends only on the shape, W, num_splits and the device, never
  * on kv_lens or idx contents, so one captured launch stays valid while the
@@ -225,7 +227,8 @@ int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv,
  *   idx       : int32 [B, n_q, Hs, k + tail], device memory, written whole
  *   workspace : as for the attention entries: ck_decode_topk_workspace_size
  *               bytes (0 when one workgroup serves a row), 256-byte aligned,
- *               zeroed once; every launch leaves it zeroed.
+ *               zeroed once; every launch leaves it zeroed apart from the
+ *               status word in its 256-byte header (ck_workspace_status).
  * Errors as for the attention entries; nothing is launched on error.
  * CK_ERR_UNSUPPORTED also when cap * 4 bytes reaches 2 GiB, or when the
  * rows' workgroups would need 2 GiB of (key, position) slots for one row
@@ -311,6 +314,36 @@ int ck_decode_attn_q8(const ck_decode_shape* shape, const void* q, const ck_q8_c
  * used.  The caller advances kv_lens afterwards.  No workspace. */
 int ck_kv_append_q8(const ck_decode_shape* shape, const void* k_new, const void* v_new,
                     const int32_t* start, const ck_q8_cache* cache, void* stream);
+
+/* Workspace status.  Every workspace (of the attention entries and of
+ * ck_decode_topk) opens with 256 bytes whose first int32 is a status word of
+ * sticky bits, zero after the caller zeroes the buffer.  A launch waits on
+ * other workgroups of the same launch in two places: a split-merge helper
+ * waits for the unit's last split to arrive (only once every split of the
+ * unit has started), and a top-k row waits at barriers for the row's other
+ * workgroups (all resident by construction).  Every such wait is bounded.  One that gives up sets a bit:
+ *   CK_WS_ERR_MERGE : a split merge gave up; its column slice of out (and
+ *                     the lse of its rows) holds NaN
+ *   CK_WS_ERR_TOPK  : a top-k row barrier gave up; that launch's lists are
+ *                     not valid
+ * and the kernel still ends normally, leaving the counters ready for the
+ * next launch.  Neither can happen while the launch's workgroups all make
+ * progress; it would take the GPU being held by other work for seconds.  The
+ * bits stay set until the caller zeroes the header (or the whole buffer):
+ * a nonzero status means that some launch since then returned invalid
+ * results.
+ * ck_workspace_status copies the word to *status; it waits for the work
+ * queued on `stream` before it (it synchronizes that stream), so it is not
+ * for use inside a captured graph.  workspace: 256-byte aligned. */
+#define CK_WS_ERR_MERGE 1
+#define CK_WS_ERR_TOPK 2
+int ck_workspace_status(const void* workspace, void* stream, int32_t* status);
+
+/* Polls a bounded wait makes before it gives up (process-wide, read at each
+ * launch; 0 restores the default of 2^22, about seconds).  Failure handling
+ * can be exercised by lowering it: every kernel still ends normally and the
+ * workspace status reports the give-up.  polls >= 0. */
+int ck_set_spin_limit(int32_t polls);
 
 /* Static text for a status code. */
 const char* ck_status_string(int status);

@@ -133,10 +133,14 @@ def check_counts(out, visible_sets, G, nbits=17):
 
 
 def counters_ready(ws: torch.Tensor, units: int) -> bool:
-    """The workspace's counter blocks are ready for another launch: for each
-    unit (2 KiB: a parity word, then two sets of 128 ints), the set the
-    parity names is all zero."""
-    blk = ws[:units * 2048].view(torch.int32).view(units, 512).cpu().numpy()
+    """The workspace is ready for another launch of its plan: the status word
+    (the first int32 of a 256-byte header) is 0, and for each unit (2 KiB of
+    counters after the header: a parity word, then two sets of 128 ints) the
+    set the parity names is all zero."""
+    w = ws.view(torch.int32).cpu().numpy()
+    if w[0] != 0:
+        return False
+    blk = w[64:64 + units * 512].reshape(units, 512)
     for u in range(units):
         par = int(blk[u, 0]) & 1
         if np.any(blk[u, 128 + 128 * par:256 + 128 * par] != 0):

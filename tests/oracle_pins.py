@@ -4,7 +4,10 @@ the mutation test, which runs them against deliberately broken copies).
 Nothing here re-types the oracle's formula.  Each check compares it with
 something fixed from outside it:
   * torch's scaled_dot_product_attention and logsumexp in float64 (a library
-    routine) with an explicit boolean mask, K/V expanded over the GQA group;
+    routine) with an explicit boolean mask, K/V expanded over the GQA group,
+    at head dims 4, 16, 128 and 256;
+  * attention written out in plain Python floats with math.exp, on tiny
+    shapes (an implementation independent of both the oracle and torch);
   * closed forms (uniform V, one visible key, K = 0, two keys);
   * invariants (split count, gather vs mask, causal row vs a shorter plain
     decode, head permutation within a group, duplicate cells);
@@ -118,6 +121,79 @@ def check_sdpa_dense(lib) -> float:
             o, l = oracle.attn(q, k, v, lens, scale, causal, lib=lib)
             ro, rl = sdpa_reference(q, k, v, lens, np.float32(scale), causal)
             worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    return worst
+
+
+def check_sdpa_wide_heads(lib) -> float:
+    """SDPA at the head dims the kernels serve (128 and 256): dense, causal,
+    keep_mask and gather sets, B = 2, cap = 64."""
+    worst = 0.0
+    rng = np.random.default_rng(17)
+    for D in (128, 256):
+        q, k, v, lens = small_case(B=2, n_q=3, Hq=4, Hkv=2, D=D, cap=64, lens=(61, 3), seed=D)
+        scale = np.float32(1.0 / math.sqrt(D))
+        km = (rng.random((2, 3, 2, 64)) < 0.6).astype(np.uint8)
+        idx = gather_lists(2, 3, 2, 64, 20, seed=D + 1)
+        for causal in (False, True):
+            for kw in ({}, {"keep_mask": km}, {"idx": idx}):
+                o, l = oracle.attn(q, k, v, lens, float(scale), causal, lib=lib, **kw)
+                ro, rl = sdpa_reference(q, k, v, lens, scale, causal, **kw)
+                worst = max(worst, max_dev(o, ro), max_dev(l, rl))
+    return worst
+
+
+def attn_brute(q, k, v, lens, scale, causal, keep_mask=None, idx=None):
+    """Attention written out with Python floats and math.exp, cell by cell:
+    for each (b, i, h) the visible cells in order, their scores, the max, the
+    exponentials, their sum, the weighted V rows and the log-sum-exp.  Small
+    shapes only."""
+    B, n_q, Hq, D = q.shape
+    cap, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    Q, K, V = q.float().tolist(), k.float().tolist(), v.float().tolist()
+    sc = float(np.float32(scale))
+    out = [[[[0.0] * D for _ in range(Hq)] for _ in range(n_q)] for _ in range(B)]
+    lse = [[[-math.inf] * Hq for _ in range(n_q)] for _ in range(B)]
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), cap)
+        for i in range(n_q):
+            lim = min(max(L - n_q + i + 1, 0), L) if causal else L
+            for h in range(Hq):
+                g = h // G
+                if idx is None:
+                    cells = [j for j in range(lim) if keep_mask is None or keep_mask[b][i][g][j]]
+                else:
+                    lst = idx[b][i] if np.asarray(idx).ndim == 3 else idx[b][i][g]
+                    cells = [int(j) for j in lst if 0 <= int(j) < lim]
+                if not cells:
+                    continue
+                s = [sc * sum(Q[b][i][h][d] * K[b][j][g][d] for d in range(D)) for j in cells]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                den = math.fsum(e)
+                for d in range(D):
+                    out[b][i][h][d] = math.fsum(w * V[b][j][g][d] for w, j in zip(e, cells)) / den
+                lse[b][i][h] = m + math.log(den)
+    return np.array(out), np.array(lse)
+
+
+def check_python_bruteforce(lib) -> float:
+    """Against attention written out in plain Python (math.exp) on tiny
+    shapes (D = 4, cap = 8, two query heads on one KV head, n_q <= 3):
+    dense, causal, keep_mask and gather sets, with garbage past the length
+    and empty rows."""
+    worst = 0.0
+    rng = np.random.default_rng(19)
+    for n_q in (1, 2, 3):
+        for lens in ((8, 0), (5, 2), (3, 8)):
+            q, k, v, L = small_case(B=2, n_q=n_q, Hq=2, Hkv=1, D=4, cap=8, lens=lens, seed=10 * n_q + lens[1])
+            km = (rng.random((2, n_q, 1, 8)) < 0.5).astype(np.uint8)
+            idx = rng.integers(-2, 10, size=(2, n_q, 1, 6)).astype(np.int32)
+            for causal in (False, True):
+                for kw in ({}, {"keep_mask": km}, {"idx": idx}):
+                    o, l = oracle.attn(q, k, v, L, 0.7, causal, lib=lib, **kw)
+                    ro, rl = attn_brute(q, k, v, L, 0.7, causal, **kw)
+                    worst = max(worst, max_dev(o, ro), max_dev(l, rl))
     return worst
 
 
@@ -503,6 +579,8 @@ def check_topk_permutation(lib) -> float:
 ALL_CHECKS = {
     "sdpa_dense": check_sdpa_dense,
     "sdpa_mask": check_sdpa_mask,
+    "sdpa_wide_heads": check_sdpa_wide_heads,
+    "python_bruteforce": check_python_bruteforce,
     "sdpa_gather": check_sdpa_gather,
     "duplicates": check_duplicates,
     "closed_forms": check_closed_forms,
