@@ -23,8 +23,9 @@ CK_MAX_SPLITS = 256
 CK_PATH_GATHER = 0
 CK_PATH_SCAN = 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misaligned pointer",
-          -4: "workspace missing or too small", -5: "HIP runtime error"}
-EXPORTS = ("ck_decode_attn", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
+          -4: "workspace missing or too small", -5: "HIP runtime error",
+          -6: "shape needs more than the no-alloc scratch holds"}
+EXPORTS = ("ck_decode_attn", "ck_decode_attn_noalloc", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
            "ck_kv_append_q8", "ck_decode_attn_workspace_size",
            "ck_decode_attn_plan", "ck_decode_sparse_path", "ck_decode_topk", "ck_decode_topk_plan",
            "ck_decode_topk_workspace_size", "ck_workspace_status", "ck_set_spin_limit", "ck_status_string")
@@ -80,6 +81,9 @@ def lib():
         L.ck_decode_attn.argtypes = [sp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
                                      ctypes.c_int, vp, vp, sz, ctypes.c_int, vp]
         L.ck_decode_attn.restype = ctypes.c_int
+        L.ck_decode_attn_noalloc.argtypes = [sp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
+                                             ctypes.c_int, vp, ctypes.c_int, vp]
+        L.ck_decode_attn_noalloc.restype = ctypes.c_int
         L.ck_decode_attn_gather.argtypes = [sp, vp, vp, vp, vp, vp, i32, i64, ctypes.c_float,
                                             ctypes.c_int, vp, ctypes.c_int, vp, vp, sz,
                                             ctypes.c_int, vp]
@@ -292,6 +296,28 @@ def decode_attn(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, cau
                               ws_bytes, num_splits, ctypes.c_void_p(st_handle))
     if st != 0:
         raise CkError(st, "ck_decode_attn")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_attn_noalloc(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, causal: bool = False,
+                        keep_mask=None, out_dtype=torch.float32, out=None, lse=None, return_lse=False,
+                        num_splits: int = 0, stream=None):
+    """``decode_attn`` through ``ck_decode_attn_noalloc``: the split merge
+    uses the library's fixed per-device scratch, so the launch needs no
+    workspace (the outputs are still the caller's).  Calls that may overlap
+    on one device must not be issued."""
+    shape, out, lse, odt = _prepare(q, k_cache, v_cache, kv_lens, out_dtype, out, lse, return_lse)
+    if keep_mask is not None:
+        _check(keep_mask, "keep_mask", torch.uint8)
+        _check_shape(keep_mask, "keep_mask", (shape.B, shape.n_q, shape.Hkv, shape.cap))
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    st_handle = _stream_handle(stream, q.device)
+    st = lib().ck_decode_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
+                                      ctypes.c_float(scale), 1 if causal else 0, _ptr(keep_mask), _ptr(out), odt,
+                                      _ptr(lse), num_splits, ctypes.c_void_p(st_handle))
+    if st != 0:
+        raise CkError(st, "ck_decode_attn_noalloc")
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "ck_decode_attn.h"
 
@@ -1335,11 +1336,40 @@ static hipError_t launch_mode(int D, int RT, bool co, const KParams& kp, int gri
     return D == 128 ? launch_d<128, MODE>(RT, co, kp, grid, st) : launch_d<256, MODE>(RT, co, kp, grid, st);
 }
 
+// ---- the file-scope scratch of ck_decode_attn_noalloc ----------------------
+// For callers that cannot allocate: the split merge's workspace (status
+// header, the counters of up to kScratchUnits units at fixed places, then
+// the partial results) lives in this array, one copy per device, zero when
+// the code object loads.  Every launch leaves each unit's next counter set
+// at zero, so any sequence of shapes may share it; calls that overlap on
+// one device race on it.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int64_t kScratchUnits = 1024;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+// The device address of `scratch` on the current device (looked up once per
+// device; the array's name is only a host-side stand-in).
+static int scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CK_ERR_HIP;
+    if (dev < 0 || dev >= 64) return CK_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return CK_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return CK_OK;
+}
+
 static int run(const ck_decode_shape* s, const void* q, const void* k, const void* v, const int32_t* kv_lens,
                const uint8_t* keep_mask, const int32_t* idx, int32_t W, int64_t idx_head_stride, float scale,
                int causal, void* out, int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
                int num_splits, void* stream, const void* k_step = nullptr, const void* v_step = nullptr,
-               const ck_q8_cache* q8 = nullptr) {
+               const ck_q8_cache* q8 = nullptr, int64_t counter_units = 0) {
     if (!s) return CK_ERR_ARG;
     ck_decode_plan pl;
     int st = plan_impl(s, W, num_splits, 1, &pl);  // shape checks only
@@ -1374,10 +1404,18 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     if (st != CK_OK) return st;
     st = plan_impl(s, W, num_splits, cus, &pl);
     if (st != CK_OK) return st;
+    // counter_units > 0: a workspace whose counter blocks are laid out for
+    // that many units whatever the plan (the file-scope scratch), so that
+    // unit u's counters sit at the same place for every shape.
+    const size_t parts = (size_t)pl.units * pl.splits * pl.rows_per_group;
+    const int64_t cnt_units = counter_units > 0 ? counter_units : pl.units;
+    if (counter_units > 0 && pl.units > counter_units) return CK_ERR_SCRATCH;
+    const size_t need = kWsHeader + align256((size_t)cnt_units * kCntStride * sizeof(int32_t)) +
+                        align256(parts * s->D * sizeof(float)) + align256(parts * 2 * sizeof(float));
     if (pl.workspace_bytes > 0) {
         if (!workspace) return CK_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return CK_ERR_ALIGN;
-        if (workspace_bytes < pl.workspace_bytes) return CK_ERR_WORKSPACE;
+        if (workspace_bytes < need) return counter_units > 0 ? CK_ERR_SCRATCH : CK_ERR_WORKSPACE;
     }
 
     KParams kp{};
@@ -1402,12 +1440,11 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.out = out;
     kp.lse = lse;
     if (pl.workspace_bytes > 0) {
-        const size_t parts = (size_t)pl.units * pl.splits * pl.rows_per_group;
         char* w = static_cast<char*>(workspace);
         kp.ws_status = reinterpret_cast<int32_t*>(w);
         w += kWsHeader;
         kp.ws_cnt = reinterpret_cast<int32_t*>(w);
-        w += align256((size_t)pl.units * kCntStride * sizeof(int32_t));
+        w += align256((size_t)cnt_units * kCntStride * sizeof(int32_t));
         kp.ws_o = reinterpret_cast<float*>(w);
         w += align256(parts * s->D * sizeof(float));
         kp.ws_ml = reinterpret_cast<float*>(w);
@@ -1511,6 +1548,17 @@ int ck_decode_attn(const ck_decode_shape* shape, const void* q, const void* k_ca
                      out_dtype, lse, workspace, workspace_bytes, num_splits, stream);
 }
 
+int ck_decode_attn_noalloc(const ck_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* kv_lens, float scale, int causal, const uint8_t* keep_mask, void* out,
+                           int out_dtype, float* lse, int num_splits, void* stream) {
+    void* ws = nullptr;
+    const int st = ckda::scratch_ptr(&ws);
+    if (st != CK_OK) return st;
+    return ckda::run(shape, q, k_cache, v_cache, kv_lens, keep_mask, nullptr, 0, 0, scale, causal, out, out_dtype,
+                     lse, ws, ckda::kScratchBytes, num_splits, stream, nullptr, nullptr, nullptr,
+                     ckda::kScratchUnits);
+}
+
 int ck_decode_attn_gather(const ck_decode_shape* shape, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* kv_lens, const int32_t* idx, int32_t W,
                           int64_t idx_head_stride, float scale, int causal, void* out, int out_dtype,
@@ -1603,6 +1651,7 @@ const char* ck_status_string(int status) {
         case CK_ERR_ALIGN: return "misaligned pointer";
         case CK_ERR_WORKSPACE: return "workspace missing or too small";
         case CK_ERR_HIP: return "HIP runtime error";
+        case CK_ERR_SCRATCH: return "shape needs more than the no-alloc scratch holds";
         default: return "unknown status";
     }
 }

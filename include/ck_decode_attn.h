@@ -92,7 +92,9 @@ enum {
     CK_ERR_UNSUPPORTED = -2,  /* D not 128/256, n_q > 6, cache too large     */
     CK_ERR_ALIGN = -3,        /* pointer misaligned (see each argument)      */
     CK_ERR_WORKSPACE = -4,    /* workspace missing or too small              */
-    CK_ERR_HIP = -5           /* the HIP runtime rejected the query/launch   */
+    CK_ERR_HIP = -5,          /* the HIP runtime rejected the query/launch   */
+    CK_ERR_SCRATCH = -6       /* ck_decode_attn_noalloc: the shape needs more
+                                 than its fixed scratch holds                 */
 };
 
 #define CK_MAX_NQ 6
@@ -151,6 +153,24 @@ int ck_decode_attn(const ck_decode_shape* shape, const void* q, const void* k_ca
                    const void* v_cache, const int32_t* kv_lens, float scale, int causal,
                    const uint8_t* keep_mask, void* out, int out_dtype, float* lse,
                    void* workspace, size_t workspace_bytes, int num_splits, void* stream);
+
+/* For callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): ck_decode_attn without a
+ * workspace argument.  The split merge uses a 32 MiB array the library holds
+ * in each device's memory until the process ends: a 256-byte status header,
+ * the counters of up to 1024 units at fixed places, then up to about 30 MiB
+ * of partial results.  A shape whose plan needs more (more than 1024 units,
+ * or more partials) returns CK_ERR_SCRATCH and launches nothing.  Every call
+ * leaves the counters ready for the next call of any shape, so no memset is
+ * ever needed; the array is shared by every call on the device, so calls
+ * that may overlap on one device (different streams) race and must not be
+ * issued.  The call allocates nothing and frees nothing; its first call on a
+ * device looks the array's address up once.  Arguments, result and errors
+ * as ck_decode_attn. */
+int ck_decode_attn_noalloc(const ck_decode_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* kv_lens, float scale, int causal,
+                           const uint8_t* keep_mask, void* out, int out_dtype, float* lse,
+                           int num_splits, void* stream);
 
 /* Gathered decode: each query attends a list of W selected cells read in
  * place from the cache, instead of masking the whole window (llama.cpp PR
