@@ -786,7 +786,6 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
                     tmbits[rt][mb] = (kDeferMask && p.mask_dw) ? mask_bits(mraw[rt][mb]) : mraw[rt][mb];
                 }
         }
-
         // -- stage K and V rows in LDS, then send the next tile's loads -----
         float* scw = sc_lds + (Q8 ? wave * 3 * TT : 0);
         if constexpr (Q8) {
@@ -815,6 +814,39 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
 #pragma unroll
             for (int n = 0; n < VI; ++n)
                 *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vraw[n];
+            // keep_mask: bit t of vkeep is set when some query row of the
+            // workgroup keeps token t of the tile.  V rows that no row keeps
+            // are overwritten with zeros, so whatever those cells hold (NaN
+            // and Inf included) meets only zero weights as zero values.  The
+            // 16 lanes of a q4 group hold the same 4 tokens of a 16-token
+            // block for different rows: one ballot per (block, token) covers
+            // them all.  (Worked out after the staging stores, when the raw
+            // K/V registers are free.  Not with two row tiles at head_dim
+            // 256, whose registers are full: the ballots' scalar registers
+            // made it spill.)
+            if constexpr (MODE == 1 && !(D == 256 && RT == 2)) {
+                uint64_t vkeep = 0;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t any = 0;
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) any |= (tmbits[rt][mb] >> e) & 1u;
+                        const uint64_t bl = __ballot(any != 0u);
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            if ((bl >> (16 * g4)) & 0xFFFFull) vkeep |= 1ull << (16 * mb + 4 * g4 + e);
+                    }
+                if (~vkeep & (TT == 64 ? ~0ull : (1ull << TT) - 1)) {  // some staged row is kept by no query
+#pragma unroll
+                    for (int n = 0; n < VI; ++n) {
+                        const int row = n * RPI + lane / CPR;
+                        if (!((vkeep >> row) & 1ull))
+                            *reinterpret_cast<u32x4*>(vlds + row * RS + (lane % CPR) * 16) = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
         }
         wave_lds_sync();
         // The next tile's loads go out now, or after QK^T where the registers
@@ -1461,6 +1493,18 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.units = pl.units;
     kp.splits = pl.splits;
     kp.S_target = pl.split_target;
+    // Plain bf16 decode with one row group per head, when the units alone
+    // leave most of the chip idle: three quarters of the planned splits are
+    // active (the grid keeps the rest, which leave at once).  Fewer, longer
+    // splits publish fewer partials, and the merge reads them back sooner.
+    // Measured on the MI355X (us per layer, head_dim 256, 4 KV heads, cold):
+    // kv_len 8000 14.3-14.5 -> 13.75, n_q = 3 at 4000 13.9 -> 12.7, kv_len
+    // 1000 / 3000 / 24000 and n_q = 4 within noise.  Shared 16-row groups
+    // (n_q 5-6) were slower with it (13.8 -> 14.5), the INT8 and masked
+    // paths are left as planned.
+    if (!q8 && W == 0 && !keep_mask && num_splits == 0 && pl.row_groups == 1 &&
+        (int64_t)pl.units * pl.split_target * 2 > cus)
+        kp.S_target = max(1, pl.split_target * 3 / 4);
     kp.c_min = pl.chunk_min;
     kp.c_max = pl.chunk_max;
     kp.gran = pl.granule;
@@ -1551,8 +1595,11 @@ int ck_decode_attn(const ck_decode_shape* shape, const void* q, const void* k_ca
 int ck_decode_attn_noalloc(const ck_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* kv_lens, float scale, int causal, const uint8_t* keep_mask, void* out,
                            int out_dtype, float* lse, int num_splits, void* stream) {
+    ck_decode_plan pl;
+    int st = ckda::plan_impl(shape, 0, num_splits, 1, &pl);  // shape checks before any HIP call
+    if (st != CK_OK) return st;
     void* ws = nullptr;
-    const int st = ckda::scratch_ptr(&ws);
+    st = ckda::scratch_ptr(&ws);
     if (st != CK_OK) return st;
     return ckda::run(shape, q, k_cache, v_cache, kv_lens, keep_mask, nullptr, 0, 0, scale, causal, out, out_dtype,
                      lse, ws, ckda::kScratchBytes, num_splits, stream, nullptr, nullptr, nullptr,

@@ -23,8 +23,15 @@
  *                            list order (a cell listed twice counts twice)
  *   out[b,i,h,:] = sum_j softmax_j(scale * q.K[b,j,g,:]) * V[b,j,g,:]
  *   lse[b,i,h]   = ln sum_j exp(scale * q.K[b,j,g,:])
- * A query with no visible cell gets out = 0 and lse = -inf.  Cells that are
- * not visible are never read, so they may hold any bits (NaN/Inf included).
+ * A query with no visible cell gets out = 0 and lse = -inf.
+ * Cell contents: cells at or past L are never read and may hold any bits
+ * (NaN/Inf included).  Cells below L (the filled prefix, the causal window's
+ * drafts included) are read in whole tiles, where a cell hidden from one
+ * query row still meets that row's zero weight, so they must hold finite
+ * values.  The exception is a cell that keep_mask excludes for every query
+ * row of its KV head: it is staged as zeros and may hold any bits (except
+ * at head_dim 256 when a workgroup holds 17-32 packed rows, see
+ * ck_decode_plan.rows_per_group, where it must be finite as well).
  *
  * Layouts (all contiguous, row-major, bf16 = IEEE binary16 brain float):
  *   q        [B, n_q, Hq, D]   bf16

@@ -218,3 +218,46 @@ def test_sparse_dispatch_routes_and_matches_oracle(D, Hkv, n_q, W, n_kv, want, m
     torch.cuda.synchronize()
     assert calls == ["gather"]
     assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what="sparse without mask")
+
+
+@pytest.mark.parametrize("D,n_q,causal,offset", [(128, 1, False, 0), (128, 1, False, 4), (256, 1, False, 0),
+                                                 (128, 3, True, 0), (256, 3, False, 4)])
+def test_unkept_cells_may_hold_any_bits(D, n_q, causal, offset):
+    """Cells below the length that keep_mask excludes for every query of the
+    KV head are staged as zeros, so they may hold any bits: with NaN, +-Inf
+    and huge values in K and V there, the result equals the oracle's (which
+    never reads them) and is bit-identical to the same launch with those
+    cells zeroed.  Tiles are skipped (rows 16-byte aligned) or all scanned
+    (offset 4)."""
+    B, Hq, Hkv, cap = 2, 16, 4, 4096
+    lens = [3000, 1777]
+    p = ck.plan(ck.Shape(B, n_q, Hq, Hkv, D, cap))
+    assert p["rows_per_group"] == 16
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 4100 + D + n_q)
+    q = synth.queries(B, n_q, Hq, D, 4101)
+    rng = np.random.default_rng(4102 + D + n_q)
+    # runs of kept cells (some tiles empty, some partly kept), per query
+    mask = np.zeros((B, n_q, Hkv, cap), np.uint8)
+    for b in range(B):
+        for i in range(n_q):
+            for g in range(Hkv):
+                starts = rng.choice(cap, size=40, replace=False)
+                for s0 in starts:
+                    mask[b, i, g, s0:s0 + int(rng.integers(1, 24))] = 1
+    unkept = ~mask.any(axis=1)                                  # [B, Hkv, cap]
+    bad = np.array([np.nan, np.inf, -np.inf, 3e38], np.float32)
+    kz, vz = k.clone(), v.clone()
+    kg, vg = k.clone(), v.clone()
+    for b in range(B):
+        for g in range(Hkv):
+            cells = np.flatnonzero(unkept[b, g, :lens[b]])
+            kz[b, cells, g] = 0
+            vz[b, cells, g] = 0
+            fill = torch.from_numpy(bad[rng.integers(0, 4, size=(len(cells), D))]).to(torch.bfloat16)
+            kg[b, cells, g] = fill
+            vg[b, cells, g] = fill.flip(0)
+    note(f"unkept cells hold any bits D={D} n_q={n_q} causal={causal} offset={offset}")
+    got = masked_gpu(q, kg, vg, lens, mask, causal=causal, offset=offset)
+    zero = masked_gpu(q, kz, vz, lens, mask, causal=causal, offset=offset)
+    assert np.array_equal(got[0], zero[0]) and np.array_equal(got[1], zero[1])
+    assert_close(got, oracle_ref(q, k, v, lens, causal=causal, keep_mask=mask), what="unkept cells")

@@ -119,7 +119,7 @@ def test_batched_ragged_graph_replay():
     with torch.cuda.graph(graph):
         ck.decode_attn(q, k, v, lens_d, out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
-    sample = [0, 7, 19, 31]
+    kh, vh, qh = k.cpu(), v.cpu(), q.cpu()  # the same bytes for the oracle (4 GiB of K+V)
     for r in range(3):
         lens = synth.ragged_lens(B, 512, cap, 4000 + r)
         lens_d.copy_(torch.from_numpy(lens))
@@ -128,15 +128,12 @@ def test_batched_ragged_graph_replay():
         torch.cuda.synchronize()
         o = out.cpu().numpy()
         ls = lse.cpu().numpy()
-        assert np.all(np.isfinite(o))
         # eager launch on the same lengths gives the same bits as the replay
         eo, el = ck.decode_attn(q, k, v, lens_d, return_lse=True, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(eo.cpu().numpy(), o) and np.array_equal(el.cpu().numpy(), ls)
-        for b in sample:
-            kb, vb = k[b:b + 1].cpu(), v[b:b + 1].cpu()
-            ref = oracle_ref(q[b:b + 1].cpu(), kb, vb, lens[b:b + 1])
-            assert_close((o[b:b + 1], ls[b:b + 1]), ref, what=f"replay {r} b={b} L={lens[b]}")
+        # every sequence of the batch against the oracle
+        assert_close((o, ls), oracle_ref(qh, kh, vh, lens), what=f"replay {r} (all {B} sequences)")
     # the counters are ready for the next launch (the set it will use is zero)
     assert counters_ready(ws, ck.plan(shape)["units"])
 
@@ -152,13 +149,15 @@ def _steps(B, n_q, Hkv, D, seed):
 @pytest.mark.parametrize("L", [0, 1, 37, 2000, 4000])
 def test_d256_step_rows_match_oracle(layer_d256, n_q, L):
     """MTP verification with the drafts passed beside the cache: prefix
-    [0, L) plus step rows 0..i for query i."""
-    note(f"step rows D=256 n_q={n_q} L={L}")
+    [0, L) plus step rows 0..i for query i (bf16 output for the longer
+    prefixes)."""
+    out_dtype = torch.bfloat16 if L >= 2000 else torch.float32
+    note(f"step rows D=256 n_q={n_q} L={L} {out_dtype}")
     k, v, (kd, vd) = layer_d256
     q = synth.queries(1, n_q, 16, 256, 1030 + n_q)
     ks, vs = _steps(1, n_q, 4, 256, 1040 + n_q + L)
-    gpu = steps_gpu(q, k, v, [L], ks, vs, device_inputs=(q.to(DEV), kd, vd))
-    assert_close(gpu, steps_ref(q, k, v, [L], ks, vs), what=f"steps n_q={n_q} L={L}")
+    gpu = steps_gpu(q, k, v, [L], ks, vs, device_inputs=(q.to(DEV), kd, vd), out_dtype=out_dtype)
+    assert_close(gpu, steps_ref(q, k, v, [L], ks, vs), out_dtype, what=f"steps n_q={n_q} L={L}")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -247,11 +246,12 @@ def sparse_case(request):
     return n_kv, q, k, v, idx
 
 
-def test_gather_matches_oracle(sparse_case):
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gather_matches_oracle(sparse_case, out_dtype):
     n_kv, q, k, v, idx = sparse_case
-    note(f"gather n_kv={n_kv}")
-    gpu = gather_gpu(q, k, v, [n_kv], idx)
-    assert_close(gpu, oracle_ref(q, k, v, [n_kv], idx=idx), what=f"gather {n_kv}")
+    note(f"gather n_kv={n_kv} {out_dtype}")
+    gpu = gather_gpu(q, k, v, [n_kv], idx, out_dtype=out_dtype)
+    assert_close(gpu, oracle_ref(q, k, v, [n_kv], idx=idx), out_dtype, what=f"gather {n_kv}")
 
 
 def test_masked_scan_matches_oracle_and_gather(sparse_case):
