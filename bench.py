@@ -307,27 +307,86 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(seconds: float):
-    """The oracle on the host cores: full layer-steps of the headline workload."""
-    import numpy as np
-    import oracle
-    from decode_attention_flash_amd import synth
-    B, n_q, Hq, Hkv, D, cap, L = 1, 1, 16, 4, 256, 24007, 8000
-    k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1002)
-    q = synth.queries(B, n_q, Hq, D, 1002)
-    lens = np.array([L], dtype=np.int32)
-    threads = min(B * n_q * Hq, oracle.default_threads())
-    oracle.attn(q, k, v, lens, 1 / math.sqrt(D), nthreads=threads)  # warm
+def host_info() -> dict:
+    """Host CPU facts for the CPU-baseline record."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count()
+    return {"host_nproc": os.cpu_count(), "host_cpus_allowed": allowed, "cpu_model": model}
+
+
+def _time_calls(fn, seconds: float) -> tuple[float, int]:
+    """Mean seconds per call of fn over at least `seconds` (one call at least)."""
+    fn()  # warm
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.attn(q, k, v, lens, 1 / math.sqrt(D), nthreads=threads)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": el / reps * 1e6, "unit": "us/layer-step", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full layer-steps of the headline workload (B=1, Hq=16, Hkv=4, "
-                      f"D=256, kv_len={L}, cap={cap}), fp64, {threads} threads"}
+            return el / reps, reps
+
+
+def cpu_baseline(seconds: float):
+    """The oracle on the host cores, beside each workload: a full layer-step
+    where it finishes in time, else a stated sample scaled to one layer-step;
+    timed with every allowed host core (capped by OMP_NUM_THREADS) and with
+    one thread.  `seconds` is the time per (workload, thread count)."""
+    import numpy as np
+    import oracle
+    from decode_attention_flash_amd import synth
+    threads = oracle.default_threads()
+    cases = []
+    # tiny decode: B=1, Hq=8, Hkv=2, D=128, cap 1024, kv_len 300
+    k, v = synth.kv_cache(1, 1024, 2, 128, [300], 1001)
+    q = synth.queries(1, 1, 8, 128, 1001)
+    cases.append(("tiny decode B=1 Hq=8 Hkv=2 D=128 kv_len=300", 1.0, "full layer-step",
+                  lambda nt: oracle.attn(q, k, v, np.array([300], np.int32), 1 / math.sqrt(128), nthreads=nt)))
+    # the headline layer: B=1, Hq=16, Hkv=4, D=256, cap 24007, kv_len 8000
+    k2, v2 = synth.kv_cache(1, 24007, 4, 256, [8000], 1002)
+    q2 = synth.queries(1, 1, 16, 256, 1002)
+    cases.append(("D=256 layer B=1 Hq=16 Hkv=4 kv_len=8000 cap=24007", 1.0, "full layer-step",
+                  lambda nt: oracle.attn(q2, k2, v2, np.array([8000], np.int32), 1 / math.sqrt(256), nthreads=nt)))
+    # ragged batch: 4 of the 32 sequences, scaled by the batch's total length
+    lens = synth.ragged_lens(32, 512, 32768, 4000)
+    pick = [0, 8, 16, 24]
+    ls = lens[pick].astype(np.int32)
+    k4, v4 = synth.kv_cache(len(pick), int(ls.max()), 8, 128, ls, 1004, garbage=False)
+    q4 = synth.queries(len(pick), 1, 32, 128, 1004)
+    cases.append(("ragged batch B=32 Hq=32 Hkv=8 D=128 cap=32768", float(lens.sum()) / float(ls.sum()),
+                  f"sequences {pick} (kv_len {ls.tolist()}), scaled by total kv_len {int(lens.sum())}",
+                  lambda nt: oracle.attn(q4, k4, v4, ls, 1 / math.sqrt(128), nthreads=nt)))
+    # sparse decode: 2048 + 64 gathered cells per KV head out of 131072
+    k5, v5 = synth.kv_cache(1, 131072, 2, 128, [131072], 1005)
+    q5 = synth.queries(1, 1, 16, 128, 1005)
+    idx5 = synth.topk_lists(1, 1, 2, 131072, 2048, 64, seed=5000 + 131072)
+    cases.append(("gathered sparse decode B=1 Hq=16 Hkv=2 D=128 n_kv=131072 W=2112", 1.0, "full layer-step",
+                  lambda nt: oracle.attn(q5, k5, v5, np.array([131072], np.int32), 1 / math.sqrt(128),
+                                         idx=idx5, nthreads=nt)))
+    per = max(0.5, seconds / (2 * len(cases)))
+    rows = []
+    for name, scale_to_step, sample, fn in cases:
+        t_multi, r_multi = _time_calls(lambda: fn(threads), per)
+        t_single, r_single = _time_calls(lambda: fn(1), per)
+        rows.append({"workload": name, "sample": sample, "threads": threads,
+                     "us_per_layer_step": round(t_multi * scale_to_step * 1e6, 1),
+                     "us_per_layer_step_1_thread": round(t_single * scale_to_step * 1e6, 1),
+                     "calls": [r_multi, r_single]})
+    head = rows[1]
+    return {"value": head["us_per_layer_step"], "unit": "us/layer-step", "cores": threads, "kind": "oracle",
+            "sample": f"full layer-steps of the headline workload ({head['workload']}), fp64, {threads} threads; "
+                      "the other workloads in 'configs'",
+            "threads": threads, "single_thread_value": head["us_per_layer_step_1_thread"],
+            **host_info(), "configs": rows}
 
 
 def main():
@@ -341,7 +400,8 @@ def main():
                     help="comma-separated sweep groups to run (dense, sparse, topk, q8; window: only the "
                          "n_q=6 causal window at kv_len 4000, for counter profiles); skips the CPU leg")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="oracle timing budget (split over four workloads, multi- and single-threaded)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (reference for counter profiles)")
     args = ap.parse_args()

@@ -143,7 +143,7 @@ def attn(q, k_cache, v_cache, kv_lens, scale: float, causal: bool = False, keep_
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
     st = lib.ck_oracle_attn(B, n_q, Hq, Hkv, D, cap, ptr(qb), ptr(kb), ptr(vb), ptr(lens),
                             ctypes.c_float(scale), 1 if causal else 0, ptr(mask_arr),
-                            ptr(idx_arr), W, hs, num_splits, ptr(out), ptr(lse), nthreads)
+                            ptr(idx_arr), W, hs, num_splits, ptr(out), ptr(lse), _threads(nthreads))
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
     return out, lse
@@ -172,7 +172,7 @@ def attn_steps(q, k_cache, v_cache, kv_lens, k_step, v_step, scale: float, num_s
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     st = lib.ck_oracle_attn_steps(B, n_q, Hq, Hkv, D, cap, ptr(qb), ptr(kb), ptr(vb), ptr(lens),
                                   ptr(ksb), ptr(vsb), ctypes.c_float(scale), num_splits, ptr(out),
-                                  ptr(lse), nthreads)
+                                  ptr(lse), _threads(nthreads))
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
     return out, lse
@@ -257,11 +257,26 @@ def attn_q8(q, kq, vq, ksc, vsc, block_table, kv_lens, scale: float, causal: boo
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     st = lib.ck_oracle_attn_q8(B, n_q, Hq, Hkv, D, page, bt.shape[1], num_pages, ptr(qb), ptr(kq), ptr(vq),
                                ptr(ksc), ptr(vsc), ptr(bt), ptr(lens), ctypes.c_float(scale),
-                               1 if causal else 0, num_splits, ptr(out), ptr(lse), nthreads)
+                               1 if causal else 0, num_splits, ptr(out), ptr(lse), _threads(nthreads))
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
     return out, lse
 
 
 def default_threads() -> int:
-    return load().ck_oracle_nthreads_default()
+    """Worker threads for a call that asks for the default (nthreads <= 0):
+    the host cores this process may run on, capped by OMP_NUM_THREADS when
+    that is set (a shared host's CPU share)."""
+    n = load().ck_oracle_nthreads_default()
+    try:
+        n = min(n, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        pass
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _threads(nthreads: int) -> int:
+    return nthreads if nthreads > 0 else default_threads()
