@@ -86,7 +86,7 @@ def time_graph(launch_layer, n_layers, steps, warmup):
 
 
 def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_layers=None,
-               masks=None):
+               masks=None, stamps=None):
     import torch
     import decode_attention_flash_amd as ck
     from decode_attention_flash_amd import synth
@@ -109,18 +109,71 @@ def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_l
         # query rows (rows below the length), so count those, per layer.
         kv_bytes = int(sum(masked_read_tokens(masks[l], lens, ck.plan(shape)["tile"]) for l in range(n)) * 4 * D / n)
 
+    grid = 0
+    if stamps is not None:  # phase timestamps: one block of workgroups per layer
+        pl = ck.plan(shape)
+        grid = pl["units"] * pl["splits"]
+        assert pl["row_groups"] == 1 and stamps.shape[0] >= n * grid
+
     def launch(l):
+        if stamps is not None:
+            ck.set_phase_stamps(stamps[l * grid:(l + 1) * grid])
         ck.decode_attn(qs[l], stack.k[l], stack.v[l], lens_d, causal=causal, out=outs[l],
                        workspace=ws, keep_mask=None if masks is None else masks[l])
 
-    ms, us = time_graph(launch, n, steps, warmup)
+    try:
+        ms, us = time_graph(launch, n, steps, warmup)
+    finally:
+        if stamps is not None:
+            ck.set_phase_stamps(None)
     algo = kv_bytes + kv_bytes_mask + 2 * B * n_q * Hq * D + 4 * B * n_q * Hq * D + 4 * B
     res = dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, algo_bytes=algo,
                kv_gbs=kv_bytes / us / 1e3, algo_gbs=algo / us / 1e3,
                frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
     if masks is not None:
         res["window_bytes"] = window_bytes
+    if stamps is not None:
+        res["grid"] = grid
     return res
+
+
+PHASES = ["length known", "first tile loaded", "tile loop done", "all waves done", "partial stored",
+          "arrived"]
+
+
+def phase_breakdown(stamps, n, grid):
+    """Per launch, times (us) from the first workgroup's start to each phase:
+    median and last over the active splits, then the median of those over
+    the launches.  The counter runs at 100 MHz."""
+    import numpy as np
+    a = stamps[:n * grid].cpu().numpy().reshape(n, grid, 16)
+    per = []
+    for l in range(n):
+        t = a[l]
+        meta = t[:, 15]
+        s = meta & 0xFFFF
+        n_active = (meta >> 32) & 0xFFFF
+        role = (meta >> 48) & 0xFF
+        rel = (t - t[:, 0].min()).astype(np.float64) / 100.0
+        act = s < n_active
+        row = {"last start": rel[:, 0].max()}
+        for k, name in enumerate(PHASES, start=1):
+            if k >= 5 and not np.any(n_active[act] > 1):
+                continue
+            row[name + " (median)"] = float(np.median(rel[act, k]))
+            row[name + " (last)"] = float(rel[act, k].max())
+        merging = act & ((role == 1) | (role == 2))
+        if np.any(merging):
+            row["merge begins (median)"] = float(np.median(rel[merging, 7]))
+            row["merge ends (last)"] = float(rel[merging, 8].max())
+            row["merging workgroups"] = int(np.sum(merging))
+            row["slices per last arrival"] = float(np.mean(t[act & (role == 1), 13]))
+        else:
+            row["output stored (last)"] = float(rel[act, 5].max())
+        row["active workgroups"] = int(np.sum(act))
+        per.append(row)
+    keys = per[0].keys()
+    return {k: float(np.median([r[k] for r in per if k in r])) for k in keys}
 
 
 def masked_read_tokens(mask, lens, tile):
@@ -397,8 +450,14 @@ def main():
     ap.add_argument("--kv-len", type=int, default=8000)
     ap.add_argument("--headline-only", action="store_true", help="skip the sweeps and the CPU leg")
     ap.add_argument("--only", default="",
-                    help="comma-separated sweep groups to run (dense, sparse, topk, q8; window: only the "
-                         "n_q=6 causal window at kv_len 4000, for counter profiles); skips the CPU leg")
+                    help="comma-separated sweep groups to run (dense, sparse, topk, q8, contraction; "
+                         "window: only the n_q=6 causal window at kv_len 4000, for counter profiles); "
+                         "skips the CPU leg")
+    ap.add_argument("--cases", default="",
+                    help="with the contraction group: comma-separated cases to run (tiny, 1000, 8000, 24000, "
+                         "ragged, gather32768, gather131072; default all)")
+    ap.add_argument("--phases", action="store_true",
+                    help="also record phase timestamps of the head_dim-256 layer at kv_len 1000, 8000, 24000")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="oracle timing budget (split over four workloads, multi- and single-threaded)")
@@ -410,7 +469,7 @@ def main():
         groups = set()
     elif args.only:
         groups = {g.strip() for g in args.only.split(",") if g.strip()}
-        unknown = groups - {"dense", "sparse", "topk", "q8", "window"}
+        unknown = groups - {"dense", "sparse", "topk", "q8", "window", "contraction"}
         if unknown:
             ap.error(f"unknown sweep groups: {sorted(unknown)}")
 
@@ -433,6 +492,8 @@ def main():
     lens_sweep = [1000, 3000, 8000, 24000]
     n_max = max(layers_for(4 * Hkv * D * L) for L in lens_sweep + [L0]) if "dense" in groups else 4
     n_max = max(n_max, layers_for(4 * Hkv * D * L0))
+    if args.phases:
+        n_max = max(n_max, layers_for(4 * Hkv * D * 1000))
     log(f"allocating {n_max} layer caches of capacity {cap}")
     stack = Stack(n_max, 1, cap, Hkv, D, 1002)
 
@@ -442,6 +503,21 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+
+    phases = None
+    if args.phases:
+        phases = []
+        for L in (1000, 8000, 24000):
+            n = min(layers_for(4 * Hkv * D * L), len(stack.k))
+            pl = ck.plan(ck.Shape(1, 1, Hq, Hkv, D, cap))
+            stamps = torch.zeros((n * pl["units"] * pl["splits"], 16), dtype=torch.int64, device="cuda")
+            r = dense_case(stack, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup, n_layers=n, stamps=stamps)
+            b = phase_breakdown(stamps, r["layers"], r["grid"])
+            log(f"phases kv_len {L} ({r['us']:.2f} us/layer with stamps on): " +
+                ", ".join(f"{k} {v:.0f}" if k.endswith("workgroups") else f"{k} {v:.2f}"
+                          for k, v in b.items()))
+            phases.append(dict(kv_len=L, us_stamped=r["us"], **b))
+            del stamps
 
     sweep = {}
     if "window" in groups:
@@ -552,6 +628,57 @@ def main():
         del qst
         torch.cuda.empty_cache()
 
+    if "contraction" in groups:
+        # The workloads of at most 8 packed rows through both contractions,
+        # each case timed MFMA then VALU on the same caches.
+        from decode_attention_flash_amd import synth
+        sweep["contraction"] = []
+        all_cases = ["tiny", "1000", "8000", "24000", "ragged", "gather32768", "gather131072"]
+        cases = [c.strip() for c in args.cases.split(",") if c.strip()] or all_cases
+        if set(cases) - set(all_cases):
+            ap.error(f"unknown contraction cases: {sorted(set(cases) - set(all_cases))}")
+
+        def both(name, run):
+            res = {}
+            for kind in ("mfma", "valu"):
+                ck.set_contraction(kind)
+                try:
+                    res[kind] = run()
+                finally:
+                    ck.set_contraction("mfma")
+            log(f"contraction {name}: mfma {res['mfma']['us']:.2f} us, valu {res['valu']['us']:.2f} us")
+            sweep["contraction"].append(dict(case=name, **res))
+
+        if "tiny" in cases:
+            st = Stack(layers_for(4 * 2 * 128 * 300), 1, 1024, 2, 128, 1001)
+            both("tiny B=1 Hq=8 Hkv=2 D=128 cap=1024 kv_len=300",
+                 lambda: dense_case(st, 1, 1, 8, 2, 128, [300], args.steps, args.warmup))
+            del st
+        d256 = [L for L in (1000, 8000, 24000) if str(L) in cases]
+        if d256:
+            st = Stack(max(layers_for(4 * Hkv * D * L) for L in d256), 1, cap, Hkv, D, 1002)
+            for L in d256:
+                both(f"B=1 Hq={Hq} Hkv={Hkv} D={D} cap={cap} kv_len={L}",
+                     lambda: dense_case(st, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup))
+            del st
+            torch.cuda.empty_cache()
+        if "ragged" in cases:
+            lens = synth.ragged_lens(32, 512, 32768, 4000)
+            st = Stack(4, 32, 32768, 8, 128, 1004)
+            both("ragged B=32 Hq=32 Hkv=8 D=128 cap=32768",
+                 lambda: dense_case(st, 32, 1, 32, 8, 128, lens.tolist(), max(3, args.steps // 4), 2,
+                                    n_layers=4))
+            del st
+            torch.cuda.empty_cache()
+        for n_kv in (32768, 131072):
+            if f"gather{n_kv}" not in cases:
+                continue
+            st = Stack(layers_for(2 * 2112 * 4 * 128), 1, n_kv, 2, 128, 1005)
+            both(f"gather B=1 Hq=16 Hkv=2 D=128 n_kv={n_kv} W=2048+64",
+                 lambda: gather_case(st, n_kv, 2048, 64, args.steps, args.warmup)[0])
+            del st
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu and not args.headline_only and not args.only:
         log("cpu baseline (oracle)")
@@ -580,10 +707,11 @@ def main():
         "frac_of_peak_kv": round(head["frac_kv"], 4),
         "roofline": {"bound": "hbm", "achieved": round(head["algo_gbs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(head["algo_gbs"] / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel<256,1,0,false>",
+                     "traffic": traffic, "kernel": "decode_kernel<256,1,0,false,0>",
                      "algo_bytes_per_launch": head["algo_bytes"]},
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "phases": phases,
     }
     print(json.dumps(line))
 

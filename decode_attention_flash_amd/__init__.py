@@ -28,9 +28,11 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misalig
 EXPORTS = ("ck_decode_attn", "ck_decode_attn_noalloc", "ck_decode_attn_gather", "ck_decode_attn_steps", "ck_decode_attn_q8",
            "ck_kv_append_q8", "ck_decode_attn_workspace_size",
            "ck_decode_attn_plan", "ck_decode_sparse_path", "ck_decode_topk", "ck_decode_topk_plan",
-           "ck_decode_topk_workspace_size", "ck_workspace_status", "ck_set_spin_limit", "ck_status_string")
+           "ck_decode_topk_workspace_size", "ck_workspace_status", "ck_set_spin_limit", "ck_set_contraction",
+           "ck_set_phase_stamps", "ck_status_string")
 CK_WS_ERR_MERGE = 1
 CK_WS_ERR_TOPK = 2
+CONTRACTIONS = {"mfma": 0, "valu": 1}
 
 
 class CkError(RuntimeError):
@@ -110,6 +112,10 @@ def lib():
         L.ck_workspace_status.restype = ctypes.c_int
         L.ck_set_spin_limit.argtypes = [i32]
         L.ck_set_spin_limit.restype = ctypes.c_int
+        L.ck_set_contraction.argtypes = [i32]
+        L.ck_set_contraction.restype = ctypes.c_int
+        L.ck_set_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        L.ck_set_phase_stamps.restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
         L.ck_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -197,6 +203,31 @@ def set_spin_limit(polls: int) -> None:
     st = lib().ck_set_spin_limit(int(polls))
     if st != 0:
         raise CkError(st, "ck_set_spin_limit")
+
+
+def set_contraction(kind: str) -> None:
+    """Contraction for plans of up to 8 packed rows (``ck_set_contraction``):
+    "mfma" (the default) or "valu".  Process-wide."""
+    if kind not in CONTRACTIONS:
+        raise ValueError(f"contraction must be one of {sorted(CONTRACTIONS)}")
+    st = lib().ck_set_contraction(CONTRACTIONS[kind])
+    if st != 0:
+        raise CkError(st, "ck_set_contraction")
+
+
+def set_phase_stamps(stamps) -> None:
+    """Phase timestamps of the attention kernels (``ck_set_phase_stamps``):
+    a device int64 tensor of workgroups x 16 words, or None to stop."""
+    if stamps is None:
+        st = lib().ck_set_phase_stamps(None, 0)
+    else:
+        if stamps.dtype != torch.int64 or stamps.dim() != 2 or stamps.shape[1] != 16 or not stamps.is_cuda:
+            raise ValueError("stamps must be a device int64 tensor of shape [workgroups, 16]")
+        if not stamps.is_contiguous():
+            raise ValueError("stamps must be contiguous")
+        st = lib().ck_set_phase_stamps(ctypes.c_void_p(stamps.data_ptr()), stamps.shape[0])
+    if st != 0:
+        raise CkError(st, "ck_set_phase_stamps")
 
 
 def cached_workspaces() -> list:

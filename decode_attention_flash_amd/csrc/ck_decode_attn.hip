@@ -38,6 +38,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "ck_decode_attn.h"
 
@@ -113,6 +114,8 @@ struct KParams {
     int32_t* ws_cnt;     // per unit kCntStride ints: counters and slice claim flags
     int32_t* ws_status;  // sticky error bits (CK_WS_*), set with an atomic OR
     int32_t spin_limit;  // polls a merge helper makes before it gives up
+    uint64_t* stamps;    // phase timestamps, kStampWords per workgroup, or null
+    int32_t stamp_wgs;   // workgroups the stamp buffer holds
     // paged INT8 cache (MODE 3)
     const int8_t* kq;
     const int8_t* vq;
@@ -191,6 +194,12 @@ __device__ __forceinline__ f32x4 mfma_k16(lds_bf16x4 a, lds_bf16x4 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two bf16 products summed into an fp32 accumulator (v_dot2c_f32_bf16).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 // Transposed LDS read (gfx950): within each 16-lane group, lane j receives
 // element j%4 of the 64-bit words read by lanes 4e+j/4, e = 0..3.
 __device__ __forceinline__ lds_bf16x4 lds_read_tr(const unsigned char* p) {
@@ -204,6 +213,25 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Phase timestamps (diagnostic instances of the kernel only, ST = true):
+// thread 0 of workgroup w writes the 100 MHz real-time counter to word k of
+// its kStampWords.  Words: 0 start, 1 length known, 2 first tile loaded
+// (wave 0), 3 tile loop done (wave 0), 4 all waves done, 5 partial (or
+// output) stores complete, 6 arrival rank known, 7 merge begins, 8 merge
+// ends; 13 the slices this workgroup merged, 14 the arrival rank, 15 split
+// | unit << 16 | n_active << 32 | role << 48 (1 last arrival, 2 helper that
+// merged, 3 other).  Words of phases a workgroup never reaches stay as they
+// were.  (A run-time switch in every kernel cost 0.5-2 us per launch: each
+// test reloads the pointer from the kernel arguments and waits for it.)
+constexpr int kStampWords = 16;
+template <bool ST, typename P>
+__device__ __forceinline__ void stamp(const P& p, int k, uint64_t v = 0, bool raw = false) {
+    if constexpr (ST) {
+        if (threadIdx.x == 0 && (int)blockIdx.x < p.stamp_wgs)
+            p.stamps[(size_t)blockIdx.x * kStampWords + k] = raw ? v : __builtin_amdgcn_s_memrealtime();
+    }
 }
 
 __device__ __forceinline__ int atomic_ld(const int32_t* p) {
@@ -415,9 +443,18 @@ __device__ void fill_slice_nan(const KParams& p, int nrows, int c, int ns, int b
 
 // MODE 0: dense, 1: dense with keep_mask, 2: gather, 3: dense over the paged
 // INT8 cache.
-template <int D, int RT, int MODE, bool CO>
+// RV = 0: QK^T and PV on MFMA.  RV = 4 or 8: the alternative VALU contraction
+// for up to RV packed rows (dense and gather, one row tile), kept to measure
+// the choice: lane l takes row l / (64 / RV) and a slice of D / (64 / RV)
+// head dims; QK^T sums bf16 pairs with v_dot2 over the slice and then over
+// the row's lanes, the softmax runs in the lane, and PV takes token pairs
+// (V rows paired by byte permutes) with v_dot2 into fp32 accumulators,
+// which are handed to the merge in the MFMA layout.
+template <int D, int RT, int MODE, bool CO, int RV = 0, bool ST = false>
 __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(const KParams p) {
     static_assert(!CO || RT == 1, "row groups share tiles only with one row tile");
+    static_assert(RV == 0 || ((RV == 4 || RV == 8) && RT == 1 && !CO && (MODE == 0 || MODE == 2)),
+                  "the VALU contraction serves up to 8 rows of dense or gathered decode");
     using Gm = Geo<D, tile_bytes(RT)>;
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS, RSK = Gm::RSK;
@@ -471,6 +508,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     }
     const int row0 = rg * p.rows_alloc;
     const int nrows = min(p.rows_alloc, p.R - row0);
+    stamp<ST>(p, 0);
 
     // ---- prologue: the length and the query rows, loaded together ----------
     // The query rows are the B operand of every QK^T MFMA.  They are the same
@@ -510,6 +548,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     const int span = GATHER ? p.W : L;
     const int C = chunk_len(span, p);
     const int n_active = span > 0 ? (span + C - 1) / C : 1;
+    stamp<ST>(p, 1);
+    stamp<ST>(p, 15, (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | (3ull << 48), true);
     if (s >= n_active) return;
     // The unit's counter set for this launch.  Every active split has read
     // the parity before it arrives, and only the last arrival changes it.
@@ -553,7 +593,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // Step rows (verification drafts that are not in the cache): the unit's
     // last split streams them as one extra tile, whose row t is visible to
     // query i when t <= i.
-    const bool steps = MODE == 0 && p.k_step != nullptr;
+    const bool steps = MODE == 0 && RV == 0 && p.k_step != nullptr;
     const size_t step_off = ((size_t)b * p.n_q * p.Hkv + g) * D;
     const uint32_t step_bytes = (uint32_t)(p.n_q - 1) * p.row_bytes + 2u * D;
     const __amdgpu_buffer_rsrc_t rks = make_rsrc(steps ? p.k_step + step_off : p.k, steps ? step_bytes : 0u);
@@ -773,6 +813,38 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
+    // VALU contraction: lane (vr, dp) holds query row vr's head dims
+    // [dp * DS, dp * DS + DS) as bf16 pairs, its fp32 accumulators for those
+    // dims, and the row's running max and (per lane, summed at the end) sum.
+    constexpr int NDP = RV > 0 ? 64 / RV : 1, DS = D / NDP, TPL = TT / NDP;
+    static_assert(RV == 0 || (TPL >= 1 && DS % 8 == 0), "VALU lane slices");
+    const int vr = lane / NDP, dp = lane % NDP;
+    uint32_t qv[RV > 0 ? DS / 2 : 1];
+    float vacc[RV > 0 ? DS : 1];
+    float m_v = -INFINITY, l_v = 0.f;
+    int lim_v = 0;
+    if constexpr (RV > 0) {
+#pragma unroll
+        for (int c = 0; c < DS / 8; ++c) {
+            const int d0 = dp * DS + 8 * c;
+            const u32x4 w = __builtin_bit_cast(u32x4, q_lds[(d0 / 32) * 64 + ((d0 / 8) % 4) * 16 + vr]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qv[4 * c + e] = w[e];
+        }
+#pragma unroll
+        for (int d = 0; d < DS; ++d) vacc[d] = 0.f;
+        int lim = L;
+        if (p.causal) {
+            lim = L - p.n_q + (GATHER ? iq : (row0 + vr) / p.G) + 1;
+            lim = lim < 0 ? 0 : (lim > L ? L : lim);
+        }
+        lim_v = vr < nrows ? lim : 0;
+    }
+
+    if (ST && first < ntiles) {
+        wait_stores();  // the first tile's loads are in
+        stamp<ST>(p, 2);
+    }
     for (int tile = first, next; tile < ntiles; tile = next) {
         const int tb = pos_begin + tile * TT;
         const bool st_tile = steps && tile == ntiles_c;
@@ -863,6 +935,114 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             issue(next, jv_next);
             if constexpr (GATHER) jv_next = list_entry(next + kWaves);
             if constexpr (Q8) jv_next = page_of(next + kWaves);
+        }
+
+        if constexpr (RV > 0) {
+            // -- VALU: scores over the lane's head-dim slice ---------------
+            float sv[TT];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const unsigned char* kr = klds + t * RSK + dp * DS * 2;
+                float a = 0.f;
+#pragma unroll
+                for (int c = 0; c < DS / 8; ++c) {
+                    const u32x4 k4 = *reinterpret_cast<const u32x4*>(kr + 16 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a = dot2(k4[e], qv[4 * c + e], a);
+                }
+                sv[t] = a;
+            }
+            // Sum over the row's NDP lanes, scattering the tokens: at each
+            // step a lane keeps half of its tokens and adds its partner's
+            // copy of that half (the partner differs in the step's lane bit,
+            // and keeps the other half).  Lane dp ends with the full scores
+            // of tokens dp * TPL .. dp * TPL + TPL - 1.
+            auto rs_step = [&](auto ctrl, int bit, int half) {
+                const bool up = (dp >> bit) & 1;
+#pragma unroll
+                for (int i = 0; i < TT / 2; ++i) {
+                    if (i < half) {
+                        const float send = up ? sv[i] : sv[half + i];
+                        const float keep = up ? sv[half + i] : sv[i];
+                        sv[i] = keep + dpp<decltype(ctrl)::value>(send);
+                    }
+                }
+            };
+            using Mir = std::integral_constant<int, kDppMirror>;
+            using HMir = std::integral_constant<int, kDppHalfMirror>;
+            using X2 = std::integral_constant<int, kDppXor2>;
+            using X1 = std::integral_constant<int, kDppXor1>;
+            if constexpr (NDP == 16) rs_step(Mir{}, 3, TT / 2);
+            rs_step(HMir{}, 2, TT / (NDP / 4));
+            rs_step(X2{}, 1, TT / (NDP / 2));
+            rs_step(X1{}, 0, TT / NDP);
+            if (tid == 0 && tile == first && n_active > 1) started_seen = atomic_ld(cnt + kStarted);
+
+            // -- online softmax of the lane's TPL tokens ----------------------
+            const int tok0 = dp * TPL;
+            const int lim_off = GATHER ? 0 : min(lim_v, pos_end) - tb;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int off = tok0 + i;
+                const bool ok = GATHER ? (vr < nrows && ((tvalid >> off) & 1ull)) : off < lim_off;
+                const float x = ok ? sv[i] * p.scale_log2 : -INFINITY;
+                sv[i] = x;
+                mx = fmaxf(mx, x);
+            }
+            mx = group_reduce<true>(mx, NDP);
+            const float m_new = fmaxf(m_v, mx);
+            const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_v - mu);
+            float lsum = 0.f;
+            uint16_t ph[TPL];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const __bf16 h = (__bf16)fast_exp2(sv[i] - mu);
+                ph[i] = __builtin_bit_cast(uint16_t, h);
+                lsum += (float)h;
+            }
+            l_v = l_v * alpha + lsum;
+            m_v = m_new;
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int d = 0; d < DS; ++d) vacc[d] *= alpha;
+            }
+            // The row's TT probabilities go through LDS (over the consumed K
+            // tile) so that every lane of the row has them all.
+            uint16_t* prow = reinterpret_cast<uint16_t*>(klds) + vr * TT;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) prow[tok0 + i] = ph[i];
+            wave_lds_sync();
+            uint32_t pp[TT / 2];
+#pragma unroll
+            for (int c = 0; c < TT / 8; ++c) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(prow + 8 * c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pp[4 * c + e] = w[e];
+            }
+
+            // -- O += P V, two tokens per v_dot2 --------------------------
+            // The bf16 pair (V[t][d], V[t+1][d]) is put together from the two
+            // rows' dwords with a byte permute.
+#pragma unroll
+            for (int j = 0; j < TT / 2; ++j) {
+                const unsigned char* v0 = vlds + (2 * j) * RS + dp * DS * 2;
+#pragma unroll
+                for (int c = 0; c < DS / 8; ++c) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(v0 + 16 * c);
+                    const u32x4 b2 = *reinterpret_cast<const u32x4*>(v0 + RS + 16 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = __builtin_amdgcn_perm(b2[e], a[e], 0x05040100u);
+                        const uint32_t hi = __builtin_amdgcn_perm(b2[e], a[e], 0x07060302u);
+                        vacc[8 * c + 2 * e] = dot2(lo, pp[j], vacc[8 * c + 2 * e]);
+                        vacc[8 * c + 2 * e + 1] = dot2(hi, pp[j], vacc[8 * c + 2 * e + 1]);
+                    }
+                }
+            }
+            wave_lds_sync();
+            continue;
         }
 
         // -- S^T = K Q^T ---------------------------------------------------
@@ -999,12 +1179,15 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
         wave_lds_sync();
     }
 
-    // Row sums were kept per lane (each lane saw 4 of every 16 tokens).
+    stamp<ST>(p, 3);
+    // Row sums were kept per lane (each lane saw 4 of every 16 tokens, or
+    // with the VALU contraction TPL of every TT).
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         st.l[rt] += __shfl_xor(st.l[rt], 16);
         st.l[rt] += __shfl_xor(st.l[rt], 32);
     }
+    if constexpr (RV > 0) l_v = group_reduce<false>(l_v, NDP);
 
     // ---- merge the four waves' states and publish ---------------------------
     // Every wave dumps its (m, l, acc) to LDS in its MFMA register layout; then
@@ -1019,19 +1202,37 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
     const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
+    if constexpr (RV == 0) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        s_ml[wave][rt][lane][0] = st.m[rt];
-        s_ml[wave][rt][lane][1] = st.l[rt];
+        for (int rt = 0; rt < RT; ++rt) {
+            s_ml[wave][rt][lane][0] = st.m[rt];
+            s_ml[wave][rt][lane][1] = st.l[rt];
+        }
+    } else if (dp == 0) {
+        s_ml[wave][0][vr][0] = m_v;
+        s_ml[wave][0][vr][1] = l_v;
     }
 #pragma unroll
     for (int rt0 = 0; rt0 < RT; rt0 += RT_ROUND) {
         __syncthreads();  // the staging area (or the previous round) is free
+        if (rt0 == 0) stamp<ST>(p, 4);
+        if constexpr (RV == 0) {
 #pragma unroll
-        for (int rl = 0; rl < RT_ROUND; ++rl)
+            for (int rl = 0; rl < RT_ROUND; ++rl)
 #pragma unroll
-            for (int n = 0; n < NB; ++n)
-                dump[((wave * RT_ROUND + rl) * NB + n) * 64 + q4 * 16 + (l16 ^ ((4 * n + q4) & 15))] = st.o[rt0 + rl][n];
+                for (int n = 0; n < NB; ++n)
+                    dump[((wave * RT_ROUND + rl) * NB + n) * 64 + q4 * 16 + (l16 ^ ((4 * n + q4) & 15))] =
+                        st.o[rt0 + rl][n];
+        } else {
+            // the same slots as the MFMA layout: (row, 4 columns) of block n,
+            // column group q
+#pragma unroll
+            for (int j = 0; j < DS / 4; ++j) {
+                const int c0 = dp * DS + 4 * j, n = c0 >> 4, q = (c0 >> 2) & 3;
+                dump[(wave * NB + n) * 64 + q * 16 + (vr ^ ((4 * n + q) & 15))] =
+                    f32x4{vacc[4 * j], vacc[4 * j + 1], vacc[4 * j + 2], vacc[4 * j + 3]};
+            }
+        }
         __syncthreads();
         constexpr int D4 = D / 4;
         const int rows_here = min(nrows - rt0 * 16, RT_ROUND * 16);
@@ -1070,7 +1271,13 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             }
         }
     }
-    if (n_active == 1) return;
+    if (n_active == 1) {
+        if constexpr (ST) {
+            wait_stores();
+            stamp<ST>(p, 5);
+        }
+        return;
+    }
 
     // ---- several splits: announce the arrival -----------------------------
     // Each wave waits for its own partial stores to complete before the
@@ -1079,9 +1286,12 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // with device-coherent loads (no L2 writeback or invalidate is needed).
     wait_stores();
     __syncthreads();
+    stamp<ST>(p, 5);
     if (tid == 0) ms.flag = atomicAdd(cnt + kArrived, 1);  // arrival rank
     __syncthreads();
     const int rank = ms.flag;
+    stamp<ST>(p, 6);
+    stamp<ST>(p, 14, (uint64_t)rank, true);
     if (rank == n_active - 1 && wave == 0) {
         // Last arrival: every active split has read the parity, so the other
         // counter set (this unit's previous launch used it) is cleared for
@@ -1109,6 +1319,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     if (!last && !helper) return;
     __syncthreads();  // everyone has read ms.flag
     if (last) {
+        stamp<ST>(p, 7);
+        stamp<ST>(p, 15, (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | (1ull << 48), true);
         merge_slice<D>(p, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
         // ns <= 64: lane c of wave 0 claims slice c, one ballot collects them.
         // The claims wait until slice 0 is merged: claimed at arrival they
@@ -1123,6 +1335,11 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
         __syncthreads();
         for (uint64_t mask = ms.owned; mask != 0; mask &= mask - 1)
             merge_slice<D>(p, unit, n_active, nrows, __builtin_ctzll(mask), ns, b, g, iq, GATHER, row0);
+        if constexpr (ST) {
+            wait_stores();
+            stamp<ST>(p, 8);
+            stamp<ST>(p, 13, 1 + (uint64_t)__builtin_popcountll(ms.owned), true);
+        }
     } else {
         const int c = n_active - 1 - rank;
         if (tid == 0) {
@@ -1146,7 +1363,16 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             ms.flag = ok;
         }
         __syncthreads();
-        if (ms.flag == 1) merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+        if (ms.flag == 1) {
+            stamp<ST>(p, 7);
+            stamp<ST>(p, 15, (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | (2ull << 48), true);
+            merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+            if constexpr (ST) {
+                wait_stores();
+                stamp<ST>(p, 8);
+                stamp<ST>(p, 13, 1, true);
+            }
+        }
         if (ms.flag == 2) fill_slice_nan<D>(p, nrows, c, ns, b, g, iq, GATHER, row0);
     }
 }
@@ -1350,12 +1576,29 @@ static int device_cus(int* cus) {
 
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-template <int D, int RT, int MODE, bool CO>
+template <int D, int RT, int MODE, bool CO, int RV = 0, bool ST = false>
 static hipError_t launch_one(const KParams& kp, int grid, hipStream_t st) {
     void* args[] = {const_cast<KParams*>(&kp)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE, CO>), dim3(grid),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE, CO, RV, ST>), dim3(grid),
                            dim3(kThreads), args, 0, st);
 }
+
+// The VALU contraction (dense or gathered decode, at most 8 packed rows).
+template <int MODE>
+static hipError_t launch_valu(int D, int rows, const KParams& kp, int grid, hipStream_t st) {
+    if (D == 128)
+        return rows <= 4 ? launch_one<128, 1, MODE, false, 4>(kp, grid, st)
+                         : launch_one<128, 1, MODE, false, 8>(kp, grid, st);
+    return rows <= 4 ? launch_one<256, 1, MODE, false, 4>(kp, grid, st)
+                     : launch_one<256, 1, MODE, false, 8>(kp, grid, st);
+}
+
+// Process-wide phase-timestamp buffer (diagnostics; null: off).
+static std::atomic<uint64_t*> g_stamps{nullptr};
+static std::atomic<int64_t> g_stamp_wgs{0};
+
+// Process-wide contraction choice for up to 8 packed rows (0: MFMA).
+static std::atomic<int> g_contraction{CK_CONTRACT_MFMA};
 
 template <int D, int MODE>
 static hipError_t launch_d(int RT, bool co, const KParams& kp, int grid, hipStream_t st) {
@@ -1510,6 +1753,9 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     kp.gran = pl.granule;
     kp.slices = pl.slices;
     kp.spin_limit = spin_limit();
+    kp.stamps = g_stamps.load(std::memory_order_relaxed);
+    const int64_t stamp_wgs = g_stamp_wgs.load(std::memory_order_relaxed);
+    kp.stamp_wgs = kp.stamps ? (int32_t)(stamp_wgs < INT32_MAX ? stamp_wgs : INT32_MAX) : 0;
     kp.W = W;
     kp.idx_head_stride = idx_head_stride;
     kp.scale_log2 = (float)((double)scale * 1.4426950408889634074);
@@ -1525,8 +1771,18 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     const bool co = RT == 1 && pl.row_groups > 1;
     const int grid = co ? (pl.units / pl.row_groups * pl.splits + 7) / 8 * 8 * pl.row_groups : pl.units * pl.splits;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool valu = g_contraction.load(std::memory_order_relaxed) == CK_CONTRACT_VALU && !q8 && !keep_mask &&
+                      !k_step && RT == 1 && !co && pl.rows <= 8;
+    // phase timestamps: the plain dense kernel with one row tile and one row
+    // group has a stamping instance
+    const bool stamped = kp.stamps != nullptr && !valu && !q8 && W == 0 && !keep_mask && RT == 1 && !co;
     hipError_t e;
-    if (q8)
+    if (stamped)
+        e = s->D == 128 ? launch_one<128, 1, 0, false, 0, true>(kp, grid, hs)
+                        : launch_one<256, 1, 0, false, 0, true>(kp, grid, hs);
+    else if (valu)
+        e = W > 0 ? launch_valu<2>(s->D, pl.rows, kp, grid, hs) : launch_valu<0>(s->D, pl.rows, kp, grid, hs);
+    else if (q8)
         e = launch_mode<3>(s->D, RT, co, kp, grid, hs);
     else if (W > 0)
         e = launch_mode<2>(s->D, RT, co, kp, grid, hs);
@@ -1687,6 +1943,20 @@ int ck_workspace_status(const void* workspace, void* stream, int32_t* status) {
 int ck_set_spin_limit(int32_t polls) {
     if (polls < 0) return CK_ERR_ARG;
     ckda::g_spin_limit.store(polls == 0 ? ckda::kDefaultSpinLimit : polls, std::memory_order_relaxed);
+    return CK_OK;
+}
+
+int ck_set_phase_stamps(void* stamps, int64_t workgroups) {
+    if (workgroups < 0 || (stamps == nullptr) != (workgroups == 0)) return CK_ERR_ARG;
+    if (stamps && !ckda::aligned(stamps, 8)) return CK_ERR_ALIGN;
+    ckda::g_stamp_wgs.store(workgroups, std::memory_order_relaxed);
+    ckda::g_stamps.store(static_cast<uint64_t*>(stamps), std::memory_order_relaxed);
+    return CK_OK;
+}
+
+int ck_set_contraction(int32_t contraction) {
+    if (contraction != CK_CONTRACT_MFMA && contraction != CK_CONTRACT_VALU) return CK_ERR_ARG;
+    ckda::g_contraction.store(contraction, std::memory_order_relaxed);
     return CK_OK;
 }
 

@@ -372,6 +372,44 @@ int ck_workspace_status(const void* workspace, void* stream, int32_t* status);
  * workspace status reports the give-up.  polls >= 0. */
 int ck_set_spin_limit(int32_t polls);
 
+/* Contraction used by the dense and gathered entries for plans of at most
+ * 8 packed query rows (n_q * G rows dense, G rows gathered), process-wide
+ * and read at each launch: CK_CONTRACT_MFMA (the default) runs QK^T and PV
+ * as bf16 MFMA tiles (16 rows, 15 of which may be padding); CK_CONTRACT_VALU
+ * runs them on the vector ALUs with v_dot2 over bf16 pairs, one row per
+ * 64 / 4 or 64 / 8 lanes, the probabilities rounded to bf16 in the same way.
+ * Both read the same bytes and give the same results up to the order of
+ * fp32 sums.  The VALU form exists to measure the choice (GQA packing makes
+ * the KV tile the shared operand of every row, the question is whether the
+ * padded MFMA or the unpadded VALU contraction keeps up with HBM); keep_mask,
+ * step rows, the INT8 cache and more than 8 rows always take MFMA.
+ * Returns CK_ERR_ARG for any other value. */
+#define CK_CONTRACT_MFMA 0
+#define CK_CONTRACT_VALU 1
+int ck_set_contraction(int32_t contraction);
+
+/* Phase timestamps of plain dense decode, for diagnosing where a launch
+ * spends its time (process-wide, read at each launch).  While a buffer is
+ * set, ck_decode_attn and ck_decode_attn_steps launches whose plan has one
+ * 16-row group per KV head (at most 16 packed rows, no keep_mask) run a
+ * stamping instance of their kernel, a little slower than the plain one;
+ * other launches are unaffected and write nothing.  stamps: device buffer of
+ * workgroups * 16 uint64 words, 8-byte aligned, owned by the caller, or NULL
+ * (with workgroups = 0) to turn stamping off.  Thread 0 of workgroup w
+ * (w < workgroups) writes the device's 100 MHz real-time counter to word
+ * 16 w + k at phase k: 0 start, 1 sequence length known, 2 first KV tile in
+ * registers (first wave), 3 tile loop done (first wave), 4 all waves done,
+ * 5 its partial result (or, with one split, the output) stored and
+ * complete, 6 arrival counted, 7 split merge begins, 8 merge ends.  Word 13
+ * holds the number of column slices it merged, word 14 the arrival rank,
+ * word 15 split | unit << 16 | active splits << 32 | role << 48 (1 last
+ * arrival, 2 helper that merged a slice, 3 neither).  A launch writes only
+ * the words of phases its workgroups reach; the grid is units * splits of
+ * ck_decode_attn_plan.  CK_ERR_ARG when exactly one of stamps and
+ * workgroups is zero or workgroups < 0, CK_ERR_ALIGN for a misaligned
+ * buffer. */
+int ck_set_phase_stamps(void* stamps, int64_t workgroups);
+
 /* Static text for a status code. */
 const char* ck_status_string(int status);
 

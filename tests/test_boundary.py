@@ -35,6 +35,26 @@ def test_status_strings():
         assert L.ck_status_string(code).decode() == text
 
 
+def test_contraction_choice():
+    """Only the two documented contractions are accepted; the default is
+    restored afterwards."""
+    with pytest.raises(ValueError):
+        ck.set_contraction("sparse")
+    L = ck.lib()
+    assert L.ck_set_contraction(2) == -1 and L.ck_set_contraction(-1) == -1
+    ck.set_contraction("valu")
+    ck.set_contraction("mfma")
+
+
+def test_phase_stamps_arguments():
+    L = ck.lib()
+    assert L.ck_set_phase_stamps(None, 5) == -1
+    assert L.ck_set_phase_stamps(ctypes.c_void_p(4096), 0) == -1
+    assert L.ck_set_phase_stamps(ctypes.c_void_p(4096), -1) == -1
+    assert L.ck_set_phase_stamps(ctypes.c_void_p(4100), 3) == -3  # CK_ERR_ALIGN, nothing is written
+    assert L.ck_set_phase_stamps(None, 0) == 0
+
+
 def shape(B=1, n_q=1, Hq=16, Hkv=4, D=256, cap=24007):
     return ck.Shape(B, n_q, Hq, Hkv, D, cap)
 

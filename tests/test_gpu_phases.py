@@ -1,0 +1,52 @@
+"""GPU: phase timestamps (ck_set_phase_stamps) leave the results bit for bit
+as they are, the recorded phases are in order in every workgroup, and the
+merge roles account for every column slice once."""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_flash_amd as ck
+from decode_attention_flash_amd import synth
+from gpu_common import DEV, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("L", [0, 40, 3000, 24000])
+def test_stamps_change_nothing_and_are_ordered(L):
+    B, Hq, Hkv, D, cap = 1, 16, 4, 256, 24007
+    k, v = synth.kv_cache(B, cap, Hkv, D, [min(L, cap)], 1101, device=DEV)
+    q = synth.queries(B, 1, Hq, D, 1101, device=DEV)
+    lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    note(f"phase stamps L={L}")
+    ref, ref_lse = ck.decode_attn(q, k, v, lens, return_lse=True)
+    pl = ck.plan(ck.shape_of(q, k))
+    grid = pl["units"] * pl["splits"]
+    stamps = torch.zeros((grid, 16), dtype=torch.int64, device=DEV)
+    ck.set_phase_stamps(stamps)
+    try:
+        out, lse = ck.decode_attn(q, k, v, lens, return_lse=True)
+    finally:
+        ck.set_phase_stamps(None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+    t = stamps.cpu().numpy()
+    assert np.all(t[:, 0] > 0) and np.all(t[:, 1] >= t[:, 0])  # every workgroup started
+    meta = t[:, 15]
+    s, n_active, role = meta & 0xFFFF, (meta >> 32) & 0xFFFF, (meta >> 48) & 0xFF
+    assert np.all(n_active == n_active[0]) and n_active[0] >= 1
+    act = s < n_active
+    assert np.sum(act) == n_active[0] * pl["units"]
+    a = t[act]
+    for k_ in (2, 3, 4, 5):
+        ok = a[:, k_] > 0  # a split with no tile (L = 0) stages none
+        assert np.all(a[ok, k_] >= a[ok, 1])
+    assert np.all(np.diff(a[:, 3:6], axis=1) >= 0)
+    if n_active[0] > 1:
+        assert np.all(a[:, 6] >= a[:, 5])
+        assert sorted(a[a[:, 14] == n_active[0] - 1, 15] >> 48 & 0xFF) == [1] * pl["units"]
+        m = a[((a[:, 15] >> 48) & 0xFF) <= 2]
+        assert np.all(m[:, 7] >= m[:, 6]) and np.all(m[:, 8] >= m[:, 7])
+        # every column slice of every unit merged exactly once
+        assert int(np.sum(m[:, 13])) == pl["units"] * min(pl["slices"], int(n_active[0]))
