@@ -168,6 +168,13 @@ def phase_breakdown(stamps, n, grid):
             row["merge ends (last)"] = float(rel[merging, 8].max())
             row["merging workgroups"] = int(np.sum(merging))
             row["slices per last arrival"] = float(np.mean(t[act & (role == 1), 13]))
+            last, helper = act & (role == 1), act & (role == 2)
+            row["last arrival's merge and claims"] = float(np.mean(rel[last, 8] - rel[last, 7]))
+            if np.any(helper):
+                row["helper start after last arrival"] = float(np.mean(rel[helper, 7]) - rel[last, 6].max())
+                row["helper merge"] = float(np.mean(rel[helper, 8] - rel[helper, 7]))
+                row["helpers end (last)"] = float(rel[helper, 8].max())
+            row["last arrivals end (last)"] = float(rel[last, 8].max())
         else:
             row["output stored (last)"] = float(rel[act, 5].max())
         row["active workgroups"] = int(np.sum(act))
@@ -707,7 +714,7 @@ def main():
         "frac_of_peak_kv": round(head["frac_kv"], 4),
         "roofline": {"bound": "hbm", "achieved": round(head["algo_gbs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(head["algo_gbs"] / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel<256,1,0,false,0>",
+                     "traffic": traffic, "kernel": "decode_kernel<256,1,0,false,0,false>",
                      "algo_bytes_per_launch": head["algo_bytes"]},
         "cpu_baseline": cpu,
         "sweep": sweep,

@@ -62,6 +62,8 @@ constexpr int kCntStride = 512, kParity = 0, kSet0 = 128, kSetStride = 128;
 constexpr int kStarted = 0, kArrived = 32, kSliceFlag = 64;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
+constexpr int kPlanSlices = 16;  // the plan's limit (see plan_impl)
+static_assert(kPlanSlices <= kMaxSlices, "slices per unit");
 
 // Bytes of K per wave tile.  With one row tile (up to 16 packed rows) the
 // kernel needs under 256 VGPRs, so with 8 KiB tiles (32 tokens at D = 128,
@@ -880,44 +882,41 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
                 scw[2 * TT + lane] = vsv > 0.f ? 1.f / vsv : 0.f;
             }
         } else {
+            // keep_mask: bit t of vkeep is set when some query row of the
+            // workgroup keeps token t of the tile.  V rows that no row keeps
+            // are staged as zeros, so whatever those cells hold (NaN and Inf
+            // included) meets only zero weights as zero values.  The 16 lanes
+            // of a q4 group hold the same 4 tokens of a 16-token block for
+            // different rows: their bits are OR-ed with DPP moves inside the
+            // group, and lane 16 g4 of each group gives its 4 bits.  (Not
+            // with two row tiles at head_dim 256, whose registers are full.)
+            uint64_t vkeep = ~0ull;
+            if constexpr (MODE == 1 && !(D == 256 && RT == 2)) {
+                vkeep = 0;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    uint32_t a4 = 0;
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) a4 |= tmbits[rt][mb];
+                    a4 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a4, kDppXor1, 0xF, 0xF, false);
+                    a4 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a4, kDppXor2, 0xF, 0xF, false);
+                    a4 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a4, kDppHalfMirror, 0xF, 0xF, false);
+                    a4 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a4, kDppMirror, 0xF, 0xF, false);
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        vkeep |= (uint64_t)((uint32_t)__builtin_amdgcn_readlane((int)a4, 16 * g4) & 0xFu)
+                                 << (16 * mb + 4 * g4);
+                }
+            }
 #pragma unroll
             for (int n = 0; n < VI; ++n)
                 *reinterpret_cast<u32x4*>(klds + (n * RPI + lane / CPR) * RSK + (lane % CPR) * 16) = kraw[n];
 #pragma unroll
-            for (int n = 0; n < VI; ++n)
-                *reinterpret_cast<u32x4*>(vlds + (n * RPI + lane / CPR) * RS + (lane % CPR) * 16) = vraw[n];
-            // keep_mask: bit t of vkeep is set when some query row of the
-            // workgroup keeps token t of the tile.  V rows that no row keeps
-            // are overwritten with zeros, so whatever those cells hold (NaN
-            // and Inf included) meets only zero weights as zero values.  The
-            // 16 lanes of a q4 group hold the same 4 tokens of a 16-token
-            // block for different rows: one ballot per (block, token) covers
-            // them all.  (Worked out after the staging stores, when the raw
-            // K/V registers are free.  Not with two row tiles at head_dim
-            // 256, whose registers are full: the ballots' scalar registers
-            // made it spill.)
-            if constexpr (MODE == 1 && !(D == 256 && RT == 2)) {
-                uint64_t vkeep = 0;
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint32_t any = 0;
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt) any |= (tmbits[rt][mb] >> e) & 1u;
-                        const uint64_t bl = __ballot(any != 0u);
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4)
-                            if ((bl >> (16 * g4)) & 0xFFFFull) vkeep |= 1ull << (16 * mb + 4 * g4 + e);
-                    }
-                if (~vkeep & (TT == 64 ? ~0ull : (1ull << TT) - 1)) {  // some staged row is kept by no query
-#pragma unroll
-                    for (int n = 0; n < VI; ++n) {
-                        const int row = n * RPI + lane / CPR;
-                        if (!((vkeep >> row) & 1ull))
-                            *reinterpret_cast<u32x4*>(vlds + row * RS + (lane % CPR) * 16) = u32x4{0u, 0u, 0u, 0u};
-                    }
-                }
+            for (int n = 0; n < VI; ++n) {
+                const int row = n * RPI + lane / CPR;
+                const bool keep = MODE != 1 || ((vkeep >> row) & 1ull);
+                *reinterpret_cast<u32x4*>(vlds + row * RS + (lane % CPR) * 16) =
+                    keep ? vraw[n] : u32x4{0u, 0u, 0u, 0u};
             }
         }
         wave_lds_sync();
@@ -1538,10 +1537,17 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     pl->row_groups = (int32_t)RG;
     pl->rows_per_group = rows_per_group;
     // Column slices of the merge: about 32 KiB of partials each, at most one
-    // per 4 columns.
+    // per 4 columns and at most kPlanSlices.  Every slice but the first is
+    // merged by a helper that polls the unit's arrival count; at 32 slices
+    // (12-24 packed rows) up to 31 helpers per unit polled one word, and a
+    // launch whose splits arrived spread out (measured with a prologue that
+    // sent the first tile earlier) took 22 us instead of 10.7 at n_q = 3,
+    // kv_len 2000.  16 measured the same or faster on every MTP window
+    // (n_q = 4 at 2000: 11.7 -> 11.5 us); 8 was slower (n_q = 3 at 4000:
+    // 12.6 -> 14.9 us).
     const int64_t merge_bytes = splits * rows_eff * s->D * 4;
     int64_t slices = 1;
-    while (slices * 32768 < merge_bytes && slices < s->D / 4 && slices < kMaxSlices) slices *= 2;
+    while (slices * 32768 < merge_bytes && slices < s->D / 4 && slices < kPlanSlices) slices *= 2;
     pl->slices = (int32_t)slices;
     pl->tile = tile_bytes(rows_per_group / 16) / (2 * s->D);
     if (splits == 1) {

@@ -35,6 +35,16 @@ def test_status_strings():
         assert L.ck_status_string(code).decode() == text
 
 
+def test_plan_merge_slices():
+    """About 32 KiB of partials per merge slice, at most 16 slices (each
+    beyond the first is a helper polling the unit's arrival count)."""
+    assert ck.plan(shape(), num_cus=256)["slices"] == 8             # 4 rows x 64 splits x 256 cols
+    assert ck.plan(shape(n_q=3), num_cus=256)["slices"] == 16       # 12 rows: 24 by size, capped
+    assert ck.plan(shape(n_q=6), num_cus=256)["slices"] == 16       # two 16-row groups
+    assert ck.plan(shape(Hq=8, Hkv=2, D=128, cap=1024), num_cus=256)["slices"] <= 16
+    assert ck.plan(shape(), num_splits=1, num_cus=256)["slices"] == 1
+
+
 def test_contraction_choice():
     """Only the two documented contractions are accepted; the default is
     restored afterwards."""
