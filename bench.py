@@ -53,9 +53,14 @@ class Stack:
                                       dtype=torch.bfloat16))
 
 
+# per-replay times (ms) of the last time_graph call
+LAST_REPLAYS_MS = []
+
+
 def time_graph(launch_layer, n_layers, steps, warmup):
     """Capture n_layers launches in one graph; time `steps` replays.
-    Returns (ms per replay, us per layer)."""
+    Returns (ms per replay, us per layer); the per-replay times are left in
+    LAST_REPLAYS_MS."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -73,16 +78,24 @@ def time_graph(launch_layer, n_layers, steps, warmup):
         graph.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         graph.replay()
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    LAST_REPLAYS_MS[:] = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     del graph
     return ms, ms * 1000.0 / n_layers
+
+
+def replay_spread(n_layers):
+    """p10 / median / p90 of the last time_graph call, in us per layer."""
+    import numpy as np
+    us = np.array(LAST_REPLAYS_MS) * 1000.0 / n_layers
+    return {"us_p10": round(float(np.percentile(us, 10)), 3), "us_median": round(float(np.median(us)), 3),
+            "us_p90": round(float(np.percentile(us, 90)), 3)}
 
 
 def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_layers=None,
@@ -129,7 +142,7 @@ def dense_case(stack, B, n_q, Hq, Hkv, D, lens, steps, warmup, causal=False, n_l
     algo = kv_bytes + kv_bytes_mask + 2 * B * n_q * Hq * D + 4 * B * n_q * Hq * D + 4 * B
     res = dict(us=us, ms_per_replay=ms, layers=n, kv_bytes=kv_bytes, algo_bytes=algo,
                kv_gbs=kv_bytes / us / 1e3, algo_gbs=algo / us / 1e3,
-               frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS)
+               frac_kv=kv_bytes / us / 1e3 / PEAK_HBM_GBS, **replay_spread(n))
     if masks is not None:
         res["window_bytes"] = window_bytes
     if stamps is not None:
@@ -538,6 +551,21 @@ def main():
             r = dense_case(stack, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup)
             log(f"kv_len {L}: {r['us']:.2f} us, {r['kv_gbs']:.0f} GB/s")
             sweep["kv_len"].append(dict(kv_len=L, cap=cap, **r))
+        # cost against length: least-squares line us = intercept + bytes / rate
+        import numpy as np
+        xb = np.array([e["kv_bytes"] for e in sweep["kv_len"]], dtype=np.float64)
+        yu = np.array([e["us"] for e in sweep["kv_len"]], dtype=np.float64)
+        slope, icpt = np.polyfit(xb, yu, 1)
+        sweep["kv_len_fit"] = {"intercept_us": round(float(icpt), 2),
+                               "marginal_gbs": round(float(1e-3 / slope), 1)}
+        log(f"kv_len fit: intercept {icpt:.2f} us, marginal {1e-3 / slope:.0f} GB/s")
+        # warm: the kv_len-8000 layer with every launch on one cache (it
+        # stays in the 256 MB Infinity Cache); labelled, never the headline
+        warm = Stack.__new__(Stack)
+        warm.k, warm.v = [stack.k[0]] * 33, [stack.v[0]] * 33
+        r = dense_case(warm, 1, 1, Hq, Hkv, D, [8000], args.steps, args.warmup, n_layers=33)
+        log(f"warm (one cache) kv_len 8000: {r['us']:.2f} us")
+        sweep["warm_kv_len_8000"] = dict(kv_len=8000, cap=cap, note="one cache replayed (warm)", **r)
         sweep["causal_window"] = []
         for L in (2000, 4000):
             for n_q in (3, 4, 5, 6):
@@ -710,6 +738,7 @@ def main():
         "config": {"workload": workload,
                    "B": 1, "n_q": 1, "Hq": Hq, "Hkv": Hkv, "D": D, "cap": cap, "kv_len": L0,
                    "layers_per_step": head["layers"], "parallelism": "none"},
+        "spread_us": {k: head[k] for k in ("us_p10", "us_median", "us_p90")},
         "hbm_gbs_kv": round(head["kv_gbs"], 1),
         "frac_of_peak_kv": round(head["frac_kv"], 4),
         "roofline": {"bound": "hbm", "achieved": round(head["algo_gbs"], 1), "peak": PEAK_HBM_GBS,
