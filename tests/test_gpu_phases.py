@@ -13,13 +13,13 @@ from gpu_common import DEV, note
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("L", [0, 40, 3000, 24000])
-def test_stamps_change_nothing_and_are_ordered(L):
-    B, Hq, Hkv, D, cap = 1, 16, 4, 256, 24007
+@pytest.mark.parametrize("D,L", [(256, 0), (256, 40), (256, 3000), (256, 24000), (128, 300), (128, 5000)])
+def test_stamps_change_nothing_and_are_ordered(D, L):
+    B, Hq, Hkv, cap = 1, 16 if D == 256 else 8, 4 if D == 256 else 2, 24007
     k, v = synth.kv_cache(B, cap, Hkv, D, [min(L, cap)], 1101, device=DEV)
     q = synth.queries(B, 1, Hq, D, 1101, device=DEV)
     lens = torch.tensor([L], dtype=torch.int32, device=DEV)
-    note(f"phase stamps L={L}")
+    note(f"phase stamps D={D} L={L}")
     ref, ref_lse = ck.decode_attn(q, k, v, lens, return_lse=True)
     pl = ck.plan(ck.shape_of(q, k))
     grid = pl["units"] * pl["splits"]
