@@ -664,8 +664,9 @@ def main():
         torch.cuda.empty_cache()
 
     if "contraction" in groups:
-        # The workloads of at most 8 packed rows through both contractions,
-        # each case timed MFMA then VALU on the same caches.
+        # The workloads of at most 8 packed rows through the three
+        # contractions, each case timed MFMA, VALU dot2, VALU fp32 on the
+        # same caches.
         from decode_attention_flash_amd import synth
         sweep["contraction"] = []
         all_cases = ["tiny", "1000", "8000", "24000", "ragged", "gather32768", "gather131072"]
@@ -675,13 +676,13 @@ def main():
 
         def both(name, run):
             res = {}
-            for kind in ("mfma", "valu"):
+            for kind in ("mfma", "valu", "valu_f32"):
                 ck.set_contraction(kind)
                 try:
                     res[kind] = run()
                 finally:
                     ck.set_contraction("mfma")
-            log(f"contraction {name}: mfma {res['mfma']['us']:.2f} us, valu {res['valu']['us']:.2f} us")
+            log(f"contraction {name}: " + ", ".join(f"{k} {v['us']:.2f} us" for k, v in res.items()))
             sweep["contraction"].append(dict(case=name, **res))
 
         if "tiny" in cases:

@@ -32,7 +32,7 @@ EXPORTS = ("ck_decode_attn", "ck_decode_attn_noalloc", "ck_decode_attn_gather", 
            "ck_set_phase_stamps", "ck_status_string")
 CK_WS_ERR_MERGE = 1
 CK_WS_ERR_TOPK = 2
-CONTRACTIONS = {"mfma": 0, "valu": 1}
+CONTRACTIONS = {"mfma": 0, "valu": 1, "valu_f32": 2}
 
 
 class CkError(RuntimeError):
@@ -207,7 +207,8 @@ def set_spin_limit(polls: int) -> None:
 
 def set_contraction(kind: str) -> None:
     """Contraction for plans of up to 8 packed rows (``ck_set_contraction``):
-    "mfma" (the default) or "valu".  Process-wide."""
+    "mfma" (the default), "valu" (v_dot2 on bf16 pairs) or "valu_f32".
+    Process-wide."""
     if kind not in CONTRACTIONS:
         raise ValueError(f"contraction must be one of {sorted(CONTRACTIONS)}")
     st = lib().ck_set_contraction(CONTRACTIONS[kind])

@@ -196,6 +196,10 @@ __device__ __forceinline__ f32x4 mfma_k16(lds_bf16x4 a, lds_bf16x4 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The low and high bf16 of a dword, widened to fp32 (exact).
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
 // Two bf16 products summed into an fp32 accumulator (v_dot2c_f32_bf16).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -451,12 +455,15 @@ __device__ void fill_slice_nan(const KParams& p, int nrows, int c, int ns, int b
 // head dims; QK^T sums bf16 pairs with v_dot2 over the slice and then over
 // the row's lanes, the softmax runs in the lane, and PV takes token pairs
 // (V rows paired by byte permutes) with v_dot2 into fp32 accumulators,
-// which are handed to the merge in the MFMA layout.
-template <int D, int RT, int MODE, bool CO, int RV = 0, bool ST = false>
+// which are handed to the merge in the MFMA layout.  VF: the same in plain
+// fp32 (every K and V element widened, one FMA per element and token, the
+// probabilities kept in fp32 instead of rounded to bf16).
+template <int D, int RT, int MODE, bool CO, int RV = 0, bool ST = false, bool VF = false>
 __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(const KParams p) {
     static_assert(!CO || RT == 1, "row groups share tiles only with one row tile");
     static_assert(RV == 0 || ((RV == 4 || RV == 8) && RT == 1 && !CO && (MODE == 0 || MODE == 2)),
                   "the VALU contraction serves up to 8 rows of dense or gathered decode");
+    static_assert(!VF || RV > 0, "the fp32 form is a VALU form");
     using Gm = Geo<D, tile_bytes(RT)>;
     constexpr int TT = Gm::TT, MB = Gm::MB, KS = Gm::KS, KB = Gm::KB, NB = Gm::NB;
     constexpr int CPR = Gm::CPR, RPI = Gm::RPI, VI = Gm::VI, RS = Gm::RS, RSK = Gm::RSK;
@@ -821,7 +828,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     constexpr int NDP = RV > 0 ? 64 / RV : 1, DS = D / NDP, TPL = TT / NDP;
     static_assert(RV == 0 || (TPL >= 1 && DS % 8 == 0), "VALU lane slices");
     const int vr = lane / NDP, dp = lane % NDP;
-    uint32_t qv[RV > 0 ? DS / 2 : 1];
+    uint32_t qv[RV > 0 && !VF ? DS / 2 : 1];
+    float qf[VF ? DS : 1];
     float vacc[RV > 0 ? DS : 1];
     float m_v = -INFINITY, l_v = 0.f;
     int lim_v = 0;
@@ -831,7 +839,14 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             const int d0 = dp * DS + 8 * c;
             const u32x4 w = __builtin_bit_cast(u32x4, q_lds[(d0 / 32) * 64 + ((d0 / 8) % 4) * 16 + vr]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qv[4 * c + e] = w[e];
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (VF) {
+                    qf[8 * c + 2 * e] = bf_lo(w[e]);
+                    qf[8 * c + 2 * e + 1] = bf_hi(w[e]);
+                } else {
+                    qv[4 * c + e] = w[e];
+                }
+            }
         }
 #pragma unroll
         for (int d = 0; d < DS; ++d) vacc[d] = 0.f;
@@ -947,7 +962,14 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
                 for (int c = 0; c < DS / 8; ++c) {
                     const u32x4 k4 = *reinterpret_cast<const u32x4*>(kr + 16 * c);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a = dot2(k4[e], qv[4 * c + e], a);
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (VF) {
+                            a = fmaf(qf[8 * c + 2 * e], bf_lo(k4[e]), a);
+                            a = fmaf(qf[8 * c + 2 * e + 1], bf_hi(k4[e]), a);
+                        } else {
+                            a = dot2(k4[e], qv[4 * c + e], a);
+                        }
+                    }
                 }
                 sv[t] = a;
             }
@@ -995,11 +1017,17 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             const float alpha = fast_exp2(m_v - mu);
             float lsum = 0.f;
             uint16_t ph[TPL];
+            float pf[TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const __bf16 h = (__bf16)fast_exp2(sv[i] - mu);
-                ph[i] = __builtin_bit_cast(uint16_t, h);
-                lsum += (float)h;
+                if constexpr (VF) {
+                    pf[i] = fast_exp2(sv[i] - mu);
+                    lsum += pf[i];
+                } else {
+                    const __bf16 h = (__bf16)fast_exp2(sv[i] - mu);
+                    ph[i] = __builtin_bit_cast(uint16_t, h);
+                    lsum += (float)h;
+                }
             }
             l_v = l_v * alpha + lsum;
             m_v = m_new;
@@ -1009,6 +1037,35 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             }
             // The row's TT probabilities go through LDS (over the consumed K
             // tile) so that every lane of the row has them all.
+            if constexpr (VF) {
+                float* prowf = reinterpret_cast<float*>(klds) + vr * TT;
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) prowf[tok0 + i] = pf[i];
+                wave_lds_sync();
+                float pt[TT];
+#pragma unroll
+                for (int c = 0; c < TT / 4; ++c) {
+                    const f32x4 w = *reinterpret_cast<const f32x4*>(prowf + 4 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pt[4 * c + e] = w[e];
+                }
+                // -- O += P V, one FMA per element and token ---------------
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    const unsigned char* v0 = vlds + t * RS + dp * DS * 2;
+#pragma unroll
+                    for (int c = 0; c < DS / 8; ++c) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(v0 + 16 * c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            vacc[8 * c + 2 * e] = fmaf(pt[t], bf_lo(a[e]), vacc[8 * c + 2 * e]);
+                            vacc[8 * c + 2 * e + 1] = fmaf(pt[t], bf_hi(a[e]), vacc[8 * c + 2 * e + 1]);
+                        }
+                    }
+                }
+                wave_lds_sync();
+                continue;
+            }
             uint16_t* prow = reinterpret_cast<uint16_t*>(klds) + vr * TT;
 #pragma unroll
             for (int i = 0; i < TPL; ++i) prow[tok0 + i] = ph[i];
@@ -1582,21 +1639,22 @@ static int device_cus(int* cus) {
 
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-template <int D, int RT, int MODE, bool CO, int RV = 0, bool ST = false>
+template <int D, int RT, int MODE, bool CO, int RV = 0, bool ST = false, bool VF = false>
 static hipError_t launch_one(const KParams& kp, int grid, hipStream_t st) {
     void* args[] = {const_cast<KParams*>(&kp)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE, CO, RV, ST>), dim3(grid),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, RT, MODE, CO, RV, ST, VF>), dim3(grid),
                            dim3(kThreads), args, 0, st);
 }
 
-// The VALU contraction (dense or gathered decode, at most 8 packed rows).
-template <int MODE>
+// The VALU contraction (dense or gathered decode, at most 8 packed rows),
+// on bf16 pairs or in fp32.
+template <int MODE, bool VF>
 static hipError_t launch_valu(int D, int rows, const KParams& kp, int grid, hipStream_t st) {
     if (D == 128)
-        return rows <= 4 ? launch_one<128, 1, MODE, false, 4>(kp, grid, st)
-                         : launch_one<128, 1, MODE, false, 8>(kp, grid, st);
-    return rows <= 4 ? launch_one<256, 1, MODE, false, 4>(kp, grid, st)
-                     : launch_one<256, 1, MODE, false, 8>(kp, grid, st);
+        return rows <= 4 ? launch_one<128, 1, MODE, false, 4, false, VF>(kp, grid, st)
+                         : launch_one<128, 1, MODE, false, 8, false, VF>(kp, grid, st);
+    return rows <= 4 ? launch_one<256, 1, MODE, false, 4, false, VF>(kp, grid, st)
+                     : launch_one<256, 1, MODE, false, 8, false, VF>(kp, grid, st);
 }
 
 // Process-wide phase-timestamp buffer (diagnostics; null: off).
@@ -1777,8 +1835,10 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     const bool co = RT == 1 && pl.row_groups > 1;
     const int grid = co ? (pl.units / pl.row_groups * pl.splits + 7) / 8 * 8 * pl.row_groups : pl.units * pl.splits;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool valu = g_contraction.load(std::memory_order_relaxed) == CK_CONTRACT_VALU && !q8 && !keep_mask &&
-                      !k_step && RT == 1 && !co && pl.rows <= 8;
+    const int contraction = g_contraction.load(std::memory_order_relaxed);
+    const bool valu = contraction != CK_CONTRACT_MFMA && !q8 && !keep_mask && !k_step && RT == 1 && !co &&
+                      pl.rows <= 8;
+    const bool vf = contraction == CK_CONTRACT_VALU_F32;
     // phase timestamps: the plain dense kernel with one row tile and one row
     // group has a stamping instance
     const bool stamped = kp.stamps != nullptr && !valu && !q8 && W == 0 && !keep_mask && RT == 1 && !co;
@@ -1786,8 +1846,12 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     if (stamped)
         e = s->D == 128 ? launch_one<128, 1, 0, false, 0, true>(kp, grid, hs)
                         : launch_one<256, 1, 0, false, 0, true>(kp, grid, hs);
+    else if (valu && vf)
+        e = W > 0 ? launch_valu<2, true>(s->D, pl.rows, kp, grid, hs)
+                  : launch_valu<0, true>(s->D, pl.rows, kp, grid, hs);
     else if (valu)
-        e = W > 0 ? launch_valu<2>(s->D, pl.rows, kp, grid, hs) : launch_valu<0>(s->D, pl.rows, kp, grid, hs);
+        e = W > 0 ? launch_valu<2, false>(s->D, pl.rows, kp, grid, hs)
+                  : launch_valu<0, false>(s->D, pl.rows, kp, grid, hs);
     else if (q8)
         e = launch_mode<3>(s->D, RT, co, kp, grid, hs);
     else if (W > 0)
@@ -1961,7 +2025,8 @@ int ck_set_phase_stamps(void* stamps, int64_t workgroups) {
 }
 
 int ck_set_contraction(int32_t contraction) {
-    if (contraction != CK_CONTRACT_MFMA && contraction != CK_CONTRACT_VALU) return CK_ERR_ARG;
+    if (contraction != CK_CONTRACT_MFMA && contraction != CK_CONTRACT_VALU && contraction != CK_CONTRACT_VALU_F32)
+        return CK_ERR_ARG;
     ckda::g_contraction.store(contraction, std::memory_order_relaxed);
     return CK_OK;
 }

@@ -374,18 +374,24 @@ int ck_set_spin_limit(int32_t polls);
 
 /* Contraction used by the dense and gathered entries for plans of at most
  * 8 packed query rows (n_q * G rows dense, G rows gathered), process-wide
- * and read at each launch: CK_CONTRACT_MFMA (the default) runs QK^T and PV
- * as bf16 MFMA tiles (16 rows, 15 of which may be padding); CK_CONTRACT_VALU
- * runs them on the vector ALUs with v_dot2 over bf16 pairs, one row per
- * 64 / 4 or 64 / 8 lanes, the probabilities rounded to bf16 in the same way.
- * Both read the same bytes and give the same results up to the order of
- * fp32 sums.  The VALU form exists to measure the choice (GQA packing makes
- * the KV tile the shared operand of every row, the question is whether the
- * padded MFMA or the unpadded VALU contraction keeps up with HBM); keep_mask,
+ * and read at each launch:
+ *   CK_CONTRACT_MFMA (the default): QK^T and PV as bf16 MFMA tiles (16 rows,
+ *     12 or 8 of which are padding at 4 or 8 rows), the probabilities rounded
+ *     to bf16 for PV;
+ *   CK_CONTRACT_VALU: both on the vector ALUs with v_dot2 over bf16 pairs,
+ *     one row per 64 / 4 or 64 / 8 lanes, the probabilities rounded the same
+ *     way;
+ *   CK_CONTRACT_VALU_F32: the same lanes in plain fp32 (every K and V element
+ *     widened, one FMA per element and token), the probabilities kept in fp32.
+ * All read the same bytes and agree with the exact result within the stated
+ * tolerances.  The VALU forms exist to measure the choice (GQA packing makes
+ * the KV tile the shared operand of every row; the question is whether the
+ * padded MFMA or an unpadded VALU contraction keeps up with HBM); keep_mask,
  * step rows, the INT8 cache and more than 8 rows always take MFMA.
  * Returns CK_ERR_ARG for any other value. */
 #define CK_CONTRACT_MFMA 0
 #define CK_CONTRACT_VALU 1
+#define CK_CONTRACT_VALU_F32 2
 int ck_set_contraction(int32_t contraction);
 
 /* Phase timestamps of plain dense decode, for diagnosing where a launch

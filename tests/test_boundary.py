@@ -51,9 +51,9 @@ def test_contraction_choice():
     with pytest.raises(ValueError):
         ck.set_contraction("sparse")
     L = ck.lib()
-    assert L.ck_set_contraction(2) == -1 and L.ck_set_contraction(-1) == -1
-    ck.set_contraction("valu")
-    ck.set_contraction("mfma")
+    assert L.ck_set_contraction(3) == -1 and L.ck_set_contraction(-1) == -1
+    for kind in ("valu", "valu_f32", "mfma"):
+        ck.set_contraction(kind)
 
 
 def test_phase_stamps_arguments():

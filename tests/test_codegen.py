@@ -52,9 +52,9 @@ def test_decode_kernels_have_no_waterfall_loops(asm):
         n_rfl = body.count("v_readfirstlane")
         assert n_rfl <= 40, f"{name}: {n_rfl} v_readfirstlane (a per-lane buffer descriptor?)"
     # D 128 and 256, modes 0-3: one row tile alone or in shared groups, two
-    # row tiles; plus the VALU contraction (4 or 8 rows) for modes 0 and 2,
-    # and the phase-stamping instance of plain decode
-    assert found == 34
+    # row tiles; plus the VALU contractions (dot2 and fp32, 4 or 8 rows) for
+    # modes 0 and 2, and the phase-stamping instance of plain decode
+    assert found == 42
 
 
 def test_no_scratch_spills(asm):
@@ -87,6 +87,6 @@ def test_one_row_tile_kernels_fit_twice_per_cu(asm):
         found += 1
         assert lds <= 80 * 1024, f"{name}: {lds} bytes of LDS, two workgroups no longer fit on a CU"
         assert vgpr <= 256, f"{name}: {vgpr} VGPRs, two waves no longer fit on a SIMD"
-    # D 128 and 256, modes 0-3, alone or in shared groups; VALU 4 and 8 rows,
-    # modes 0 and 2; phase stamps
-    assert found == 26
+    # D 128 and 256, modes 0-3, alone or in shared groups; VALU (dot2 and
+    # fp32) 4 and 8 rows, modes 0 and 2; phase stamps
+    assert found == 34

@@ -1,8 +1,8 @@
-"""GPU parity of the VALU contraction (ck_set_contraction(CK_CONTRACT_VALU)):
-dense and gathered decode of up to 8 packed rows with QK^T and PV on v_dot2
-instead of MFMA, against the fp64 oracle to the same tolerances, with the
-same bit-exact index handling, and against the MFMA kernel on the same
-inputs (the two differ only in the order of fp32 sums)."""
+"""GPU parity of the VALU contractions (ck_set_contraction): dense and
+gathered decode of up to 8 packed rows with QK^T and PV on v_dot2 over bf16
+pairs (CK_CONTRACT_VALU) or in plain fp32 (CK_CONTRACT_VALU_F32) instead of
+MFMA, against the fp64 oracle to the same tolerances, with the same
+bit-exact index handling, and against the MFMA kernel on the same inputs."""
 
 import numpy as np
 import pytest
@@ -16,11 +16,11 @@ from gpu_common import (DEV, TOL_F32, assert_close, check_counts, counting_case,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture
-def valu():
-    ck.set_contraction("valu")
+@pytest.fixture(params=["valu", "valu_f32"])
+def valu(request):
+    ck.set_contraction(request.param)
     try:
-        yield
+        yield request.param
     finally:
         ck.set_contraction("mfma")
 
@@ -142,22 +142,24 @@ def test_gather_index_handling_bit_exact(valu):
     check_counts(og, [[[idx[0, 0, g] for g in range(Hkv)]]], Hq // Hkv)
 
 
-def test_agrees_with_mfma(layer_d256):
-    """Same inputs through both contractions: equal within the fp32 tolerance
-    (both round the probabilities to bf16 the same way; only the order of the
-    fp32 sums differs), and not bit-identical, which shows that the second
-    launch took the other kernel."""
+@pytest.mark.parametrize("kind", ["valu", "valu_f32"])
+def test_agrees_with_mfma(layer_d256, kind):
+    """Same inputs through MFMA and a VALU contraction: equal within the fp32
+    tolerance (the dot2 form rounds the probabilities to bf16 as MFMA does and
+    differs only in the order of fp32 sums; the fp32 form keeps them in fp32),
+    and not bit-identical, which shows that the second launch took the other
+    kernel."""
     k, v, (kd, vd) = layer_d256
     q = synth.queries(1, 1, 16, 256, 1077)
-    note("valu vs mfma D=256 L=8000")
+    note(f"{kind} vs mfma D=256 L=8000")
     ck.set_contraction("mfma")
     a, la = dense_gpu(q, k, v, [8000], device_inputs=(q.to(DEV), kd, vd))
-    ck.set_contraction("valu")
+    ck.set_contraction(kind)
     try:
         b, lb = dense_gpu(q, k, v, [8000], device_inputs=(q.to(DEV), kd, vd))
     finally:
         ck.set_contraction("mfma")
     assert float(np.max(np.abs(a - b))) <= TOL_F32
-    assert float(np.max(np.abs(la - lb))) <= 1e-4
+    assert float(np.max(np.abs(la - lb))) <= 4e-3
     assert not np.array_equal(a, b)
 
