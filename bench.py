@@ -744,7 +744,7 @@ def main():
         "frac_of_peak_kv": round(head["frac_kv"], 4),
         "roofline": {"bound": "hbm", "achieved": round(head["algo_gbs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(head["algo_gbs"] / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel<256,1,0,false,0,false>",
+                     "traffic": traffic, "kernel": "decode_kernel<256,1,0,false,0,false,false>",
                      "algo_bytes_per_launch": head["algo_bytes"]},
         "cpu_baseline": cpu,
         "sweep": sweep,
