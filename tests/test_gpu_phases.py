@@ -50,3 +50,26 @@ def test_stamps_change_nothing_and_are_ordered(D, L):
         assert np.all(m[:, 7] >= m[:, 6]) and np.all(m[:, 8] >= m[:, 7])
         # every column slice of every unit merged exactly once
         assert int(np.sum(m[:, 13])) == pl["units"] * min(pl["slices"], int(n_active[0]))
+
+
+def test_stamps_on_step_rows_change_nothing():
+    """The step-row entry runs the stamping instance too: same bits."""
+    B, n_q, Hq, Hkv, D, cap, L = 1, 3, 16, 4, 256, 4096, 2000
+    k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1102, device=DEV)
+    q = synth.queries(B, n_q, Hq, D, 1102, device=DEV)
+    g = synth.generator(1103)
+    ks = synth.bf16_normal((B, n_q, Hkv, D), g).to(DEV)
+    vs = synth.bf16_normal((B, n_q, Hkv, D), g).to(DEV)
+    lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    note("phase stamps on step rows")
+    ref = ck.decode_attn_steps(q, k, v, lens, ks, vs)
+    pl = ck.plan(ck.shape_of(q, k))
+    stamps = torch.zeros((pl["units"] * pl["splits"], 16), dtype=torch.int64, device=DEV)
+    ck.set_phase_stamps(stamps)
+    try:
+        out = ck.decode_attn_steps(q, k, v, lens, ks, vs)
+    finally:
+        ck.set_phase_stamps(None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert int((stamps[:, 0] > 0).sum()) == pl["units"] * pl["splits"]  # the stamping instance ran

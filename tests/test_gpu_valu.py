@@ -72,6 +72,18 @@ def test_gather(valu, out_dtype):
     assert_close(gpu, oracle_ref(q, k, v, [n_kv], idx=idx), out_dtype, "valu gather")
 
 
+def test_gather_causal_queries(valu):
+    """Three queries with causal limits over their own lists (8 rows each):
+    the limit cuts the tail of the later lists differently per query."""
+    n_kv, L = 8192, 8000
+    k, v = synth.kv_cache(2, n_kv, 2, 128, [L, 5000], 1006)
+    q = synth.queries(2, 3, 16, 128, 1006)
+    idx = synth.topk_lists(2, 3, 2, n_kv, 512, 64, seed=5123)
+    note("valu gather causal n_q=3")
+    gpu = gather_gpu(q, k, v, [L, 5000], idx, causal=True)
+    assert_close(gpu, oracle_ref(q, k, v, [L, 5000], causal=True, idx=idx), what="valu gather causal")
+
+
 def test_batched_ragged(valu):
     """B=32, Hq=32, Hkv=8, D=128, capacity 32768, lengths uniform in
     [512, 32768]: every sequence against the oracle."""
