@@ -216,17 +216,27 @@ def set_contraction(kind: str) -> None:
         raise CkError(st, "ck_set_contraction")
 
 
+_stamps_ref = None  # the buffer set with set_phase_stamps, kept alive while set
+
+
 def set_phase_stamps(stamps) -> None:
     """Phase timestamps of the attention kernels (``ck_set_phase_stamps``):
-    a device int64 tensor of workgroups x 16 words, or None to stop."""
+    a device int64 tensor of workgroups x 16 words, or None to stop.  The
+    tensor is held here until stamping is turned off (launches write to it;
+    graphs captured while it was set keep writing to it when replayed)."""
+    global _stamps_ref
     if stamps is None:
         st = lib().ck_set_phase_stamps(None, 0)
+        if st == 0:
+            _stamps_ref = None
     else:
         if stamps.dtype != torch.int64 or stamps.dim() != 2 or stamps.shape[1] != 16 or not stamps.is_cuda:
             raise ValueError("stamps must be a device int64 tensor of shape [workgroups, 16]")
         if not stamps.is_contiguous():
             raise ValueError("stamps must be contiguous")
         st = lib().ck_set_phase_stamps(ctypes.c_void_p(stamps.data_ptr()), stamps.shape[0])
+        if st == 0:
+            _stamps_ref = stamps
     if st != 0:
         raise CkError(st, "ck_set_phase_stamps")
 

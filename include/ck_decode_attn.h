@@ -411,9 +411,10 @@ int ck_set_contraction(int32_t contraction);
  * word 15 split | unit << 16 | active splits << 32 | role << 48 (1 last
  * arrival, 2 helper that merged a slice, 3 neither).  A launch writes only
  * the words of phases its workgroups reach; the grid is units * splits of
- * ck_decode_attn_plan.  CK_ERR_ARG when exactly one of stamps and
- * workgroups is zero or workgroups < 0, CK_ERR_ALIGN for a misaligned
- * buffer. */
+ * ck_decode_attn_plan.  The buffer must stay allocated while it is set, and
+ * as long as graphs captured meanwhile are replayed (their launches keep
+ * its address).  CK_ERR_ARG when exactly one of stamps and workgroups is
+ * zero or workgroups < 0, CK_ERR_ALIGN for a misaligned buffer. */
 int ck_set_phase_stamps(void* stamps, int64_t workgroups);
 
 /* Static text for a status code. */
