@@ -119,7 +119,7 @@ def merge(mem, c, ns, n_active, rows, cols, out):
             out.setdefault((r, col), []).append(num / den if den > 0 else 0.0)
 
 
-def workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, log):
+def workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, log, mistake=None):
     """Generator: split s of the unit; every yield is a point where other
     workgroups may run and stores may land."""
     par = mem.load(PARITY) & 1
@@ -142,7 +142,7 @@ def workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, l
             mem.store(s, part(s, r, col), acc[col])
         mem.store(s, ml(s, r), (m, l))
     yield
-    while not mem.landed(s):                 # wait for its own stores
+    while mistake != "no store wait" and not mem.landed(s):  # wait for its own stores
         yield
     rank = mem.atomic_add(arrived(par), 1)
     yield
@@ -151,10 +151,11 @@ def workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, l
     helper = not last and rank >= n_active - ns
     if last:
         other = par ^ 1
-        for c in range(n_slices):
-            mem.store(s, flag(other, c), 0)
-        mem.store(s, started(other), 0)
-        mem.store(s, arrived(other), 0)
+        if mistake != "no clear":
+            for c in range(n_slices):
+                mem.store(s, flag(other, c), 0)
+            mem.store(s, started(other), 0)
+            mem.store(s, arrived(other), 0)
         mem.store(s, PARITY, other)
         merge(mem, 0, ns, n_active, rows, cols, out)
         log.append(("merged", s, 0))
@@ -166,7 +167,7 @@ def workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, l
             log.append(("merged", s, c))
     elif helper:
         c = n_active - 1 - rank
-        if seen == n_active and mem.atomic_exch(flag(par, c), 1) == 0:
+        if (seen == n_active or mistake == "ignore started") and mem.atomic_exch(flag(par, c), 1) == 0:
             spins = 0
             while mem.load(arrived(par)) < n_active:
                 spins += 1
@@ -182,7 +183,7 @@ def workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, l
             log.append(("merged", s, c))
 
 
-def run_launch(mem, S, n_active, n_slices, rows, cols, resident, rng, spin_limit=10_000):
+def run_launch(mem, S, n_active, n_slices, rows, cols, resident, rng, spin_limit=10_000, mistake=None):
     """One launch of S workgroups (the grid's splits), dispatched in order
     with at most `resident` running at once.  Returns (outputs by (row,
     column), expected, log)."""
@@ -201,7 +202,7 @@ def run_launch(mem, S, n_active, n_slices, rows, cols, resident, rng, spin_limit
     while queue or running or mem.pending:
         while queue and len(running) < resident:
             s = queue.pop(0)
-            running[s] = workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, log)
+            running[s] = workgroup(mem, s, n_active, n_slices, rows, cols, values, out, spin_limit, log, mistake)
         choices = list(running) + (["land"] if mem.pending else [])
         pick = rng.choice(choices)
         if pick == "land":
@@ -283,3 +284,36 @@ def test_tiny_poll_limit_gives_up_visibly():
         else:
             assert all(close(v[0], expect[k]) for k, v in out.items())
     assert seen_fail
+
+
+def launch_is_right(mem, out, expect, slices):
+    if sorted(out) != sorted(expect):
+        return False
+    if any(len(v) != 1 or not close(v[0], expect[k]) for k, v in out.items()):
+        return False
+    return mem.load(STATUS) == 0 and next_set_clear(mem, slices)
+
+
+@pytest.mark.parametrize("mistake", ["ignore started", "no store wait", "no clear"])
+def test_planted_mistakes_are_caught(mistake):
+    """Each planted mistake makes some schedule produce a wrong output, a
+    wait that runs into the poll limit, or a counter set left dirty: a helper
+    that commits to waiting without having seen every split started, an
+    arrival before the split's stores have landed, a last arrival that does
+    not clear the next counter set."""
+    rng = random.Random(sum(map(ord, mistake)))
+    caught = False
+    for trial in range(300):
+        mem = Memory()
+        S, slices = 8, 4
+        resident = rng.choice([1, 2, 8])
+        for _ in range(3):
+            n_active = rng.choice([S, S - 1, 5])
+            out, expect, log = run_launch(mem, S, n_active, slices, 2, 8, resident, rng, spin_limit=50,
+                                          mistake=mistake)
+            if not launch_is_right(mem, out, expect, slices):
+                caught = True
+                break
+        if caught:
+            break
+    assert caught, mistake
