@@ -113,7 +113,12 @@ enum {
  * padded to whole chunks of 8 x row_groups workgroups when several 16-row
  * groups share the tiles of one head; padding workgroups exit at once);
  * rows = packed query rows per (sequence, [query,] KV head): n_q*G dense,
- * G gather. */
+ * G gather.  The device cuts each unit's range from its length; plain bf16
+ * decode (no keep_mask, no INT8 cache, automatic split count) with one row
+ * group per head, whose units alone leave most compute units idle
+ * (2 * units * split_target > CUs), aims at three quarters of split_target
+ * (fewer, longer splits publish fewer partials); the grid, and so the
+ * workspace, is that of the plan either way. */
 typedef struct ck_decode_plan {
     int32_t units;
     int32_t splits;          /* grid splits per unit                         */
