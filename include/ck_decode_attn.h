@@ -389,9 +389,12 @@ int ck_set_spin_limit(int32_t polls);
  *   CK_CONTRACT_VALU_F32: the same lanes in plain fp32 (every K and V element
  *     widened, one FMA per element and token), the probabilities kept in fp32.
  * All read the same bytes and agree with the exact result within the stated
- * tolerances.  The VALU forms exist to measure the choice (GQA packing makes
- * the KV tile the shared operand of every row; the question is whether the
- * padded MFMA or an unpadded VALU contraction keeps up with HBM); keep_mask,
+ * tolerances.  The VALU forms exist to measure the choice: packing the GQA
+ * group's query heads as rows makes every KV tile read from HBM serve all of
+ * them (comfy-kitchen PR "Performance improvements for qwen 3.x LLM
+ * (Part 1)", GQA decode), which leaves 4 or 8 rows per tile, and the
+ * question is whether the padded MFMA or an unpadded VALU contraction keeps
+ * up with the loads; keep_mask,
  * step rows, the INT8 cache and more than 8 rows always take MFMA.
  * Returns CK_ERR_ARG for any other value. */
 #define CK_CONTRACT_MFMA 0
@@ -400,7 +403,10 @@ int ck_set_spin_limit(int32_t polls);
 int ck_set_contraction(int32_t contraction);
 
 /* Phase timestamps of plain dense decode, for diagnosing where a launch
- * spends its time (process-wide, read at each launch).  While a buffer is
+ * spends its time, in particular the part of a decode step's cost that does
+ * not follow the filled length (ComfyUI issue "Qwen3.5 text generation
+ * attends over the full KV capacity every step, so decode speed drops with
+ * max_length", Measurements) (process-wide, read at each launch).  While a buffer is
  * set, ck_decode_attn and ck_decode_attn_steps launches whose plan has one
  * 16-row group per KV head (at most 16 packed rows, no keep_mask) run a
  * stamping instance of their kernel, a little slower than the plain one;
