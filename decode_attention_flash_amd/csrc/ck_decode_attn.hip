@@ -358,28 +358,69 @@ __device__ __forceinline__ float group_reduce(float v, int span) {
     return v;
 }
 
+// The merge's reductions over groups of `span` lanes (a uniform power of
+// two) as straight-line code: every DPP step runs, and a step beyond the span
+// adds +0 (or takes the max with -inf) through a lane mask the compiler
+// cannot turn back into a branch.  The merge runs once per launch on one wave
+// per output group, so its instruction count is its time.  Only the two
+// cross-row steps sit behind one uniform branch.
+__device__ __forceinline__ uint32_t opaque_mask(bool on) {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(on ? ~0u : 0u));
+    return v;
+}
+template <bool MAX>
+__device__ __forceinline__ float masked_step(float v, float x, uint32_t m) {
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x) & m;
+    if constexpr (MAX)
+        return fmaxf(v, __builtin_bit_cast(float, xb | (0xFF800000u & ~m)));
+    else
+        return v + __builtin_bit_cast(float, xb);
+}
+template <bool MAX, int N>
+__device__ __forceinline__ void group_reduce_masked(float (&v)[N], int span) {
+    const uint32_t m2 = opaque_mask(span >= 2), m4 = opaque_mask(span >= 4);
+    const uint32_t m8 = opaque_mask(span >= 8), m16 = opaque_mask(span >= 16);
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = masked_step<MAX>(v[k], dpp<kDppXor1>(v[k]), m2);
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = masked_step<MAX>(v[k], dpp<kDppXor2>(v[k]), m4);
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = masked_step<MAX>(v[k], dpp<kDppHalfMirror>(v[k]), m8);
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = masked_step<MAX>(v[k], dpp<kDppMirror>(v[k]), m16);
+    if (span >= 32) {
+        auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] = op(v[k], __shfl_xor(v[k], 16));
+        if (span >= 64) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) v[k] = op(v[k], __shfl_xor(v[k], 32));
+        }
+    }
+}
+
 // Merge column slice `c` of `ns` for one unit from the n_active published
 // partials (acc_s, m_s, l_s):  O = sum_s w_s acc_s / sum_s w_s l_s with
 // w_s = 2^(m_s - max m).  Each output group (row, 4 columns) is taken by TPP
-// neighbouring lanes, each lane by a strided subset of at most PRE splits
+// neighbouring lanes, each lane by a strided subset of at most NS splits
 // whose loads are all issued before the first use, so a pass over the
 // outputs costs one round trip.  A lane takes the max of its m_s, then sums
 // its weighted terms (independent exponentials, no serial chain); the TPP
 // lanes then agree on the max, rescale once and sum.  The order is fixed, so
-// the result does not depend on which workgroup merges or when.
-template <int D>
-__device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows, int c, int ns, int b, int g,
-                            int iq, bool gather, int row0) {
+// the result does not depend on which workgroup merges or when.  NS is the
+// slot count rounded up to 4, 8 or 16: every slot costs instructions whether
+// or not a split fills it (a lane past the splits loads at an offset beyond
+// the buffer, which reads zeros without a memory access; skipping the slots
+// no lane fills, behind a uniform branch each, measured 0.1 us slower).
+template <int D, int NS>
+__device__ __forceinline__ void merge_slice_n(const KParams& p, int unit, int n_active, int nrows, int c, int ns,
+                                              int b, int g, int iq, bool gather, int row0, int TPP) {
     constexpr int D4 = D / 4;
-    constexpr int PRE = 16;
     const int tid = threadIdx.x;
     const int col_lo = c * D4 / ns, col_hi = (c + 1) * D4 / ns;
     const int ncol = col_hi - col_lo;
     const int P = nrows * ncol;
-    int TPP = 1;
-    while (TPP < 64 && 2 * TPP * P <= kThreads) TPP *= 2;
-    static_assert(CK_MAX_SPLITS <= 64 * PRE, "a lane holds at most PRE splits");
-    while (TPP < 64 && TPP * PRE < n_active) TPP *= 2;
     const int per_pass = kThreads / TPP;
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
@@ -393,42 +434,69 @@ __device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows,
         const int col = act ? col_lo + pos % ncol : 0;
         const uint32_t xoff = (uint32_t)(rr * D + 4 * col) * 4u;
         const uint32_t moff = (uint32_t)(rr * p.splits) * 8u;
-        f32x4 x[PRE];
-        f32x2 ml[PRE];
+        f32x4 x[NS];
+        f32x2 ml[NS];
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) {
+        for (int u = 0; u < NS; ++u) {
             const int s2 = j + u * TPP;
             const bool ok = act && s2 < n_active;
-            x[u] = ok ? load_dev4(ro, xoff + (uint32_t)s2 * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-            ml[u] = ok ? load_dev2(rml, moff + (uint32_t)s2 * 8u) : f32x2{-INFINITY, 0.f};
+            x[u] = load_dev4(ro, ok ? xoff + (uint32_t)s2 * sstride : kOOB);
+            ml[u] = load_dev2(rml, ok ? moff + (uint32_t)s2 * 8u : kOOB);
         }
         float M = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) M = fmaxf(M, ml[u][0]);
-        float den = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < NS; ++u) {
+            ml[u][0] = (act && j + u * TPP < n_active) ? ml[u][0] : -INFINITY;
+            M = fmaxf(M, ml[u][0]);
+        }
+        float v[5] = {0.f, 0.f, 0.f, 0.f, 0.f};  // den, acc[0..3]
         {
             const float mu = (M == -INFINITY) ? 0.f : M;
 #pragma unroll
-            for (int u = 0; u < PRE; ++u) {
+            for (int u = 0; u < NS; ++u) {
                 const float w = fast_exp2(ml[u][0] - mu);
-                den += w * ml[u][1];
-                acc += w * x[u];
+                v[0] += w * ml[u][1];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k + 1] += w * x[u][k];
             }
         }
-        const float Mg = group_reduce<true>(M, TPP);
+        float mg[1] = {M};
+        group_reduce_masked<true>(mg, TPP);
+        const float Mg = mg[0];
         const float mu = (Mg == -INFINITY) ? 0.f : Mg;
         const float r = fast_exp2(M - mu);
-        den = group_reduce<false>(den * r, TPP);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = group_reduce<false>(acc[k] * r, TPP);
+        for (int k = 0; k < 5; ++k) v[k] *= r;
+        group_reduce_masked<false>(v, TPP);
         if (act && j == 0) {
+            const float den = v[0];
             const float inv = den > 0.f ? 1.f / den : 0.f;
             const size_t orow = out_row(p, b, g, row0 + rr, iq, gather);
-            store4<D>(p, orow, 4 * col, acc * inv);
+            store4<D>(p, orow, 4 * col, f32x4{v[1], v[2], v[3], v[4]} * inv);
             if (col == 0 && p.lse != nullptr) p.lse[orow] = den > 0.f ? (Mg + __log2f(den)) * kLn2 : -INFINITY;
         }
     }
+}
+
+constexpr int kMergeSlots = 16;  // splits one lane of the merge holds at most
+static_assert(CK_MAX_SPLITS <= 64 * kMergeSlots, "a lane holds at most kMergeSlots splits");
+
+template <int D>
+__device__ void merge_slice(const KParams& p, int unit, int n_active, int nrows, int c, int ns, int b, int g,
+                            int iq, bool gather, int row0) {
+    constexpr int D4 = D / 4;
+    const int ncol = (c + 1) * D4 / ns - c * D4 / ns;
+    const int P = nrows * ncol;
+    int TPP = 1;
+    while (TPP < 64 && 2 * TPP * P <= kThreads) TPP *= 2;
+    while (TPP < 64 && TPP * kMergeSlots < n_active) TPP *= 2;
+    const int nslot = (n_active + TPP - 1) / TPP;
+    if (nslot <= 4)
+        merge_slice_n<D, 4>(p, unit, n_active, nrows, c, ns, b, g, iq, gather, row0, TPP);
+    else if (nslot <= 8)
+        merge_slice_n<D, 8>(p, unit, n_active, nrows, c, ns, b, g, iq, gather, row0, TPP);
+    else
+        merge_slice_n<D, kMergeSlots>(p, unit, n_active, nrows, c, ns, b, g, iq, gather, row0, TPP);
 }
 
 // A merge that gave up: its column slice of the output (and the lse of its
@@ -1374,30 +1442,11 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     const bool helper = !last && rank >= n_active - ns;
     if (!last && !helper) return;
     __syncthreads();  // everyone has read ms.flag
-    if (last) {
-        stamp<ST>(p, 7);
-        stamp<ST>(p, 15, (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | (1ull << 48), true);
-        merge_slice<D>(p, unit, n_active, nrows, 0, ns, b, g, iq, GATHER, row0);
-        // ns <= 64: lane c of wave 0 claims slice c, one ballot collects them.
-        // The claims wait until slice 0 is merged: claimed at arrival they
-        // take slices from helpers that arrived just before (their claims
-        // still in flight), and merging those one after another cost 1.5-2.5
-        // us on short sequences.
-        if (wave == 0) {
-            const bool own = lane >= 1 && lane < ns && atomicExch(cnt + kSliceFlag + lane, 1) == 0;
-            const uint64_t mask = __ballot(own);
-            if (lane == 0) ms.owned = mask;
-        }
-        __syncthreads();
-        for (uint64_t mask = ms.owned; mask != 0; mask &= mask - 1)
-            merge_slice<D>(p, unit, n_active, nrows, __builtin_ctzll(mask), ns, b, g, iq, GATHER, row0);
-        if constexpr (ST) {
-            wait_stores();
-            stamp<ST>(p, 8);
-            stamp<ST>(p, 13, 1 + (uint64_t)__builtin_popcountll(ms.owned), true);
-        }
-    } else {
-        const int c = n_active - 1 - rank;
+    // The slice this workgroup merges first: 0 for the last split; a helper's
+    // own slice once it has won the claim and seen every arrival.
+    int c = 0;
+    if (!last) {
+        c = n_active - 1 - rank;
         if (tid == 0) {
             // 0: not ours, 1: merge, 2: gave up waiting
             int ok = 0;
@@ -1419,17 +1468,44 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             ms.flag = ok;
         }
         __syncthreads();
-        if (ms.flag == 1) {
-            stamp<ST>(p, 7);
-            stamp<ST>(p, 15, (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | (2ull << 48), true);
-            merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
-            if constexpr (ST) {
-                wait_stores();
-                stamp<ST>(p, 8);
-                stamp<ST>(p, 13, 1, true);
+        const int ok = ms.flag;
+        if (ok == 2) fill_slice_nan<D>(p, nrows, c, ns, b, g, iq, GATHER, row0);
+        if (ok != 1) return;
+    }
+    stamp<ST>(p, 7);
+    stamp<ST>(p, 15,
+              (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | ((last ? 1ull : 2ull) << 48), true);
+    // One call site for every slice (the merge is inlined once): the last
+    // split's first slice is followed by its claims, then by each slice it
+    // won.  ns <= 64: lane c of wave 0 claims slice c, one ballot collects
+    // them.  The claims wait until slice 0 is merged: claimed at arrival they
+    // take slices from helpers that arrived just before (their claims still
+    // in flight), and merging those one after another cost 1.5-2.5 us on
+    // short sequences.
+    uint64_t more = 0;
+    int merged = 0;
+    for (bool first_slice = true;; first_slice = false) {
+        merge_slice<D>(p, unit, n_active, nrows, c, ns, b, g, iq, GATHER, row0);
+        ++merged;
+        if (last && first_slice) {
+            if (wave == 0) {
+                const bool own = lane >= 1 && lane < ns && atomicExch(cnt + kSliceFlag + lane, 1) == 0;
+                const uint64_t mask = __ballot(own);
+                if (lane == 0) ms.owned = mask;
             }
+            __syncthreads();
+            const uint64_t owned = ms.owned;
+            more = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(owned >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)owned);
         }
-        if (ms.flag == 2) fill_slice_nan<D>(p, nrows, c, ns, b, g, iq, GATHER, row0);
+        if (more == 0) break;
+        c = __builtin_ctzll(more);
+        more &= more - 1;
+    }
+    if constexpr (ST) {
+        wait_stores();
+        stamp<ST>(p, 8);
+        stamp<ST>(p, 13, (uint64_t)merged, true);
     }
 }
 
@@ -1593,18 +1669,21 @@ static int plan_impl(const ck_decode_shape* s, int32_t W, int num_splits, int nu
     pl->rows = (int32_t)R;
     pl->row_groups = (int32_t)RG;
     pl->rows_per_group = rows_per_group;
-    // Column slices of the merge: about 32 KiB of partials each, at most one
+    // Column slices of the merge: about 16 KiB of partials each, at most one
     // per 4 columns and at most kPlanSlices.  Every slice but the first is
-    // merged by a helper that polls the unit's arrival count; at 32 slices
-    // (12-24 packed rows) up to 31 helpers per unit polled one word, and a
-    // launch whose splits arrived spread out (measured with a prologue that
-    // sent the first tile earlier) took 22 us instead of 10.7 at n_q = 3,
-    // kv_len 2000.  16 measured the same or faster on every MTP window
-    // (n_q = 4 at 2000: 11.7 -> 11.5 us); 8 was slower (n_q = 3 at 4000:
-    // 12.6 -> 14.9 us).
+    // merged by a helper that polls the unit's arrival count.  A merging
+    // lane's work follows the splits it holds, so smaller slices shorten the
+    // merge: 16 against 32 KiB took 9.7 / 12.6 / 22.2 us against 10.3 / 13.1 /
+    // 22.6 at kv_len 3000 / 8000 / 24000 (head_dim 256, 4 KV heads).  The cap
+    // matters for 12-24 packed rows: 32 slices made n_q = 3 windows faster
+    // (0.3-0.55 us) and n_q = 4-5 slower (0.2-0.35 us); with a prologue that
+    // sent the first tile earlier, 31 helpers polling one word per unit made
+    // a launch whose splits arrived spread out take 22 us instead of 10.7
+    // (n_q = 3, kv_len 2000).  A cap of 8 was slower (n_q = 3 at 4000: 12.6
+    // -> 14.9 us).
     const int64_t merge_bytes = splits * rows_eff * s->D * 4;
     int64_t slices = 1;
-    while (slices * 32768 < merge_bytes && slices < s->D / 4 && slices < kPlanSlices) slices *= 2;
+    while (slices * 16384 < merge_bytes && slices < s->D / 4 && slices < kPlanSlices) slices *= 2;
     pl->slices = (int32_t)slices;
     pl->tile = tile_bytes(rows_per_group / 16) / (2 * s->D);
     if (splits == 1) {

@@ -36,12 +36,13 @@ def test_status_strings():
 
 
 def test_plan_merge_slices():
-    """About 32 KiB of partials per merge slice, at most 16 slices (each
+    """About 16 KiB of partials per merge slice, at most 16 slices (each
     beyond the first is a helper polling the unit's arrival count)."""
-    assert ck.plan(shape(), num_cus=256)["slices"] == 8             # 4 rows x 64 splits x 256 cols
-    assert ck.plan(shape(n_q=3), num_cus=256)["slices"] == 16       # 12 rows: 24 by size, capped
+    assert ck.plan(shape(), num_cus=256)["slices"] == 16            # 4 rows x 64 splits x 256 cols: 256 KiB
+    assert ck.plan(shape(n_q=3), num_cus=256)["slices"] == 16       # 12 rows: 48 by size, capped
     assert ck.plan(shape(n_q=6), num_cus=256)["slices"] == 16       # two 16-row groups
-    assert ck.plan(shape(Hq=8, Hkv=2, D=128, cap=1024), num_cus=256)["slices"] <= 16
+    assert ck.plan(shape(Hq=8, Hkv=2, D=128, cap=1024), num_cus=256)["slices"] == 2  # 16 x 4 x 128: 32 KiB
+    assert ck.plan(shape(B=32, Hq=32, Hkv=8, D=128, cap=32768), num_cus=256)["slices"] == 1  # 8 x 4 x 128
     assert ck.plan(shape(), num_splits=1, num_cus=256)["slices"] == 1
 
 
