@@ -384,6 +384,49 @@ def test_split_count_does_not_change_result(layer_d256, num_splits):
     assert_close(gpu, oracle_ref(q, k, v, [3000], causal=True), what=f"S={num_splits}")
 
 
+def merge_slots(plan, R, D, L, num_splits):
+    """Splits per merging lane, rounded up to the kernel's 4, 8 or 16 slots,
+    for one sequence of length L under `plan` (the split count, chunk and
+    output-group arithmetic the kernel's split merge uses)."""
+    tt, target = plan["granule"], num_splits if num_splits else plan["split_target"]
+    c = -(-L // target)
+    c = max(-(-c // tt) * tt, plan["chunk_min"])
+    n_active = -(-L // c)
+    ns = min(plan["slices"], n_active)
+    P = min(R, plan["rows_per_group"]) * ((D // 4) // ns)
+    tpp = 1
+    while tpp < 64 and 2 * tpp * P <= 256:
+        tpp *= 2
+    while tpp < 64 and tpp * 16 < n_active:
+        tpp *= 2
+    nslot = -(-n_active // tpp)
+    return n_active, 4 if nslot <= 4 else 8 if nslot <= 8 else 16
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,n_q,L,num_splits,slots", [
+    (256, 16, 4, 1, 3000, 64, 4),
+    (256, 16, 4, 2, 3000, 64, 8),
+    (256, 16, 4, 4, 3000, 64, 16),
+    (128, 8, 2, 1, 8000, 128, 4),
+    (128, 8, 2, 2, 8000, 128, 8),
+    (128, 8, 2, 4, 8000, 128, 16),
+], ids=lambda x: str(x))
+def test_merge_slot_counts(D, Hq, Hkv, n_q, L, num_splits, slots):
+    """Each of the merge's slot counts (4, 8 and 16 splits per lane) at both
+    head dims, against the oracle: many splits over a causal window, so the
+    merging lanes hold full, partial and empty slots."""
+    cap = L + 64
+    R = n_q * (Hq // Hkv)
+    plan = ck.plan(ck.Shape(1, n_q, Hq, Hkv, D, cap), num_splits=num_splits, num_cus=256)
+    n_active, got = merge_slots(plan, R, D, L, num_splits)
+    assert got == slots and n_active > 1, (n_active, got)
+    k, v = synth.kv_cache(1, cap, Hkv, D, [L], 1200 + D + n_q)
+    q = synth.queries(1, n_q, Hq, D, 1200 + D + n_q)
+    note(f"merge slots {slots}: D={D} n_q={n_q} L={L} S={num_splits} active={n_active}")
+    gpu = dense_gpu(q, k, v, [L], causal=n_q > 1, num_splits=num_splits)
+    assert_close(gpu, oracle_ref(q, k, v, [L], causal=n_q > 1), what=f"slots {slots}")
+
+
 @pytest.mark.parametrize("D", [128, 256])
 def test_edge_lengths(D):
     """Empty, single-cell, tile-boundary, full and out-of-range lengths in
