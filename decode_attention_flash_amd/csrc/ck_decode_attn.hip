@@ -361,9 +361,9 @@ __device__ __forceinline__ float group_reduce(float v, int span) {
 // The merge's reductions over groups of `span` lanes (a uniform power of
 // two) as straight-line code: every DPP step runs, and a step beyond the span
 // adds +0 (or takes the max with -inf) through a lane mask the compiler
-// cannot turn back into a branch.  The merge runs once per launch on one wave
-// per output group, so its instruction count is its time.  Only the two
-// cross-row steps sit behind one uniform branch.
+// cannot turn back into a branch.  A merging wave runs this code once per
+// launch, so its instruction count is its time.  Only the two cross-row
+// steps sit behind one uniform branch.
 __device__ __forceinline__ uint32_t opaque_mask(bool on) {
     uint32_t v;
     asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(on ? ~0u : 0u));
