@@ -1320,9 +1320,12 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // unit has a single split, else this split's partial (unnormalised acc,
     // m, l) with device-coherent stores.  Row tiles are dumped in rounds when
     // all of them do not fit in LDS at once.
-    constexpr int RT_ROUND = (kWaves * RT * NB * 64 * 16 <= kWaves * Gm::STAGE) ? RT : 1;
-    static_assert(kWaves * RT_ROUND * NB * 64 * 16 <= kWaves * Gm::STAGE, "merge area exceeds LDS");
-    f32x4* dump = reinterpret_cast<f32x4*>(smem);
+    constexpr int RT_ROUND = (RT * NB * 64 * 16 <= Gm::STAGE) ? RT : 1;
+    static_assert(RT_ROUND * NB * 64 * 16 <= Gm::STAGE, "a wave's dump exceeds its staging area");
+    static_assert(Gm::STAGE % 16 == 0, "16-byte dump slots");
+    // Wave w dumps into its own staging area, which no other wave touches, so
+    // the first round's dump needs no barrier before it.
+    auto dump_of = [&](int w) { return reinterpret_cast<f32x4*>(smem + w * Gm::STAGE); };
     const uint32_t unit_parts = (uint32_t)(p.splits * p.rows_alloc);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.ws_o + (size_t)unit * unit_parts * D, unit_parts * D * 4u);
     const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.ws_ml + (size_t)unit * unit_parts * 2, unit_parts * 8u);
@@ -1338,22 +1341,21 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     }
 #pragma unroll
     for (int rt0 = 0; rt0 < RT; rt0 += RT_ROUND) {
-        __syncthreads();  // the staging area (or the previous round) is free
+        if (ST || rt0 > 0) __syncthreads();  // the previous round's reads are done
         if (rt0 == 0) stamp<ST>(p, 4);
         if constexpr (RV == 0) {
 #pragma unroll
             for (int rl = 0; rl < RT_ROUND; ++rl)
 #pragma unroll
                 for (int n = 0; n < NB; ++n)
-                    dump[((wave * RT_ROUND + rl) * NB + n) * 64 + q4 * 16 + (l16 ^ ((4 * n + q4) & 15))] =
-                        st.o[rt0 + rl][n];
+                    dump_of(wave)[(rl * NB + n) * 64 + q4 * 16 + (l16 ^ ((4 * n + q4) & 15))] = st.o[rt0 + rl][n];
         } else {
             // the same slots as the MFMA layout: (row, 4 columns) of block n,
             // column group q
 #pragma unroll
             for (int j = 0; j < DS / 4; ++j) {
                 const int c0 = dp * DS + 4 * j, n = c0 >> 4, q = (c0 >> 2) & 3;
-                dump[(wave * NB + n) * 64 + q * 16 + (vr ^ ((4 * n + q) & 15))] =
+                dump_of(wave)[n * 64 + q * 16 + (vr ^ ((4 * n + q) & 15))] =
                     f32x4{vacc[4 * j], vacc[4 * j + 1], vacc[4 * j + 2], vacc[4 * j + 3]};
             }
         }
@@ -1381,7 +1383,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             for (int w = 0; w < kWaves; ++w) {
                 const float wt = fast_exp2(mw[w] - mu);
                 den += wt * s_ml[w][rt0 + rl][r16][1];
-                a += wt * dump[((w * RT_ROUND + rl) * NB + (d4 >> 2)) * 64 + src];
+                a += wt * dump_of(w)[(rl * NB + (d4 >> 2)) * 64 + src];
             }
             if (n_active == 1) {
                 const size_t orow = out_row(p, b, g, row0 + rr, iq, GATHER);
