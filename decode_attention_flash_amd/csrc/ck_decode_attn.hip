@@ -63,6 +63,17 @@ constexpr int kStarted = 0, kArrived = 32, kSliceFlag = 64;
 constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ballot
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 constexpr int kPlanSlices = 16;  // the plan's limit (see plan_impl)
+// Short work: with an automatic split count, a unit whose span holds at most
+// kSingleSplitBytes of K+V (4·D bytes per position) is streamed by one
+// split, which writes the output
+// itself: the split merge's store, arrival and read-back cost more than one
+// workgroup's read of that much (head_dim 128 at 100 / 200 tokens: 4.35 /
+// 5.55 us against 6.9 / 7.2; 160 KiB measured even, 200 KiB slower).  A merge
+// of at most kSingleSliceBytes of partials runs as one column slice (no
+// helpers): their claim and polling cost more than they share (head_dim 128,
+// 300-1000 tokens: 0.4-0.5 us less; 64 KiB was slower at head_dim 256).
+constexpr int64_t kSingleSplitBytes = 128 * 1024;
+constexpr int64_t kSingleSliceBytes = 32 * 1024;
 static_assert(kPlanSlices <= kMaxSlices, "slices per unit");
 
 // Bytes of K per wave tile.  With one row tile (up to 16 packed rows) the
@@ -130,6 +141,7 @@ struct KParams {
     int32_t units;   // work units (grid = splits x units)
     int32_t splits;  // grid splits per unit
     int32_t S_target, c_min, c_max, gran;
+    int32_t auto_splits;  // split count chosen by the plan (short spans take one split)
     int32_t slices;  // column slices of the merge
     int32_t W;
     int64_t idx_head_stride;  // 0: one list per query shared by its heads
@@ -623,7 +635,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     }
     const int L = L_raw < 0 ? 0 : (L_raw > p.cap ? p.cap : L_raw);
     const int span = GATHER ? p.W : L;
-    const int C = chunk_len(span, p);
+    const int C = p.auto_splits && (int64_t)span * 4 * D <= kSingleSplitBytes ? span : chunk_len(span, p);
     const int n_active = span > 0 ? (span + C - 1) / C : 1;
     stamp<ST>(p, 1);
     stamp<ST>(p, 15, (uint64_t)s | ((uint64_t)unit << 16) | ((uint64_t)n_active << 32) | (3ull << 48), true);
@@ -1438,8 +1450,9 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // slice's claim flag, but only if every split of the unit was already
     // running, so its wait for the other arrivals can never depend on a
     // workgroup that has not been scheduled.  After slice 0 the last split
-    // claims and merges every slice no helper took.
-    const int ns = min(p.slices, n_active);
+    // claims and merges every slice no helper took.  A small merge is one
+    // slice.
+    const int ns = (int64_t)n_active * nrows * D * 4 <= kSingleSliceBytes ? 1 : min(p.slices, n_active);
     const bool last = rank == n_active - 1;
     const bool helper = !last && rank >= n_active - ns;
     if (!last && !helper) return;
@@ -1894,6 +1907,7 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
         (int64_t)pl.units * pl.split_target * 2 > cus)
         kp.S_target = max(1, pl.split_target * 3 / 4);
     kp.c_min = pl.chunk_min;
+    kp.auto_splits = num_splits == 0 ? 1 : 0;
     kp.c_max = pl.chunk_max;
     kp.gran = pl.granule;
     kp.slices = pl.slices;

@@ -113,8 +113,11 @@ enum {
  * padded to whole chunks of 8 x row_groups workgroups when several 16-row
  * groups share the tiles of one head; padding workgroups exit at once);
  * rows = packed query rows per (sequence, [query,] KV head): n_q*G dense,
- * G gather.  The device cuts each unit's range from its length; plain bf16
- * decode (no keep_mask, no INT8 cache, automatic split count) with one row
+ * G gather.  The device cuts each unit's range from its length.  With an
+ * automatic split count, a unit whose range holds at most 128 KiB of K+V
+ * (4 * D bytes per position) is streamed by one split, which writes the
+ * output itself (no split merge).  Plain bf16 decode (no keep_mask, no INT8
+ * cache, automatic split count) with one row
  * group per head, whose units alone leave most compute units idle
  * (2 * units * split_target > CUs), aims at three quarters of split_target
  * (fewer, longer splits publish fewer partials); the grid, and so the
@@ -131,7 +134,9 @@ typedef struct ck_decode_plan {
     int32_t rows_per_group;  /* rows handled by one workgroup: 16, or 32 for
                                 17-32 rows when two 16-row groups would get
                                 fewer than 16 splits each                    */
-    int32_t slices;          /* column slices the split merge is cut into    */
+    int32_t slices;          /* column slices the split merge is cut into at
+                                most; a merge of at most 32 KiB of partials
+                                is one slice                                 */
     int32_t tile;            /* cache positions (or list entries) per wave
                                 tile: a masked scan reads whole tiles that
                                 hold a kept cell and skips the others        */

@@ -392,8 +392,9 @@ def merge_slots(plan, R, D, L, num_splits):
     c = -(-L // target)
     c = max(-(-c // tt) * tt, plan["chunk_min"])
     n_active = -(-L // c)
-    ns = min(plan["slices"], n_active)
-    P = min(R, plan["rows_per_group"]) * ((D // 4) // ns)
+    nrows = min(R, plan["rows_per_group"])
+    ns = 1 if n_active * nrows * D * 4 <= 32 * 1024 else min(plan["slices"], n_active)
+    P = nrows * ((D // 4) // ns)
     tpp = 1
     while tpp < 64 and 2 * tpp * P <= 256:
         tpp *= 2
@@ -425,6 +426,24 @@ def test_merge_slot_counts(D, Hq, Hkv, n_q, L, num_splits, slots):
     note(f"merge slots {slots}: D={D} n_q={n_q} L={L} S={num_splits} active={n_active}")
     gpu = dense_gpu(q, k, v, [L], causal=n_q > 1, num_splits=num_splits)
     assert_close(gpu, oracle_ref(q, k, v, [L], causal=n_q > 1), what=f"slots {slots}")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_short_span_single_split_threshold(D):
+    """Lengths around the automatic single-split threshold (128 KiB of K+V per
+    unit: 256 positions at head_dim 128, 128 at 256), plain and as a causal
+    window, and a merge small enough to run as one column slice."""
+    Hq, Hkv = 8, 2
+    edge = 128 * 1024 // (4 * D)
+    lens = np.array([edge - 2, edge - 1, edge, edge + 1, edge + 17, 3 * edge], dtype=np.int32)
+    cap = int(lens.max()) + 8
+    B = len(lens)
+    k, v = synth.kv_cache(B, cap, Hkv, D, lens, 61 + D)
+    for n_q in (1, 3):
+        q = synth.queries(B, n_q, Hq, D, 62 + D + n_q)
+        note(f"single-split threshold D={D} n_q={n_q} lens={lens.tolist()}")
+        gpu = dense_gpu(q, k, v, lens, causal=n_q > 1)
+        assert_close(gpu, oracle_ref(q, k, v, lens, causal=n_q > 1), what=f"threshold D={D} n_q={n_q}")
 
 
 @pytest.mark.parametrize("D", [128, 256])
