@@ -568,10 +568,15 @@ def main():
         sweep["warm_kv_len_8000"] = dict(kv_len=8000, cap=cap, note="one cache replayed (warm)", **r)
         sweep["causal_window"] = []
         for L in (2000, 4000):
+            # the same bytes as one query: the window's cost against it
+            r1 = dense_case(stack, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup)
+            log(f"window n_q=1 L={L}: {r1['us']:.2f} us")
+            sweep["causal_window"].append(dict(kv_len=L, n_q=1, ratio_vs_nq1=1.0, **r1))
             for n_q in (3, 4, 5, 6):
                 r = dense_case(stack, 1, n_q, Hq, Hkv, D, [L], args.steps, args.warmup, causal=True)
-                log(f"window n_q={n_q} L={L}: {r['us']:.2f} us")
-                sweep["causal_window"].append(dict(kv_len=L, n_q=n_q, **r))
+                ratio = r["us"] / r1["us"]
+                log(f"window n_q={n_q} L={L}: {r['us']:.2f} us ({ratio:.2f}x n_q=1)")
+                sweep["causal_window"].append(dict(kv_len=L, n_q=n_q, ratio_vs_nq1=round(ratio, 3), **r))
         sweep["step_rows"] = []
         for L in (2000, 4000):
             for n_q in (3, 4, 5, 6):
