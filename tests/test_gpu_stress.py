@@ -73,3 +73,11 @@ def test_stress_ragged_batch(num_splits):
     """The ragged batch shape (B=32, Hq=32, Hkv=8, D=128, capacity 32768),
     lengths uniform in [512, 32768]."""
     stress(32, 32, 8, 128, 32768, 512, 32768, num_splits, 5200 + num_splits)
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_stress_short_spans(num_splits):
+    """Short sequences (B=2, Hq=8, Hkv=2, D=128, capacity 1024), lengths
+    uniform in [1, 1024]: with automatic splits the lengths cross the
+    single-split bound (256 positions) and the one-slice merge bound."""
+    stress(2, 8, 2, 128, 1024, 1, 1024, num_splits, 5300 + num_splits)
