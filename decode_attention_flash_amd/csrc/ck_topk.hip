@@ -39,11 +39,17 @@ constexpr int kBins = 2048;           // widest digit: 11 bits
 constexpr int kAuxDevice = 16;  // sc1: served from the device's point of coherence
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
-// Per-row workspace, in 32-bit words: barrier and completion counters, the
-// three level histograms, then (above, equal) counts per workgroup.
+// Per-row workspace, in 32-bit words: a parity word naming the set the next
+// launch uses and, 64 bytes apart, the barrier counters of two sets; the
+// three level histograms of each set; then (above, equal) counts per
+// workgroup.  A launch uses one set and clears the other one early (its
+// stores overlap the score loads), and the row's last arrival at its final
+// barrier flips the parity: no clearing pass or completion count at the end.
 constexpr int kWsCounters = 64;
+constexpr int kWsParity = 0, kWsCtr0 = 16, kWsCtrStride = 16;
 constexpr int kWsHist = kWsCounters;
-constexpr int kWsCounts = kWsHist + 3 * kBins;
+constexpr int kWsHistSet = 3 * kBins;
+constexpr int kWsCounts = kWsHist + 2 * kWsHistSet;
 constexpr int kMaxWgPerRow = 256;
 constexpr int kWsCand = kWsCounts + 2 * kMaxWgPerRow;  // then (key, position) pairs, per workgroup
 constexpr int kCand = 4096;                               // threshold-bin cells gathered in LDS
@@ -248,14 +254,29 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
 
     const bool shared_row = p.P > 1;
     uint32_t* ws = p.ws + (size_t)row * p.ws_row_words;
-    uint32_t* ctr = ws;  // [0] barrier arrivals, [1] completions
+    // This launch's set, and the other set (the previous launch's) cleared
+    // now: every workgroup its share of the histograms, workgroup 0 the
+    // counter.  Nothing waits on these stores; the launch boundary orders
+    // them before the next launch, which uses that set.
+    int par = 0;
+    if (shared_row) {
+        par = __builtin_amdgcn_readfirstlane(ld_dev(ws + kWsParity)) & 1;
+        uint32_t* other = ws + kWsHist + (par ^ 1) * kWsHistSet;
+        const int chunk = (kWsHistSet + p.P - 1) / p.P;
+        for (int j = w * chunk + tid; j < min(kWsHistSet, (w + 1) * chunk); j += kThreads) st_dev(other + j, 0u);
+        if (w == 0 && tid == 0) st_dev(ws + kWsCtr0 + (par ^ 1) * kWsCtrStride, 0u);
+    }
+    uint32_t* ctr = ws + kWsCtr0 + par * kWsCtrStride;  // barrier arrivals of this launch's set
     int barriers = 0;
-    auto row_barrier = [&]() {
+    // The row's last arrival at its final barrier flips the parity: every
+    // workgroup of the row read it before arriving there.
+    auto row_barrier = [&](bool final) {
         ++barriers;
         wait_stores();
         __syncthreads();
         if (tid == 0) {
-            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t rank = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (final && rank == (uint32_t)(barriers * p.P - 1)) st_dev(ws + kWsParity, (uint32_t)(par ^ 1));
             int spins = 0;
             while (ld_dev(ctr) < barriers * p.P) {
                 __builtin_amdgcn_s_sleep(1);
@@ -331,13 +352,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             if (in) atomicAdd(&lh[(key >> shift) & (uint32_t)(nb - 1)], 1u);
         });
         __syncthreads();
-        uint32_t* gh = ws + kWsHist + lvl * kBins;
+        uint32_t* gh = ws + kWsHist + par * kWsHistSet + lvl * kBins;
         if (shared_row) {
             for (int j = tid; j < nb; j += kThreads) {
                 const uint32_t c = lh[j];
                 if (c) __hip_atomic_fetch_add(gh + j, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            row_barrier();
+            row_barrier(false);
         }
         uint32_t n_above, n_bin;
         const uint32_t digit = find_bin(shared_row ? gh : nullptr, nb, k_rem, &n_above, &n_bin);
@@ -380,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             st_dev(counts + 2 * w, a_w);
             st_dev(counts + 2 * w + 1, c_w);
         }
-        row_barrier();
+        row_barrier(true);
         const uint32_t a = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
         const uint32_t c = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid + 1) : 0u;
         uint32_t a_tot, c_tot;
@@ -470,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
                 st_dev(counts + 2 * w, g_w);
                 st_dev(counts + 2 * w + 1, e_w);
             }
-            row_barrier();
+            row_barrier(true);
             // Thread t < P holds workgroup t's counts; scans give every
             // workgroup's equal-key rank start and output offset.
             const uint32_t g = tid < p.P ? (uint32_t)ld_dev(counts + 2 * tid) : 0u;
@@ -529,23 +550,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
         load_raw(sb, x);
         to_keys(x, sb, kk);
         emit(kk, sb);
-    }
-
-    // ---- leave the row's workspace zeroed for the next launch ----
-    if (shared_row) {
-        // Every workgroup passed the last barrier after reading the level
-        // histograms, so they can be cleared; the counts are rewritten by
-        // every launch.  The last workgroup to finish resets the counters.
-        const int words = 3 * kBins;
-        const int chunk = (words + p.P - 1) / p.P;
-        for (int j = w * chunk + tid; j < min(words, (w + 1) * chunk); j += kThreads) st_dev(ws + kWsHist + j, 0u);
-        wait_stores();
-        __syncthreads();
-        if (tid == 0 && __hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                            (uint32_t)(p.P - 1)) {
-            st_dev(ctr, 0u);
-            st_dev(ctr + 1, 0u);
-        }
     }
 }
 

@@ -264,8 +264,13 @@ int ck_decode_sparse_path(const ck_decode_shape* shape, int32_t W, int64_t n_kv,
  *   idx       : int32 [B, n_q, Hs, k + tail], device memory, written whole
  *   workspace : as for the attention entries: ck_decode_topk_workspace_size
  *               bytes (0 when one workgroup serves a row), 256-byte aligned,
- *               zeroed once; every launch leaves it zeroed apart from the
- *               status word in its 256-byte header (ck_workspace_status).
+ *               zeroed once.  Each row holds a parity word and two sets of
+ *               barrier counters and level histograms: a launch uses the
+ *               set the parity names (zero when it starts), clears the
+ *               other and flips the parity, so the buffer serves any number
+ *               of launches of the same plan, eager or replayed from a
+ *               graph, without a memset; its 256-byte header holds the
+ *               status word (ck_workspace_status).
  * Errors as for the attention entries; nothing is launched on error.
  * CK_ERR_UNSUPPORTED also when cap * 4 bytes reaches 2 GiB, or when the
  * rows' workgroups would need 2 GiB of (key, position) slots for one row

@@ -69,8 +69,9 @@ def test_topk_barrier_gives_up_visibly():
     assert p["wgs_per_row"] > 1 and p["workspace_bytes"] > 0
     ws = torch.zeros(p["workspace_bytes"], dtype=torch.uint8, device=DEV)
     P = p["wgs_per_row"]
-    # row 0's barrier count: the first word after the 256-byte header
-    ws.view(torch.int32)[64] = -P
+    # row 0's barrier count of counter set 0 (the set a zeroed workspace's
+    # parity names): word 16 of the row, after the 256-byte header
+    ws.view(torch.int32)[64 + 16] = -P
     note("top-k give-up: row barrier count starts at -P, poll limit 1000")
     ck.set_spin_limit(1000)
     try:
