@@ -64,14 +64,14 @@ constexpr int kMaxSlices = 64;  // slice claims are collected by one wave's ball
 static_assert(kMaxSlices <= 64, "one claim per lane of a wave");
 constexpr int kPlanSlices = 16;  // the plan's limit (see plan_impl)
 // Short work: with an automatic split count, a unit whose span holds at most
-// kSingleSplitBytes of K+V (4·D bytes per position) is streamed by one
-// split, which writes the output
-// itself: the split merge's store, arrival and read-back cost more than one
-// workgroup's read of that much (head_dim 128 at 100 / 200 tokens: 4.35 /
-// 5.55 us against 6.9 / 7.2; 160 KiB measured even, 200 KiB slower).  A merge
-// of at most kSingleSliceBytes of partials runs as one column slice (no
-// helpers): their claim and polling cost more than they share (head_dim 128,
-// 300-1000 tokens: 0.4-0.5 us less; 64 KiB was slower at head_dim 256).
+// kSingleSplitBytes of K+V (4·D bytes per position) is streamed by one split,
+// which writes the output itself: the split merge's store, arrival and
+// read-back cost more than one workgroup's read of that much (head_dim 128
+// at 100 / 200 tokens: 4.35 / 5.55 us against 6.9 / 7.2; 160 KiB measured
+// even, 200 KiB slower).  A merge of at most kSingleSliceBytes of partials
+// runs as one column slice (no helpers): their claim and polling cost more
+// than they share (head_dim 128, 300-1000 tokens: 0.4-0.5 us less; 64 KiB
+// was slower at head_dim 256).
 constexpr int64_t kSingleSplitBytes = 128 * 1024;
 constexpr int64_t kSingleSliceBytes = 32 * 1024;
 static_assert(kPlanSlices <= kMaxSlices, "slices per unit");
