@@ -585,6 +585,21 @@ def main():
                 sweep["step_rows"].append(dict(prefix=L - n_q, n_q=n_q, **r))
         del stack
         torch.cuda.empty_cache()
+        # short sequences: the tiny decode layer (Hq=8, Hkv=2, D=128, capacity
+        # 1024) and the head_dim-256 layer at 100 tokens
+        sweep["short"] = []
+        st = Stack(256, 1, 1024, 2, 128, 1001)
+        for L in (100, 300, 1000):
+            r = dense_case(st, 1, 1, 8, 2, 128, [L], args.steps, args.warmup)
+            log(f"short D=128 kv_len {L}: {r['us']:.2f} us")
+            sweep["short"].append(dict(D=128, Hq=8, Hkv=2, cap=1024, kv_len=L, **r))
+        del st
+        st = Stack(256, 1, 1024, Hkv, D, 1002)
+        r = dense_case(st, 1, 1, Hq, Hkv, D, [100], args.steps, args.warmup)
+        log(f"short D=256 kv_len 100: {r['us']:.2f} us")
+        sweep["short"].append(dict(D=D, Hq=Hq, Hkv=Hkv, cap=1024, kv_len=100, **r))
+        del st
+        torch.cuda.empty_cache()
         sweep["capacity"] = []
         for c in (8199, 16263, 24007):
             n = layers_for(4 * Hkv * D * 3000)
