@@ -50,6 +50,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer descriptor, dword data format
 constexpr uint32_t kOOB = 0x80000000u;        // an offset beyond every range we build
+constexpr int kBtFirst = 4 * 64;               // block-table entries loaded with the length
 constexpr int kMaxQueries = CK_MAX_NQ;         // query rows per sequence (n_q)
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -609,6 +610,12 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     int32_t* const ucnt = p.ws_cnt + kCntStride * unit;
     const int par_word = p.splits > 1 ? atomic_ld(ucnt + kParity) : 0;
     const int L_raw = p.kv_lens[b];
+    // Paged INT8 cache: the sequence's first kBtFirst block-table entries, 16
+    // bytes a lane, travel with the length.  Past the table the load reads 0.
+    const __amdgpu_buffer_rsrc_t rbt =
+        make_rsrc(Q8 ? p.block_table + (size_t)b * p.max_pages : p.kv_lens, Q8 ? (uint32_t)p.max_pages * 4u : 0u);
+    u32x4 bt_first{0u, 0u, 0u, 0u};
+    if constexpr (Q8) bt_first = bload128(rbt, (uint32_t)lane * 16u);
     constexpr int QF = RT * KS * 64 / kThreads;  // fragments per thread
     bf16x8 qfrag[QF];
     {
@@ -719,11 +726,20 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // with a vector-memory load (a scalar load would be counted with the LDS
     // accesses, and every LDS wait would then also wait for it).  Past the
     // table the load reads 0; such tiles are past the split and read nothing.
-    const __amdgpu_buffer_rsrc_t rbt =
-        make_rsrc(Q8 ? p.block_table + (size_t)b * p.max_pages : p.kv_lens, Q8 ? (uint32_t)p.max_pages * 4u : 0u);
     auto page_of = [&](int tile) -> int {
         const uint32_t idx = (uint32_t)((pos_begin + tile * TT) / (Q8 ? p.page : 1));
         return __builtin_amdgcn_raw_buffer_load_b32(rbt, idx * 4u, 0, 0);
+    };
+    // The first tile's page comes from the entries loaded with the length
+    // when it is among them, so its loads need no round trip after the
+    // length is known.
+    auto first_page_of = [&](int tile) -> int {
+        const int idx = __builtin_amdgcn_readfirstlane((pos_begin + tile * TT) / (Q8 ? p.page : 1));
+        if (idx >= kBtFirst) return page_of(tile);
+        const int ln = idx >> 2, c = idx & 3;
+        const uint32_t x = __builtin_amdgcn_readlane((int)bt_first[0], ln), y = __builtin_amdgcn_readlane((int)bt_first[1], ln),
+                       z = __builtin_amdgcn_readlane((int)bt_first[2], ln), w = __builtin_amdgcn_readlane((int)bt_first[3], ln);
+        return (int)(c == 0 ? x : c == 1 ? y : c == 2 ? z : w);
     };
 
     // Issue the K and V loads (and mask loads) of one tile.  Load n of a lane
@@ -893,7 +909,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     }
     if (first < ntiles) {
         if constexpr (GATHER) jv_next = list_entry(wave);
-        if constexpr (Q8) jv_next = page_of(wave);
+        if constexpr (Q8) jv_next = first_page_of(wave);
         issue(first, jv_next);
         if constexpr (GATHER) jv_next = list_entry(wave + kWaves);
         if constexpr (Q8) jv_next = page_of(wave + kWaves);
