@@ -142,6 +142,7 @@ struct KParams {
     int32_t units;   // work units (grid = splits x units)
     int32_t splits;  // grid splits per unit
     int32_t S_target, c_min, c_max, gran;
+    int32_t S_win, win_span;  // spans of at most win_span positions aim at S_win splits
     int32_t auto_splits;  // split count chosen by the plan (short spans take one split)
     int32_t slices;  // column slices of the merge
     int32_t W;
@@ -264,7 +265,8 @@ __device__ __forceinline__ void atomic_st(int32_t* p, int v) {
 // workgroup of a unit, so they agree on the split count.  It never yields
 // more splits than the grid holds.
 __device__ __forceinline__ int chunk_len(int span, const KParams& p) {
-    int c = (span + p.S_target - 1) / p.S_target;
+    const int S = span <= p.win_span ? p.S_win : p.S_target;
+    int c = (span + S - 1) / S;
     c = (c + p.gran - 1) / p.gran * p.gran;
     if (c < p.c_min) c = p.c_min;
     if (p.c_max > 0 && c > p.c_max) c = p.c_max;
@@ -1618,6 +1620,10 @@ static int chunk_max_tokens(int D) { return (int)(kChunkMaxBytes / (4 * D)); }
 // against 4*D bytes of K+V per token it streams: at least 5 tokens per packed
 // row keeps that round trip under 40 % of the split's cache traffic.
 constexpr int kTokensPerRow = 5;
+// Windows of 8 or more rows at head_dim 256 up to kWindowSpan positions: at
+// most kWindowSplits active splits per unit (see the launch).
+constexpr int kWindowSplits = 32;
+constexpr int kWindowSpan = 6144;
 // Fewest splits per group at which 17-32 packed rows still take two 16-row
 // groups rather than one of 32 (see plan_impl).
 constexpr int64_t kPairSplits = 16;
@@ -1919,9 +1925,26 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     // 1000 / 3000 / 24000 and n_q = 4 within noise.  Shared 16-row groups
     // (n_q 5-6) were slower with it (13.8 -> 14.5), the INT8 and masked
     // paths are left as planned.
-    if (!q8 && W == 0 && !keep_mask && num_splits == 0 && pl.row_groups == 1 &&
-        (int64_t)pl.units * pl.split_target * 2 > cus)
-        kp.S_target = max(1, pl.split_target * 3 / 4);
+    const bool few_units = !q8 && W == 0 && !keep_mask && num_splits == 0 && pl.row_groups == 1 &&
+                           (int64_t)pl.units * pl.split_target * 2 > cus;
+    if (few_units) kp.S_target = max(1, pl.split_target * 3 / 4);
+    // Causal windows (and step rows) of 8-16 packed rows at head_dim 256 make
+    // partials 2-4 times those of one query, so up to kWindowSpan positions a
+    // unit aims at no more than kWindowSplits splits: their merge costs more
+    // than the extra splits save on the stream.  Measured on the MI355X (us
+    // per layer, B = 1, 4 KV heads, cold; 48 -> 32 splits): n_q = 3 at kv_len
+    // 3000 / 4000 / 5000 / 6000 11.9 / 12.4 / 13.0 / 13.9 -> 11.1 / 11.7 /
+    // 12.6 / 13.2, n_q = 4 at 4000 / 6000 13.2 / 14.8 -> 12.3 / 13.7, n_q =
+    // 2 at 3000 10.7 -> 10.4, 2000 unchanged.  Longer spans keep the target:
+    // with 32 splits n_q = 2 at 7000 took 13.8-14.2 against 13.1, n_q = 3 at
+    // 8000 15.5 against 14.5.  With two sequences (a target of 24) halving
+    // the splits was 1.0-1.3 us slower, so the bound is a cap, not a fraction.
+    kp.S_win = kp.S_target;
+    kp.win_span = 0;
+    if (few_units && pl.rows >= 8 && s->D == 256) {
+        kp.S_win = min(kp.S_target, kWindowSplits);
+        kp.win_span = kWindowSpan;
+    }
     kp.c_min = pl.chunk_min;
     kp.auto_splits = num_splits == 0 ? 1 : 0;
     kp.c_max = pl.chunk_max;

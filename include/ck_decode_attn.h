@@ -120,8 +120,10 @@ enum {
  * cache, automatic split count) with one row
  * group per head, whose units alone leave most compute units idle
  * (2 * units * split_target > CUs), aims at three quarters of split_target
- * (fewer, longer splits publish fewer partials); the grid, and so the
- * workspace, is that of the plan either way. */
+ * (fewer, longer splits publish fewer partials), and at no more than 32
+ * splits for 8 or more packed rows at head_dim 256 over a range of at most
+ * 6144 positions; the grid, and so the workspace, is that of the plan
+ * either way. */
 typedef struct ck_decode_plan {
     int32_t units;
     int32_t splits;          /* grid splits per unit                         */

@@ -62,7 +62,7 @@ def test_d256_capacity_sweep_bit_identical():
 
 
 @pytest.mark.parametrize("n_q", [3, 4, 5, 6])
-@pytest.mark.parametrize("L", [2000, 4000])
+@pytest.mark.parametrize("L", [2000, 4000, 6144, 6145])  # 6144: the last span with the window split cap
 def test_d256_causal_window(layer_d256, n_q, L):
     note(f"causal window n_q={n_q} L={L}")
     k, v, (kd, vd) = layer_d256

@@ -76,3 +76,43 @@ def test_stamps_on_step_rows_change_nothing():
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert int((stamps[:, 0] > 0).sum()) == pl["units"] * pl["splits"]  # the stamping instance ran
+
+
+def active_splits(pl, rows, D, L):
+    """Active splits per unit of plain automatic-split decode with one row
+    group per head whose units leave most of the 256 CUs idle: three quarters
+    of the split target, at most 32 for windows of 8 or more rows at head_dim
+    256 up to 6144 positions; the range is cut in whole granules."""
+    S = max(1, pl["split_target"] * 3 // 4)
+    if rows >= 8 and D == 256 and L <= 6144:
+        S = min(S, 32)
+    gran = pl["granule"]
+    c = max(-(-(-(-L // S)) // gran) * gran, pl["chunk_min"])
+    need = -(-(-(-L // pl["splits"])) // gran) * gran
+    return -(-L // max(c, need))
+
+
+@pytest.mark.parametrize("n_q,L", [(1, 4000), (2, 3000), (3, 4000), (3, 6144), (3, 6145), (4, 6000), (4, 8000)])
+def test_window_split_count(n_q, L):
+    """The active split count the kernel takes for causal windows, read from
+    the stamps, on both sides of the 6144-position window bound; the stamped
+    launch gives the plain launch's bits."""
+    B, Hq, Hkv, D, cap = 1, 16, 4, 256, 8192
+    k, v = synth.kv_cache(B, cap, Hkv, D, [L], 1104 + n_q, device=DEV)
+    q = synth.queries(B, n_q, Hq, D, 1104 + n_q, device=DEV)
+    lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    note(f"window split count n_q={n_q} L={L}")
+    ref = ck.decode_attn(q, k, v, lens, causal=True)
+    pl = ck.plan(ck.shape_of(q, k))
+    assert pl["units"] == 4 and pl["row_groups"] == 1
+    stamps = torch.zeros((pl["units"] * pl["splits"], 16), dtype=torch.int64, device=DEV)
+    ck.set_phase_stamps(stamps)
+    try:
+        out = ck.decode_attn(q, k, v, lens, causal=True)
+    finally:
+        ck.set_phase_stamps(None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    n_active = (stamps[:, 15].cpu().numpy() >> 32) & 0xFFFF
+    want = active_splits(pl, n_q * (Hq // Hkv), D, L)
+    assert np.all(n_active == want), (sorted(set(n_active.tolist())), want)
