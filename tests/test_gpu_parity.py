@@ -146,7 +146,7 @@ def _steps(B, n_q, Hkv, D, seed):
 
 
 @pytest.mark.parametrize("n_q", [1, 3, 6])
-@pytest.mark.parametrize("L", [0, 1, 37, 2000, 4000])
+@pytest.mark.parametrize("L", [0, 1, 37, 2000, 4000, 6144, 6145])
 def test_d256_step_rows_match_oracle(layer_d256, n_q, L):
     """MTP verification with the drafts passed beside the cache: prefix
     [0, L) plus step rows 0..i for query i (bf16 output for the longer
