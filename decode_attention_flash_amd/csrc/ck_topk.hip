@@ -53,6 +53,7 @@ constexpr int kWsCounts = kWsHist + 2 * kWsHistSet;
 constexpr int kMaxWgPerRow = 256;
 constexpr int kWsCand = kWsCounts + 2 * kMaxWgPerRow;  // then (key, position) pairs, per workgroup
 constexpr int kCand = 4096;                               // threshold-bin cells gathered in LDS
+constexpr int kRankMax = 64;                              // a bin of at most this many keys is ranked by one wave
 constexpr size_t kWsHeader = 256;                         // the status word, then the rows
 // Super-blocks of a workgroup whose keys stay in registers: 1 when a
 // workgroup holds one (a row split over many workgroups), else 8.  Each
@@ -440,9 +441,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             }
         }
         __syncthreads();
-        // the remaining 21 bits in two LDS digits (11 and 10)
+        // the remaining 21 bits in LDS: an 11-bit digit, then the last 10
+        // bits of the chosen bin.  The bin usually holds a few keys (of ~2000
+        // normal scores over 2048 bins): up to kRankMax of them are ranked by
+        // one wave, key against key, instead of a third histogram.
+        uint32_t n_bin1 = 0;
+        bool ranked = false;
 #pragma unroll 1
         for (int lvl = 1; lvl < 3; ++lvl) {
+            if (lvl == 2 && n_bin1 <= (uint32_t)kRankMax) {
+                ranked = true;
+                break;
+            }
             const int shift = lvl == 1 ? 10 : 0;
             const int nb = lvl == 1 ? 2048 : 1024;
             const int above = lvl == 1 ? 21 : 10;
@@ -457,9 +467,44 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TParams p) {
             const uint32_t digit = find_bin(nullptr, nb, k_rem, &n_above, &n_bin);
             prefix = (prefix << (lvl == 2 ? 10 : 11)) | digit;
             k_rem -= (int)n_above;
+            n_bin1 = n_bin;
         }
-        T = prefix;
-        n_eq_take = k_rem;
+        if (ranked) {
+            // The bin's keys (their top 22 bits equal prefix) go to lh[0..),
+            // counted in lh[kRankMax]; lane j of wave 0 holds key j and counts
+            // the keys above it and equal to it.  The key with k_rem - 1 keys
+            // above it, or fewer but with equals reaching k_rem, is T.
+            if (tid == 0) lh[kRankMax] = 0u;
+            __syncthreads();
+            for (int e = tid; e < n_c; e += kThreads) {
+                const uint32_t key = ck_key[e];
+                if ((key >> 10) == prefix) {
+                    const uint32_t at = atomicAdd(&lh[kRankMax], 1u);
+                    if (at < (uint32_t)kRankMax) lh[at] = key;
+                }
+            }
+            __syncthreads();
+            if (tid < 64) {
+                const int m = (int)n_bin1;
+                const uint32_t mine = tid < m ? lh[tid] : 0u;
+                uint32_t gt = 0, eq = 0;
+                for (int j = 0; j < m; ++j) {
+                    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+                    gt += o > mine ? 1u : 0u;
+                    eq += o == mine ? 1u : 0u;
+                }
+                if (tid < m && gt < (uint32_t)k_rem && (uint32_t)k_rem <= gt + eq) {
+                    pick[0] = mine;  // every lane holding T writes the same values
+                    pick[1] = (uint32_t)k_rem - gt;
+                }
+            }
+            __syncthreads();
+            T = pick[0];
+            n_eq_take = (int)pick[1];
+        } else {
+            T = prefix;
+            n_eq_take = k_rem;
+        }
         // selected pairs before this workgroup's range, and equal keys there
         const int start = sb0 * kSuper;
         uint32_t gb_t = 0, eb_t = 0;

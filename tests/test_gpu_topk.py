@@ -169,3 +169,23 @@ def test_concentrated_and_tied_rows_full_size(kind):
     sc = torch.stack([row, row.flip(0)]).view(1, 1, 2, n_kv).contiguous()
     check(sc, [n_kv], 2048, 64, what=kind)
     check(sc, [n_kv - 12345], 2048, 64, causal=False, what=f"{kind} shorter")
+
+
+@pytest.mark.parametrize("n_kv", [32768, 131072])
+@pytest.mark.parametrize("copies", [30, 62, 70, 300])
+def test_threshold_ties_in_lds_selection(n_kv, copies):
+    """Normal scores whose k-th largest value is copied into `copies` other
+    cells below it: the threshold bin still fits in LDS, and after its
+    11-bit digit the remaining bin holds about `copies` keys, so both the
+    one-wave ranking (up to 64 keys) and the last histogram level (more)
+    choose among exact ties."""
+    note(f"topk threshold ties n_kv={n_kv} copies={copies}")
+    sc = synth.index_scores(1, 1, 2, n_kv, 7100 + copies).numpy().copy()
+    rng = np.random.default_rng(7200 + copies)
+    for h in range(2):
+        row = sc[0, 0, h, : n_kv - 64]
+        v = np.sort(row)[::-1][2047]
+        below = np.flatnonzero(row < v)
+        row[rng.choice(below, size=copies, replace=False)] = v
+    got = check(torch.from_numpy(sc), [n_kv], 2048, 64, what=f"ties {copies}")
+    assert np.all(np.diff(got, axis=-1) > 0)
