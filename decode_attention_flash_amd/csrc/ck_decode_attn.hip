@@ -1620,8 +1620,8 @@ static int chunk_max_tokens(int D) { return (int)(kChunkMaxBytes / (4 * D)); }
 // against 4*D bytes of K+V per token it streams: at least 5 tokens per packed
 // row keeps that round trip under 40 % of the split's cache traffic.
 constexpr int kTokensPerRow = 5;
-// Windows of 8 or more rows at head_dim 256 up to kWindowSpan positions: at
-// most kWindowSplits active splits per unit (see the launch).
+// Units of 8 or more packed rows at head_dim 256 over at most kWindowSpan
+// positions: at most kWindowSplits active splits per unit (see the launch).
 constexpr int kWindowSplits = 32;
 constexpr int kWindowSpan = 6144;
 // Fewest splits per group at which 17-32 packed rows still take two 16-row
@@ -1928,10 +1928,11 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     const bool few_units = !q8 && W == 0 && !keep_mask && num_splits == 0 && pl.row_groups == 1 &&
                            (int64_t)pl.units * pl.split_target * 2 > cus;
     if (few_units) kp.S_target = max(1, pl.split_target * 3 / 4);
-    // Causal windows (and step rows) of 8-16 packed rows at head_dim 256 make
-    // partials 2-4 times those of one query, so up to kWindowSpan positions a
-    // unit aims at no more than kWindowSplits splits: their merge costs more
-    // than the extra splits save on the stream.  Measured on the MI355X (us
+    // Units of 8 or more packed rows at head_dim 256 (causal windows, step
+    // rows, groups of 8 or more query heads) make partials 2-4 times those of
+    // one query of a 4-head group, so up to kWindowSpan positions such a unit
+    // aims at no more than kWindowSplits splits: their merge costs more than
+    // the extra splits save on the stream.  Measured on the MI355X (us
     // per layer, B = 1, 4 KV heads, cold; 48 -> 32 splits): n_q = 3 at kv_len
     // 3000 / 4000 / 5000 / 6000 11.9 / 12.4 / 13.0 / 13.9 -> 11.1 / 11.7 /
     // 12.6 / 13.2, n_q = 4 at 4000 / 6000 13.2 / 14.8 -> 12.3 / 13.7, n_q =
