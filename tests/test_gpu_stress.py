@@ -6,7 +6,8 @@ launch.  Each case captures one launch in a graph and replays it 1000 times
 with fresh lengths written into the device length buffer before each
 replay, for the automatic plan and for forced split counts 2, 7 and 64.
 After every replay an eager launch on the same lengths (its own output
-buffers, the same workspace) must give the same bits; the case stops at
+buffers, the same workspace) must give the same bits (also for causal windows,
+whose split count changes at 6144 positions); the case stops at
 the first mismatch.  At the end the workspace's status word is zero and
 its counters are ready for the next launch."""
 import numpy as np
@@ -22,19 +23,19 @@ pytestmark = pytest.mark.gpu
 REPLAYS = 1000
 
 
-def stress(B, Hq, Hkv, D, cap, lo, hi, num_splits, seed):
+def stress(B, Hq, Hkv, D, cap, lo, hi, num_splits, seed, n_q=1):
     k, v = synth.kv_cache(B, cap, Hkv, D, [cap] * B, seed, device=DEV, garbage=False)
-    q = synth.queries(B, 1, Hq, D, seed, device=DEV)
+    q = synth.queries(B, n_q, Hq, D, seed, device=DEV)
     shape = ck.shape_of(q, k)
     ws = ck.new_workspace(shape, num_splits=num_splits)
     lens_d = torch.full((B,), hi, dtype=torch.int32, device=DEV)
-    out = torch.empty((B, 1, Hq, D), dtype=torch.float32, device=DEV)
-    lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, n_q, Hq, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device=DEV)
     eo = torch.empty_like(out)
     el = torch.empty_like(lse)
 
     def launch(o, l):
-        ck.decode_attn(q, k, v, lens_d, out=o, lse=l, workspace=ws, num_splits=num_splits)
+        ck.decode_attn(q, k, v, lens_d, causal=n_q > 1, out=o, lse=l, workspace=ws, num_splits=num_splits)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -48,7 +49,7 @@ def stress(B, Hq, Hkv, D, cap, lo, hi, num_splits, seed):
     torch.cuda.synchronize()
     rng = np.random.default_rng(seed)
     lens_all = torch.from_numpy(rng.integers(lo, hi + 1, size=(REPLAYS, B)).astype(np.int32)).to(DEV)
-    note(f"stress B={B} D={D} cap={cap} splits={num_splits}: {REPLAYS} replays")
+    note(f"stress B={B} n_q={n_q} D={D} cap={cap} splits={num_splits}: {REPLAYS} replays")
     for r in range(REPLAYS):
         lens_d.copy_(lens_all[r])
         graph.replay()
@@ -81,3 +82,11 @@ def test_stress_short_spans(num_splits):
     uniform in [1, 1024]: with automatic splits the lengths cross the
     single-split bound (256 positions) and the one-slice merge bound."""
     stress(2, 8, 2, 128, 1024, 1, 1024, num_splits, 5300 + num_splits)
+
+
+@pytest.mark.parametrize("n_q", [3, 4, 6])
+def test_stress_windows(n_q):
+    """Causal windows over the head_dim-256 layer, lengths uniform in [1,
+    8192]: n_q 3-4 cross the 6144-position bound of their split cap, n_q 6
+    runs as two 16-row groups sharing tiles."""
+    stress(1, 16, 4, 256, 8192, 1, 8192, 0, 5400 + n_q, n_q=n_q)
