@@ -111,6 +111,25 @@ def test_d256_decode_matches_oracle(L):
     assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what=f"q8 L={L}")
 
 
+@pytest.mark.parametrize("D,L", [(128, 16384), (128, 16447), (128, 20000), (256, 19000)])
+def test_long_block_table(D, L):
+    """A block table of 320 entries (64-token pages): the first tile of a
+    split that starts within the first 256 entries takes its page from the
+    entries loaded with the length, a later one from its own load."""
+    B, Hkv, page, max_pages = 1, 2, 64, 320
+    Hq = 8 if D == 128 else 4
+    note(f"q8 long block table D={D} L={L}")
+    bt, pages, num_pages = filled_case(B, Hkv, D, page, max_pages, [L], 2150 + L)
+    c = make_cache(bt, pages, num_pages, page, Hkv, D)
+    q = synth.queries(B, 1, Hq, D, 2151)
+    lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    for num_splits in (0, 16):
+        out, lse = ck.decode_attn_q8(q.to(DEV), c, lens, return_lse=True, num_splits=num_splits)
+        torch.cuda.synchronize()
+        ref = oracle.attn_q8(q, *pages, bt, np.array([L], np.int32), 1 / math.sqrt(D))
+        assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what=f"q8 long table L={L} S={num_splits}")
+
+
 @pytest.mark.parametrize("n_q", [3, 6])
 def test_d256_causal_window_matches_oracle(n_q):
     B, Hq, Hkv, D, page, max_pages, L = 1, 16, 4, 256, 64, 64, 2000
