@@ -631,8 +631,11 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             const int r = row0 + rr;
             const int i = GATHER ? iq : r / p.G;
             const int j = GATHER ? r : r % p.G;
-            const uint32_t qoff =
-                rr < nrows ? (uint32_t)((i * p.Hq + g * p.G + j) * D + 32 * ks + 8 * (fl >> 4)) * 2u : kOOB;
+            // Paged INT8 cache: k-step ks of lane group q covers head dims
+            // 64 (ks / 2) + 16 q + 8 (ks % 2), the order in which each lane
+            // loads its K codes (16 per load) straight into MFMA operands.
+            const int col = Q8 ? 64 * (ks >> 1) + 16 * (fl >> 4) + 8 * (ks & 1) : 32 * ks + 8 * (fl >> 4);
+            const uint32_t qoff = rr < nrows ? (uint32_t)((i * p.Hq + g * p.G + j) * D + col) * 2u : kOOB;
             qfrag[u] = __builtin_bit_cast(bf16x8, bload128(rq, qoff));
         }
     }
@@ -749,6 +752,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
     // RPI whole rows.
     u32x4 kraw[VI], vraw[VI];
     u32x4 k8[Gm::VI8], v8[Gm::VI8];  // paged INT8 tile (MODE 3)
+    bf16x8 kop[Q8 ? 2 * Gm::VI8 : 1];  // its K as bf16 MFMA operands, [mb][k-step]
+    static_assert(Gm::VI8 * 2 == MB * KS, "one 16-code K load per two k-steps of an M block");
     float ksv = 0.f, vsv = 0.f;       // scales of token `lane` of that tile
     uint32_t mraw[RT][MB];
     constexpr bool kDeferMask = !(D == 256 && RT == 2);
@@ -780,18 +785,21 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
             const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ksc + prow, sbytes);
             const __amdgpu_buffer_rsrc_t rvs8 = make_rsrc(p.vsc + prow, sbytes);
             constexpr int CPR8 = Gm::CPR8, RPI8 = Gm::RPI8;
-            uint32_t o8[Gm::VI8];
+            uint32_t o8[Gm::VI8], ok8[Gm::VI8];
 #pragma unroll
-            for (int n = 0; n < Gm::VI8; ++n)
+            for (int n = 0; n < Gm::VI8; ++n) {
                 o8[n] = (uint32_t)(n * RPI8 + lane / CPR8) * rstride + (uint32_t)(lane % CPR8) * 16u;
+                // K: row 16 mb + l16, head dims 64 u + 16 q4 .. + 15 (n = mb * KS / 2 + u)
+                ok8[n] = (uint32_t)(16 * (n / (KS / 2)) + l16) * rstride + (uint32_t)(64 * (n % (KS / 2)) + 16 * q4);
+            }
             if constexpr (CO) {  // the other row groups read these tiles again: keep them in L2
 #pragma unroll
-                for (int n = 0; n < Gm::VI8; ++n) k8[n] = bload128<0>(rk8, o8[n]);
+                for (int n = 0; n < Gm::VI8; ++n) k8[n] = bload128<0>(rk8, ok8[n]);
 #pragma unroll
                 for (int n = 0; n < Gm::VI8; ++n) v8[n] = bload128<0>(rv8, o8[n]);
             } else {
 #pragma unroll
-                for (int n = 0; n < Gm::VI8; ++n) k8[n] = bload128<2>(rk8, o8[n]);
+                for (int n = 0; n < Gm::VI8; ++n) k8[n] = bload128<2>(rk8, ok8[n]);
 #pragma unroll
                 for (int n = 0; n < Gm::VI8; ++n) v8[n] = bload128<2>(rv8, o8[n]);
             }
@@ -976,15 +984,17 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
         // -- stage K and V rows in LDS, then send the next tile's loads -----
         float* scw = sc_lds + (Q8 ? wave * 3 * TT : 0);
         if constexpr (Q8) {
-            // int8 codes become bf16 in the same layout; the scales go beside.
+            // K codes become bf16 MFMA operands in registers (two k-steps per
+            // load); V codes become bf16 in the LDS layout of the bf16 path;
+            // the scales go beside.
             constexpr int CPR8 = Gm::CPR8, RPI8 = Gm::RPI8;
 #pragma unroll
             for (int n = 0; n < Gm::VI8; ++n) {
                 const int row = n * RPI8 + lane / CPR8, c8 = lane % CPR8;
                 u32x4 lo, hi;
                 i8x16_to_bf16(k8[n], lo, hi);
-                *reinterpret_cast<u32x4*>(klds + row * RSK + c8 * 32) = lo;
-                *reinterpret_cast<u32x4*>(klds + row * RSK + c8 * 32 + 16) = hi;
+                kop[2 * n] = __builtin_bit_cast(bf16x8, lo);
+                kop[2 * n + 1] = __builtin_bit_cast(bf16x8, hi);
                 i8x16_to_bf16(v8[n], lo, hi);
                 *reinterpret_cast<u32x4*>(vlds + row * RS + c8 * 32) = lo;
                 *reinterpret_cast<u32x4*>(vlds + row * RS + c8 * 32 + 16) = hi;
@@ -1209,7 +1219,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(RT)) void decode_kernel(co
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(klds + (16 * mb + l16) * RSK + 64 * ks + 16 * q4);
+                const bf16x8 ka = Q8 ? kop[mb * KS + ks]
+                                     : *reinterpret_cast<const bf16x8*>(klds + (16 * mb + l16) * RSK + 64 * ks + 16 * q4);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) sc[rt][mb] = mfma(ka, q_lds[(rt * KS + ks) * 64 + lane], sc[rt][mb]);
             }
