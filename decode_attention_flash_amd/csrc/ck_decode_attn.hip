@@ -1631,8 +1631,9 @@ static int chunk_max_tokens(int D) { return (int)(kChunkMaxBytes / (4 * D)); }
 // against 4*D bytes of K+V per token it streams: at least 5 tokens per packed
 // row keeps that round trip under 40 % of the split's cache traffic.
 constexpr int kTokensPerRow = 5;
-// Units of 8 or more packed rows at head_dim 256 over at most kWindowSpan
-// positions: at most kWindowSplits active splits per unit (see the launch).
+// Units of 8 or more packed rows (12 with the INT8 cache) at head_dim 256
+// over at most kWindowSpan positions: at most kWindowSplits active splits per
+// unit (see the launch).
 constexpr int kWindowSplits = 32;
 constexpr int kWindowSpan = 6144;
 // Fewest splits per group at which 17-32 packed rows still take two 16-row
@@ -1951,9 +1952,15 @@ static int run(const ck_decode_shape* s, const void* q, const void* k, const voi
     // with 32 splits n_q = 2 at 7000 took 13.8-14.2 against 13.1, n_q = 3 at
     // 8000 15.5 against 14.5.  With two sequences (a target of 24) halving
     // the splits was 1.0-1.3 us slower, so the bound is a cap, not a fraction.
+    // The INT8 cache, which keeps every planned split otherwise, takes the
+    // cap from 12 rows: n_q = 3 / 4 at kv_len 4000 13.1 / 13.8 -> 12.2 / 12.7
+    // us, at 6000 14.4 / 15.5 -> 13.6 / 14.3, 2000 unchanged, while n_q = 2
+    // was 0.05-0.5 us slower with it (kv_len 3000-6000).
+    const bool q8_units = q8 && W == 0 && !keep_mask && num_splits == 0 && pl.row_groups == 1 &&
+                          (int64_t)pl.units * pl.split_target * 2 > cus;
     kp.S_win = kp.S_target;
     kp.win_span = 0;
-    if (few_units && pl.rows >= 8 && s->D == 256) {
+    if (((few_units && pl.rows >= 8) || (q8_units && pl.rows >= 12)) && s->D == 256) {
         kp.S_win = min(kp.S_target, kWindowSplits);
         kp.win_span = kWindowSpan;
     }

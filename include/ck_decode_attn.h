@@ -122,8 +122,9 @@ enum {
  * (2 * units * split_target > CUs), aims at three quarters of split_target
  * (fewer, longer splits publish fewer partials), and at no more than 32
  * splits for 8 or more packed rows at head_dim 256 over a range of at most
- * 6144 positions; the grid, and so the workspace, is that of the plan
- * either way. */
+ * 6144 positions (with the INT8 cache, which otherwise aims at split_target,
+ * from 12 rows); the grid, and so the workspace, is that of the plan either
+ * way. */
 typedef struct ck_decode_plan {
     int32_t units;
     int32_t splits;          /* grid splits per unit                         */

@@ -130,10 +130,11 @@ def test_long_block_table(D, L):
         assert_close((out.cpu().numpy(), lse.cpu().numpy()), ref, what=f"q8 long table L={L} S={num_splits}")
 
 
-@pytest.mark.parametrize("n_q", [3, 6])
-def test_d256_causal_window_matches_oracle(n_q):
-    B, Hq, Hkv, D, page, max_pages, L = 1, 16, 4, 256, 64, 64, 2000
-    note(f"q8 window n_q={n_q}")
+@pytest.mark.parametrize("n_q", [3, 4, 6])
+@pytest.mark.parametrize("L", [2000, 4000, 6144, 6145])  # 6144: the last span with the window split cap
+def test_d256_causal_window_matches_oracle(n_q, L):
+    B, Hq, Hkv, D, page, max_pages = 1, 16, 4, 256, 64, 100
+    note(f"q8 window n_q={n_q} L={L}")
     bt, pages, num_pages = filled_case(B, Hkv, D, page, max_pages, [L], 2200 + n_q)
     c = make_cache(bt, pages, num_pages, page, Hkv, D)
     q = synth.queries(B, n_q, Hq, D, 2201)
@@ -142,7 +143,7 @@ def test_d256_causal_window_matches_oracle(n_q):
         out, lse = ck.decode_attn_q8(q.to(DEV), c, lens, causal=True, out_dtype=out_dtype, return_lse=True)
         torch.cuda.synchronize()
         ref = oracle.attn_q8(q, *pages, bt, np.array([L], np.int32), 1 / math.sqrt(D), True)
-        assert_close((out.float().cpu().numpy(), lse.cpu().numpy()), ref, out_dtype, f"q8 window {n_q}")
+        assert_close((out.float().cpu().numpy(), lse.cpu().numpy()), ref, out_dtype, f"q8 window {n_q} L={L}")
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,D,lens,rpg", [
