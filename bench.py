@@ -672,6 +672,12 @@ def main():
             r = q8_case(qst, 1, 1, Hq, Hkv, D, [L], args.steps, args.warmup)
             log(f"int8 pages kv_len {L}: {r['us']:.2f} us, {r['kv_gbs']:.0f} GB/s")
             sweep["q8_kv_len"].append(dict(kv_len=L, page=128, **r))
+        sweep["q8_causal_window"] = []
+        for L in (2000, 4000):
+            for n_q in (3, 4, 5, 6):
+                r = q8_case(qst, 1, n_q, Hq, Hkv, D, [L], args.steps, args.warmup, causal=True)
+                log(f"int8 pages window n_q={n_q} L={L}: {r['us']:.2f} us")
+                sweep["q8_causal_window"].append(dict(kv_len=L, n_q=n_q, page=128, **r))
         del qst
         torch.cuda.empty_cache()
         from decode_attention_flash_amd import synth
